@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of paged GQA decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload large|splitk_B8_L1024|...]
+
+Prints ONE JSON line. A step is one call of the library's entry point
+(host plan + decode kernel [+ LSE merge kernel]) over one batch of synthetic
+input that is already resident in HBM. `value` is the achieved algorithmic
+bandwidth in GB/s: (K+V bytes of the valid tokens + Q + O bytes) / time per
+call; `ms_per_step` is the time per call. The default workload is the
+bandwidth-bound large decode: batch 64, context 4,096, Hq/Hkv 32/8, D 128,
+bf16, block size 16, whose 1 GiB of K+V per call does not fit the 256 MB
+Infinity Cache, so every call streams from HBM.
+
+Before timing, the output of the timed configuration is checked against the
+fp64 CPU oracle; a case that fails is not timed.
+
+Other modes:
+  --calibrate-copy   only run device-to-device copies of a known size
+                     (reference kernel for the HBM traffic counters)
+  --ingest-pmc F W CF CW
+                     turn four rocprofv3 --pmc counter CSVs (FETCH_SIZE and
+                     WRITE_SIZE of the bench run, then of the copy run) into
+                     profiles/traffic_<workload>.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + achieved HBM GB/s (% of peak), paged GQA decode Hq/Hkv 32/8 D128"
+PEAK_GBPS = 8000.0          # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "paged_gqa_decode_02_amd", "csrc", "pd_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_KERNEL = "pd_decode_kernel"
+COPY_BYTES = 1 << 30
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def make_workload(name: str, seed: int = 0):
+    import workloads
+    if name == "large":
+        return workloads.large(seed)
+    if name == "ragged":
+        return workloads.ragged(seed)
+    if name == "tiny":
+        return workloads.tiny(seed)
+    if name.startswith("splitk_"):
+        _, b, l = name.split("_")
+        return workloads.splitk(int(b[1:]), int(l[1:]), seed)
+    if name.startswith("short_"):
+        # short_B32_L64_bf16_bs16
+        _, b, l, dt, bs = name.split("_")
+        return workloads.short(int(b[1:]), int(l[1:]), dt, int(bs[2:]), seed)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def upload(case, torch):
+    q, k, v = (t.to("cuda") for t in case.torch_views())
+    bt = torch.from_numpy(case.block_table).to("cuda")
+    cl = torch.from_numpy(case.context_lens).to("cuda")
+    return q, k, v, bt, cl
+
+
+def parity(case, out_bits_np):
+    """Both gates of the parity tests; returns the error summary."""
+    import numpy as np
+    import oracle
+    ref, _ = oracle.attention_case(case)
+    g = oracle.widen(out_bits_np, case.dtype)
+    err = np.abs(g - ref)
+    ok = bool(np.all(np.isfinite(g)) and np.all(err <= 1e-2 + 1e-2 * np.abs(ref)))
+    return ok, {"max_abs": float(err.max()), "max_rel_gt_1e-2":
+                float((err / np.maximum(np.abs(ref), 1e-2)).max())}
+
+
+def time_calls(fn, iters: int, warmup: int, torch) -> float:
+    """Average ms per call over `iters` calls, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def time_graph(fn, iters: int, torch) -> float:
+    """Average ms per call when `iters` calls are captured in one HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def replicas_for(case, torch, pd, min_bytes=1 << 30):
+    """Device replicas of the whole input set, enough to cover min_bytes, so
+    that a rotating loop cannot be served from the 256 MB Infinity Cache."""
+    base = upload(case, torch)
+    foot = sum(t.numel() * t.element_size() for t in base)
+    R = max(1, math.ceil(min_bytes / foot))
+    reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    outs = [torch.empty_like(base[0]) for _ in range(R)]
+    wss = [pd.alloc_workspace(r[0], r[1], r[3]) for r in reps]
+    return reps, outs, wss, foot
+
+
+def bench_other(name, torch, pd, iters=200, warmup=20):
+    case = make_workload(name)
+    reps, outs, wss, foot = replicas_for(case, torch, pd)
+    R = len(reps)
+
+    def call(i):
+        q, k, v, bt, cl = reps[i % R]
+        pd.paged_decode_attention(q, k, v, bt, cl, outs[i % R], scale=case.scale,
+                                  workspace=wss[i % R])
+
+    call(0)
+    torch.cuda.synchronize()
+    ok, err = parity(case, outs[0].cpu().view(torch.int16).numpy().view("uint16"))
+    if not ok:
+        return {"parity": "FAIL", **err}
+    ms = time_calls(call, iters, warmup, torch)
+    iters_g = max(R, (iters // R) * R)
+    ms_g = time_graph(call, iters_g, torch)
+    S, P = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
+                                case.block_size, torch.bfloat16 if case.dtype == "bf16"
+                                else torch.float16)
+    nbytes = case.algorithmic_bytes()
+    res = {"us_per_call": round(ms * 1e3, 3), "us_per_call_graph": round(ms_g * 1e3, 3),
+           "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
+           "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
+           "algorithmic_bytes": nbytes, "splits": S, "partition_tokens": P,
+           "replicas": R, "rotated_bytes": R * foot, "max_abs_err": round(err["max_abs"], 6)}
+    del reps, outs, wss
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(case, nseq: int):
+    """Time the fp64 oracle on the first `nseq` sequences of the workload."""
+    import oracle
+    share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    nthreads = max(1, min(16, share or 1))
+    sub_cl = case.context_lens[:nseq]
+    t0 = time.perf_counter()
+    _, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
+                                  case.block_table[:nseq], sub_cl, scale=case.scale,
+                                  dtype=case.dtype, nthreads=nthreads, return_threads=True)
+    dt = time.perf_counter() - t0
+    nbytes = 4096 * int(sub_cl.astype("int64").sum()) + 16384 * nseq
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
+                      f"one oracle call, fp64, {used} threads"}
+
+
+def load_traffic(workload: str):
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None  # counters were taken on an older kernel
+    return t
+
+
+def read_pmc(path: str, counter: str, kernel_substr: str):
+    """Per-dispatch values of `counter` for kernels whose name contains kernel_substr."""
+    vals = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if kernel_substr in row.get("Kernel_Name", "") and row.get("Counter_Name") == counter:
+                vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def ingest_pmc(workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    import statistics
+    f = read_pmc(fetch_csv, "FETCH_SIZE", DECODE_KERNEL)
+    w = read_pmc(write_csv, "WRITE_SIZE", DECODE_KERNEL)
+    cf = read_pmc(cfetch_csv, "FETCH_SIZE", "opy")
+    cw = read_pmc(cwrite_csv, "WRITE_SIZE", "opy")
+    if not (f and w and cf and cw):
+        raise SystemExit("missing counter rows")
+    # FETCH_SIZE / WRITE_SIZE are in KiB per dispatch; the copy moves COPY_BYTES each way
+    kf = COPY_BYTES / (statistics.median(cf) * 1024.0)
+    kw = COPY_BYTES / (statistics.median(cw) * 1024.0)
+    fetch = statistics.median(f) * 1024.0 * kf
+    write = statistics.median(w) * 1024.0 * kw
+    doc = {"workload": workload, "kernel": DECODE_KERNEL, "kernel_sha": kernel_sha(),
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write,
+           "copy_calibration": {"bytes": COPY_BYTES, "fetch_factor": kf, "write_factor": kw},
+           "raw_median_kib": {"fetch": statistics.median(f), "write": statistics.median(w),
+                              "copy_fetch": statistics.median(cf),
+                              "copy_write": statistics.median(cw)},
+           "dispatches": {"fetch": len(f), "write": len(w)}}
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(doc, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(doc))
+
+
+def calibrate_copy(torch, n=20):
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(n):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "copies": n}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--splits", type=int, default=None, help="force the split count")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=64)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
+    args = ap.parse_args()
+
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; there is no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_gqa_decode_02_amd as pd
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+
+    case = make_workload(args.workload, args.seed)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float16
+    q, k, v, bt, cl = upload(case, torch)
+    out = torch.empty_like(q)
+    ws = pd.alloc_workspace(q, k, bt, args.splits)
+    S, P = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
+                                case.block_size, dt, args.splits)
+
+    def call(i):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=case.scale, workspace=ws,
+                                  num_splits=args.splits)
+
+    call(0)
+    torch.cuda.synchronize()
+    ok, err = parity(case, out.cpu().view(torch.int16).numpy().view("uint16"))
+    if not ok:
+        print(json.dumps({"metric": METRIC, "error": "parity check failed", **err}))
+        sys.exit(1)
+
+    ms = time_calls(call, args.steps, args.warmup, torch)
+    nbytes = case.algorithmic_bytes()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+
+    traffic = load_traffic(args.workload)
+    roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_GBPS, 4),
+            "traffic": None if traffic is None else traffic["traffic_bytes_per_launch"],
+            "kernel": DECODE_KERNEL + ("" if S == 1 else " + pd_merge_kernel"),
+            "algorithmic_bytes_per_launch": nbytes}
+
+    res = {"metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "us_per_call": round(ms * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": case.dtype, "accumulate": "f32", "data": "synthetic",
+           "config": {"workload": case.name, "batch": case.B, "context": int(case.context_lens.max()),
+                      "Hq": case.Hq, "Hkv": case.Hkv, "head_dim": case.D,
+                      "block_size": case.block_size, "splits": S, "partition_tokens": P,
+                      "algorithmic_bytes": nbytes},
+           "parity": {"ok": ok, **{k2: round(v2, 6) for k2, v2 in err.items()}},
+           "roofline": roof}
+    if not args.no_others:
+        others = {}
+        for name in ("splitk_B8_L1024", "splitk_B1_L1024", "ragged", "short_B32_L64_bf16_bs16"):
+            others[name] = bench_other(name, torch, pd)
+        res["others"] = others
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_seqs, case.B))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

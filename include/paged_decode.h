@@ -1,0 +1,151 @@
+/*
+ * paged_decode.h - C ABI of the MI355X (gfx950) paged GQA decode library.
+ *
+ * One query token per head attends over a KV cache scattered in fixed-size
+ * blocks through a block table, with the query heads that share a KV head
+ * packed into one pass over that head's K/V bytes, and long contexts split
+ * into partitions whose partial results are merged by log-sum-exp (Loom
+ * Kernels home page, "Supported now": paged MQA/GQA decode, GQA packing +
+ * local split-K/LSE; benchmark page, "What the ratios mean": the
+ * native-cache short-context route and the D128 long-context split-K/LSE
+ * path at Hq/Hkv 32/8).
+ *
+ * What a call computes, for every sequence b < B and query head h < Hq, with
+ * G = Hq / Hkv, g = h / G (consecutive grouping) and L = context_lens[b]:
+ *
+ *   s_t   = scale * sum_d q[b][h][d] * K[blk(t)][t % block_size][g][d],  t < L
+ *   out[b][h][:] = sum_t softmax(s)_t * V[blk(t)][t % block_size][g][:]
+ *
+ * where blk(t) = block_table[b][t / block_size]. L = 0 gives a zero row.
+ * Scores, softmax and accumulation run in fp32; the output is rounded once
+ * to the input dtype, round-to-nearest-even.
+ *
+ * Layouts (row-major, contiguous, element type = dtype unless stated):
+ *   q, out         [B, Hq, D]
+ *   k_cache        [num_blocks, block_size, Hkv, D]
+ *   v_cache        [num_blocks, block_size, Hkv, D]
+ *   block_table    int32 [B, max_blocks_per_seq]
+ *   context_lens   int32 [B]
+ *   workspace      caller-owned device scratch for the split-K partials
+ *
+ * Ownership: every pointer is borrowed device memory that the caller keeps
+ * alive until the work queued on `stream` has finished. The library never
+ * allocates, frees, synchronises, or reads device memory on the host, so a
+ * call can be captured in a HIP graph; block_table and context_lens are read
+ * on the device when the kernels run. Inputs are never written; only `out`
+ * and the workspace are.
+ *
+ * Device-side contract (not checkable on the host, the caller's duty):
+ * 0 <= context_lens[b] <= max_blocks_per_seq * block_size, and every block
+ * id the first ceil(L / block_size) entries of a row hold is in
+ * [0, num_blocks). Entries past those, and cache slots at or after L in the
+ * last block, are never read.
+ *
+ * Errors: every entry point returns PD_OK or one of the codes below and
+ * writes nothing when it fails before launching. No C++ exception crosses
+ * the ABI. Supported now: D = 128, Hq / Hkv = 4, block_size 16 or 32,
+ * dtype f16 or bf16; other valid shapes return PD_ERR_UNSUPPORTED.
+ */
+#ifndef PAGED_DECODE_H
+#define PAGED_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PAGED_DECODE_ABI_VERSION 1
+
+/* dtype codes */
+#define PD_DTYPE_F16 0
+#define PD_DTYPE_BF16 1
+
+/* status codes */
+#define PD_OK 0
+#define PD_ERR_NULL 1          /* a required pointer is NULL */
+#define PD_ERR_SHAPE 2         /* a size is out of range or inconsistent */
+#define PD_ERR_DTYPE 3         /* dtype is not PD_DTYPE_F16 / PD_DTYPE_BF16 */
+#define PD_ERR_ALIGN 4         /* q/k/v/out not 16-byte, tables not 4-byte, workspace not 256-byte aligned */
+#define PD_ERR_ALIAS 5         /* out overlaps q, block_table, context_lens or the workspace */
+#define PD_ERR_WORKSPACE 6     /* workspace missing or smaller than required */
+#define PD_ERR_UNSUPPORTED 7   /* valid but not implemented (D, group size, block size) */
+#define PD_ERR_HIP 8           /* the HIP runtime rejected a launch */
+#define PD_ERR_INTERNAL 9      /* unexpected internal failure */
+#define PD_ERR_VALUE 10        /* scale is not a finite positive number */
+
+/* Version of this ABI (PAGED_DECODE_ABI_VERSION of the built library). */
+int32_t paged_decode_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* paged_decode_strerror(int32_t code);
+
+/*
+ * Split plan for a shape: the number of context partitions S and the tokens
+ * per partition P (a multiple of block_size) that paged_decode_attention
+ * will use. Partition p covers tokens [p*P, min((p+1)*P, L)) of a sequence;
+ * S = 1 means a single pass that writes `out` directly. A pure function of
+ * its arguments (the heuristic is tuned for a full 256-CU MI355X); it
+ * touches no device. Returns PD_OK, or the error the attention call would
+ * give for the shape.
+ */
+int32_t paged_decode_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                          int32_t max_blocks_per_seq, int32_t block_size, int32_t dtype,
+                          int32_t* num_splits, int32_t* partition_tokens);
+
+/*
+ * Workspace bytes paged_decode_attention needs for this shape: 0 when the
+ * plan has S = 1, else room for fp32 partial outputs [B, Hq, S, D] and fp32
+ * partial log-sum-exps [B, Hq, S]. Returns 0 for an invalid shape too
+ * (paged_decode_plan tells the two apart).
+ */
+size_t paged_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t dtype);
+
+/*
+ * Paged decode attention (see the top of this file). Queues one or two
+ * kernels on `stream` (a hipStream_t; NULL is the null stream) and returns
+ * without waiting. `workspace` may be NULL when
+ * paged_decode_workspace_bytes(...) is 0. `scale` is usually
+ * 1/sqrt(D) rounded to float.
+ */
+int32_t paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t max_blocks_per_seq, void* out,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t block_size, float scale, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same kernels with the split count forced to `num_splits` (>= 1) instead
+ * of the heuristic's; P becomes the smallest multiple of block_size with
+ * S*P >= max_blocks_per_seq * block_size, and S is then recomputed as
+ * ceil(max_blocks_per_seq * block_size / P), so it can come out smaller than
+ * asked. For tests and measurements of the split path; the result equals the
+ * planned call's up to fp32 rounding order.
+ */
+int32_t paged_decode_attention_splits(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      int32_t max_blocks_per_seq, void* out,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t block_size, float scale, int32_t dtype,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      int32_t num_splits);
+
+/* Plan and workspace size for a forced split count, as used by
+ * paged_decode_attention_splits. */
+int32_t paged_decode_plan_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_blocks_per_seq, int32_t block_size, int32_t dtype,
+                                 int32_t requested_splits,
+                                 int32_t* num_splits, int32_t* partition_tokens);
+size_t paged_decode_workspace_bytes_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                           int32_t max_blocks_per_seq, int32_t block_size,
+                                           int32_t dtype, int32_t requested_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_DECODE_H */

@@ -1,0 +1,159 @@
+"""MI355X-native paged GQA decode attention.
+
+A thin ctypes binding over the C ABI in ``include/paged_decode.h`` (built as
+``_lib/libpaged_decode.so`` by ``python -m paged_gqa_decode_02_amd.build``).
+The functions keep the C names; they only marshal torch tensors into pointers,
+sizes and the current HIP stream. Every step of the computation runs in the
+library's HIP kernels. Importing this package fails if the library has not
+been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libpaged_decode.so")
+
+PD_DTYPE_F16 = 0
+PD_DTYPE_BF16 = 1
+_DTYPE_CODE = {torch.float16: PD_DTYPE_F16, torch.bfloat16: PD_DTYPE_BF16}
+
+PD_OK = 0
+STATUS_NAMES = {
+    0: "PD_OK", 1: "PD_ERR_NULL", 2: "PD_ERR_SHAPE", 3: "PD_ERR_DTYPE", 4: "PD_ERR_ALIGN",
+    5: "PD_ERR_ALIAS", 6: "PD_ERR_WORKSPACE", 7: "PD_ERR_UNSUPPORTED", 8: "PD_ERR_HIP",
+    9: "PD_ERR_INTERNAL", 10: "PD_ERR_VALUE",
+}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"paged_gqa_decode_02_amd: HIP library not built ({LIB_PATH} missing); "
+        "run `python -m paged_gqa_decode_02_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+_P, _I, _Z, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+_PI = ctypes.POINTER(ctypes.c_int32)
+
+lib.paged_decode_abi_version.argtypes = []
+lib.paged_decode_abi_version.restype = _I
+lib.paged_decode_strerror.argtypes = [_I]
+lib.paged_decode_strerror.restype = ctypes.c_char_p
+lib.paged_decode_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I, _PI, _PI]
+lib.paged_decode_plan.restype = _I
+lib.paged_decode_plan_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _PI, _PI]
+lib.paged_decode_plan_splits.restype = _I
+lib.paged_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+lib.paged_decode_workspace_bytes.restype = _Z
+lib.paged_decode_workspace_bytes_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
+lib.paged_decode_workspace_bytes_splits.restype = _Z
+_ATTN = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
+lib.paged_decode_attention.argtypes = _ATTN
+lib.paged_decode_attention.restype = _I
+lib.paged_decode_attention_splits.argtypes = _ATTN + [_I]
+lib.paged_decode_attention_splits.restype = _I
+
+
+class PagedDecodeError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = int(code)
+        super().__init__(f"{STATUS_NAMES.get(self.code, self.code)}: {paged_decode_strerror(self.code)}")
+
+
+def paged_decode_abi_version() -> int:
+    return int(lib.paged_decode_abi_version())
+
+
+def paged_decode_strerror(code: int) -> str:
+    return lib.paged_decode_strerror(int(code)).decode()
+
+
+def paged_decode_plan(B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype, num_splits=None):
+    """(S, P) the library uses for this shape; ``num_splits`` forces S."""
+    s, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    dt = _DTYPE_CODE.get(dtype, dtype)
+    if num_splits is None:
+        rc = lib.paged_decode_plan(B, Hq, Hkv, D, max_blocks_per_seq, block_size, dt,
+                                   ctypes.byref(s), ctypes.byref(p))
+    else:
+        rc = lib.paged_decode_plan_splits(B, Hq, Hkv, D, max_blocks_per_seq, block_size, dt,
+                                          int(num_splits), ctypes.byref(s), ctypes.byref(p))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return s.value, p.value
+
+
+def paged_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype,
+                                 num_splits=None) -> int:
+    dt = _DTYPE_CODE.get(dtype, dtype)
+    if num_splits is None:
+        return int(lib.paged_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq,
+                                                    block_size, dt))
+    return int(lib.paged_decode_workspace_bytes_splits(B, Hq, Hkv, D, max_blocks_per_seq,
+                                                       block_size, dt, int(num_splits)))
+
+
+def _shape(q, k_cache, block_table):
+    B, Hq, D = q.shape
+    _, bs, Hkv, _ = k_cache.shape
+    return int(B), int(Hq), int(Hkv), int(D), int(block_table.shape[1]), int(bs)
+
+
+def alloc_workspace(q, k_cache, block_table, num_splits=None) -> torch.Tensor:
+    """A device workspace of the size the call needs (possibly 0 bytes)."""
+    B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
+    n = paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, bs, q.dtype, num_splits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=None, *,
+                           scale=None, workspace=None, num_splits=None, stream=None):
+    """Paged decode attention on the current (or given) stream.
+
+    q [B,Hq,D], k_cache/v_cache [num_blocks,block_size,Hkv,D] (f16 or bf16,
+    contiguous, on the GPU); block_table int32 [B,max_blocks_per_seq];
+    context_lens int32 [B]. ``out`` (same shape/dtype as q) and
+    ``workspace`` are allocated when not given. ``num_splits`` forces the
+    split count (``paged_decode_attention_splits``). Returns ``out``.
+    """
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k_cache and v_cache must share one dtype, float16 or bfloat16")
+    B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = D ** -0.5
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_table, num_splits)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
+    args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+            context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
+            _DTYPE_CODE[q.dtype], workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), handle]
+    if num_splits is None:
+        rc = lib.paged_decode_attention(*args)
+    else:
+        rc = lib.paged_decode_attention_splits(*args, int(num_splits))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return out
+
+
+def paged_decode_attention_splits(q, k_cache, v_cache, block_table, context_lens, num_splits,
+                                  out=None, **kw):
+    """``paged_decode_attention`` with the split count forced to ``num_splits``."""
+    return paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out,
+                                  num_splits=num_splits, **kw)

@@ -1,0 +1,61 @@
+"""Build the in-tree HIP library ``_lib/libpaged_decode.so`` for gfx950.
+
+    python -m paged_gqa_decode_02_amd.build
+
+Compiles the kernels (``csrc/pd_kernels.hip``) and the host side
+(``csrc/pd_api.cpp``, ``csrc/pd_plan.cpp``) with hipcc into one shared
+library exporting the C ABI of ``include/paged_decode.h``. Packed fp32 VALU
+instructions are disabled for the device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB_DIR = os.path.join(HERE, "_lib")
+LIB = os.path.join(LIB_DIR, "libpaged_decode.so")
+ARCH = "gfx950"
+
+SOURCES = ["pd_kernels.hip", "pd_api.cpp", "pd_plan.cpp"]
+HEADERS = ["pd_internal.h"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile the library (always) and return its path."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function",
+           "-I", os.path.join(ROOT, "include")]
+    cmd += list(extra_flags or [])
+    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature; that warning is harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    err = "\n".join(x for x in res.stderr.splitlines() if noise not in x)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

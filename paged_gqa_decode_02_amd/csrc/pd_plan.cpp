@@ -1,0 +1,78 @@
+// Host-side shape checks and the split-count heuristic.
+//
+// The split count is chosen per (batch, context) shape: the Loom Kernels
+// benchmark page ("What the ratios mean") describes the decode route as
+// shape-gated, with short contexts and a long-context split-K/LSE path. Here
+// that becomes one kernel family whose partition count S is a pure function
+// of the host-visible shape, so results are reproducible call to call and
+// the same plan is baked into a captured graph.
+#include <limits.h>
+
+#include "../../include/paged_decode.h"
+#include "pd_internal.h"
+
+namespace pd {
+
+namespace {
+
+constexpr int64_t kCUs = 256;              // MI355X compute units
+constexpr int64_t kTargetGroups = 4 * kCUs;  // workgroups that fill the chip
+constexpr int64_t kMinPartition = 64;      // fewest tokens worth a partition
+constexpr int64_t kMaxSplits = 1024;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+int32_t check_shape(const Shape& s) {
+  if (s.dtype != PD_DTYPE_F16 && s.dtype != PD_DTYPE_BF16) return PD_ERR_DTYPE;
+  if (s.B < 0 || s.Hq < 1 || s.Hkv < 1 || s.D < 1 || s.block_size < 1 ||
+      s.max_blocks_per_seq < 1)
+    return PD_ERR_SHAPE;
+  if (s.Hq % s.Hkv != 0) return PD_ERR_SHAPE;
+  if ((int64_t)s.max_blocks_per_seq * s.block_size > INT_MAX / 2) return PD_ERR_SHAPE;
+  if (s.D != kHeadDim || s.Hq / s.Hkv != kGroup) return PD_ERR_UNSUPPORTED;
+  if (s.block_size != 16 && s.block_size != 32) return PD_ERR_UNSUPPORTED;
+  // grid limits: (S, Hkv, B) with y and z below 65536
+  if (s.B > 65535 || s.Hkv > 65535) return PD_ERR_SHAPE;
+  return PD_OK;
+}
+
+int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
+  int32_t st = check_shape(s);
+  if (st != PD_OK) return st;
+  const int64_t bs = s.block_size;
+  const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
+  const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
+  int64_t want;
+  if (requested_splits > 0) {
+    want = requested_splits;
+  } else {
+    want = ceil_div(kTargetGroups, units);
+    const int64_t by_len = ceil_div(cap, kMinPartition);
+    if (want > by_len) want = by_len;
+  }
+  if (want < 1) want = 1;
+  if (want > kMaxSplits) want = kMaxSplits;
+  int64_t P = round_up(ceil_div(cap, want), bs);
+  int64_t S = ceil_div(cap, P);
+  plan->splits = (int32_t)S;
+  plan->partition_tokens = (int32_t)P;
+  // wavefronts per workgroup: one wave per 64 tokens of partition, up to 4
+  int64_t w = P / 64;
+  plan->waves = w >= 4 ? 4 : (w >= 2 ? 2 : 1);
+  return PD_OK;
+}
+
+size_t partials_bytes(const Shape& s, const Plan& p) {
+  return align256((size_t)s.B * s.Hq * p.splits * s.D * sizeof(float));
+}
+
+size_t workspace_bytes(const Shape& s, const Plan& p) {
+  if (p.splits <= 1) return 0;
+  return partials_bytes(s, p) + align256((size_t)s.B * s.Hq * p.splits * sizeof(float));
+}
+
+}  // namespace pd

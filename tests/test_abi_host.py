@@ -1,0 +1,172 @@
+"""Host-side checks of the C-ABI library: it loads, exports what the header
+declares, and every argument error is reported before anything is launched.
+No GPU: every call here returns before the library touches the HIP runtime,
+and the pointers passed are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_decode_02_amd as pd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_decode.h")
+F16, BF16 = pd.PD_DTYPE_F16, pd.PD_DTYPE_BF16
+CODES = {name: code for code, name in pd.STATUS_NAMES.items()}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_decode_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(pd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_the_header():
+    src = open(HEADER).read()
+    for name, val in re.findall(r"#define (PD_(?:OK|ERR_\w+)) (\d+)", src):
+        assert CODES[name] == int(val), name
+
+
+def test_abi_version_and_strerror():
+    assert pd.paged_decode_abi_version() == 1
+    seen = set()
+    for code in pd.STATUS_NAMES:
+        msg = pd.paged_decode_strerror(code)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert pd.paged_decode_strerror(12345) == "unknown status code"
+
+
+# ---------------------------------------------------------------------------
+# plan
+
+SHAPES = [(B, L, bs) for B in (1, 2, 4, 8, 32, 64) for L in (16, 32, 64, 128, 1024, 4096)
+          for bs in (16, 32)]
+
+
+@pytest.mark.parametrize("B,L,bs", SHAPES)
+def test_plan_covers_the_context_with_block_aligned_partitions(B, L, bs):
+    MB = -(-L // bs)
+    S, P = pd.paged_decode_plan(B, 32, 8, 128, MB, bs, BF16)
+    assert S >= 1 and P >= bs and P % bs == 0
+    assert S * P >= MB * bs > (S - 1) * P
+    assert (S, P) == pd.paged_decode_plan(B, 32, 8, 128, MB, bs, BF16)  # deterministic
+    ws = pd.paged_decode_workspace_bytes(B, 32, 8, 128, MB, bs, BF16)
+    if S == 1:
+        assert ws == 0
+    else:
+        assert ws >= B * 32 * S * (128 + 1) * 4 and ws % 256 == 0
+
+
+def test_plan_splits_small_batches_and_not_large_ones():
+    assert pd.paged_decode_plan(1, 32, 8, 128, 64, 16, BF16)[0] > 1      # B1 ctx1024
+    assert pd.paged_decode_plan(64, 32, 8, 128, 256, 16, BF16)[0] <= 4   # B64 ctx4096
+    assert pd.paged_decode_plan(32, 32, 8, 128, 1, 16, BF16)[0] == 1     # B32 ctx16
+
+
+@pytest.mark.parametrize("req", [1, 2, 3, 4, 5, 7, 16, 64, 1000])
+def test_forced_splits(req):
+    MB, bs = 64, 16
+    S, P = pd.paged_decode_plan(2, 32, 8, 128, MB, bs, BF16, num_splits=req)
+    assert P % bs == 0 and S * P >= MB * bs and S <= req
+    assert S == -(-MB * bs // P)
+    # P is the smallest block multiple with req*P >= cap
+    assert P == -(-(-(-MB * bs // req)) // bs) * bs
+    ws = pd.paged_decode_workspace_bytes(2, 32, 8, 128, MB, bs, BF16, num_splits=req)
+    assert (ws == 0) == (S == 1)
+
+
+def test_plan_rejects_what_the_attention_call_rejects():
+    with pytest.raises(pd.PagedDecodeError) as e:
+        pd.paged_decode_plan(1, 32, 8, 64, 4, 16, BF16)
+    assert e.value.code == CODES["PD_ERR_UNSUPPORTED"]
+    with pytest.raises(pd.PagedDecodeError) as e:
+        pd.paged_decode_plan(1, 30, 8, 128, 4, 16, BF16)
+    assert e.value.code == CODES["PD_ERR_SHAPE"]
+    with pytest.raises(pd.PagedDecodeError) as e:
+        pd.paged_decode_plan(1, 32, 8, 128, 4, 16, 7)
+    assert e.value.code == CODES["PD_ERR_DTYPE"]
+    with pytest.raises(pd.PagedDecodeError) as e:
+        pd.paged_decode_plan(1, 32, 8, 128, 4, 16, BF16, num_splits=0)
+    assert e.value.code == CODES["PD_ERR_SHAPE"]
+    assert pd.paged_decode_workspace_bytes(1, 32, 8, 64, 4, 16, BF16) == 0
+
+
+# ---------------------------------------------------------------------------
+# argument errors of the attention call (fake device addresses, never touched)
+
+BASE = 1 << 32
+
+
+def call(**over):
+    B, Hq, Hkv, D, MB, bs = 2, 32, 8, 128, 4, 16
+    a = dict(q=BASE, k=BASE + (1 << 24), v=BASE + (2 << 24), bt=BASE + (3 << 24),
+             cl=BASE + (3 << 24) + 4096, MB=MB, out=BASE + (4 << 24), B=B, Hq=Hq, Hkv=Hkv,
+             D=D, bs=bs, scale=0.0883883, dtype=BF16, ws=0, ws_bytes=0, stream=0, splits=None)
+    a.update(over)
+    args = [a["q"], a["k"], a["v"], a["bt"], a["cl"], a["MB"], a["out"], a["B"], a["Hq"],
+            a["Hkv"], a["D"], a["bs"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"]]
+    if a["splits"] is None:
+        return pd.lib.paged_decode_attention(*args)
+    return pd.lib.paged_decode_attention_splits(*args, a["splits"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), "PD_ERR_DTYPE"),
+    (dict(D=64), "PD_ERR_UNSUPPORTED"),
+    (dict(Hq=16), "PD_ERR_UNSUPPORTED"),
+    (dict(Hq=30), "PD_ERR_SHAPE"),
+    (dict(bs=8), "PD_ERR_UNSUPPORTED"),
+    (dict(bs=0), "PD_ERR_SHAPE"),
+    (dict(MB=0), "PD_ERR_SHAPE"),
+    (dict(B=-1), "PD_ERR_SHAPE"),
+    (dict(B=70000), "PD_ERR_SHAPE"),
+    (dict(scale=float("nan")), "PD_ERR_VALUE"),
+    (dict(scale=float("inf")), "PD_ERR_VALUE"),
+    (dict(scale=0.0), "PD_ERR_VALUE"),
+    (dict(scale=-1.0), "PD_ERR_VALUE"),
+    (dict(q=0), "PD_ERR_NULL"),
+    (dict(k=0), "PD_ERR_NULL"),
+    (dict(v=0), "PD_ERR_NULL"),
+    (dict(bt=0), "PD_ERR_NULL"),
+    (dict(cl=0), "PD_ERR_NULL"),
+    (dict(out=0), "PD_ERR_NULL"),
+    (dict(q=BASE + 8), "PD_ERR_ALIGN"),
+    (dict(k=BASE + (1 << 24) + 2), "PD_ERR_ALIGN"),
+    (dict(v=BASE + (2 << 24) + 4), "PD_ERR_ALIGN"),
+    (dict(out=BASE + (4 << 24) + 8), "PD_ERR_ALIGN"),
+    (dict(bt=BASE + (3 << 24) + 2), "PD_ERR_ALIGN"),
+    (dict(cl=BASE + (3 << 24) + 4097), "PD_ERR_ALIGN"),
+    (dict(out=BASE + 4096), "PD_ERR_ALIAS"),           # inside q
+    (dict(out=BASE - 4096), "PD_ERR_ALIAS"),           # straddles q's start
+    (dict(out=BASE + (3 << 24) - 16), "PD_ERR_ALIAS"),  # runs into the block table
+    (dict(splits=0), "PD_ERR_SHAPE"),
+])
+def test_argument_errors_are_reported_before_launch(over, code):
+    assert call(**over) == CODES[code]
+
+
+def test_split_path_needs_a_big_enough_aligned_disjoint_workspace():
+    MB, bs = 64, 16
+    need = pd.paged_decode_workspace_bytes(2, 32, 8, 128, MB, bs, BF16, num_splits=8)
+    assert need > 0
+    ws = BASE + (8 << 24)
+    assert call(MB=MB, splits=8, ws=0, ws_bytes=need) == CODES["PD_ERR_WORKSPACE"]
+    assert call(MB=MB, splits=8, ws=ws, ws_bytes=need - 1) == CODES["PD_ERR_WORKSPACE"]
+    assert call(MB=MB, splits=8, ws=ws + 16, ws_bytes=need) == CODES["PD_ERR_ALIGN"]
+    out = BASE + (4 << 24)
+    assert call(MB=MB, splits=8, ws=out, ws_bytes=need) == CODES["PD_ERR_ALIAS"]
+
+
+def test_empty_batch_is_a_no_op():
+    # B = 0: nothing to compute, no pointer needed, nothing launched
+    assert call(B=0, q=0, k=0, v=0, bt=0, cl=0, out=0) == CODES["PD_OK"]

@@ -1,0 +1,110 @@
+"""GPU integration checks of the call boundary: current-stream ordering,
+what the call may write, buffer reuse, and HIP-graph capture/replay with the
+paging metadata read at replay time (Loom Kernels benchmark page, "Validation
+ladder": current-stream, mutation-schema and buffer-reuse tests, then graph
+capture/replay)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_decode_02_amd as pd
+import workloads
+from helpers import compare, device_case, out_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def test_call_is_ordered_on_a_non_default_stream():
+    c = workloads.splitk(4, 512, seed=21)
+    q, k, v, bt, cl = device_case(c)
+    ref, _ = oracle.attention_case(c)
+    s = torch.cuda.Stream()
+    q_src = q.clone()
+    q.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        # producer on the same stream, queued right before the call
+        torch.cuda._sleep(2_000_000)
+        q.copy_(q_src)
+        out = pd.paged_decode_attention(q, k, v, bt, cl, scale=c.scale)
+    s.synchronize()
+    compare(out_bits(out), ref, "bf16", what="stream order")
+
+
+def test_only_out_is_written_and_canaries_survive():
+    c = workloads.splitk(2, 256, seed=22)
+    q, k, v, bt, cl = device_case(c)
+    before = [t.clone() for t in (q, k, v, bt, cl)]
+    n = q.numel()
+    buf = torch.full((n + 2 * 4096,), 1234.0, dtype=q.dtype, device="cuda")
+    out = buf[4096:4096 + n].view_as(q)
+    for s in (None, 1, 4):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale, num_splits=s)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:4096] == 1234.0) and torch.all(buf[4096 + n:] == 1234.0)
+        for a, b in zip(before, (q, k, v, bt, cl)):
+            assert torch.equal(a, b)
+    ref, _ = oracle.attention_case(c)
+    compare(out_bits(out), ref, "bf16", what="canary")
+
+
+def test_out_and_workspace_reuse_across_shapes():
+    out = None
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for B, L in ((8, 1024), (1, 128), (8, 1024), (2, 512)):
+        c = workloads.splitk(B, L, seed=23 + B + L)
+        q, k, v, bt, cl = device_case(c)
+        if out is None or out.shape != q.shape:
+            out = torch.empty_like(q)
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle.attention_case(c)
+        compare(out_bits(out), ref, "bf16", what=f"reuse B{B} L{L}")
+
+
+def test_graph_replay_reads_context_lens_at_replay_time():
+    # one captured call, replayed with different context lengths written
+    # between replays (all within max_blocks_per_seq * block_size)
+    c = workloads.make_case("graph", 4, [700, 900, 1024, 513], dtype="bf16", block_size=16,
+                            seed=24, max_blocks_per_seq=64)
+    q, k, v, bt, cl = device_case(c)
+    out = torch.empty_like(q)
+    ws = pd.alloc_workspace(q, k, bt)
+    # warm up on a side stream, as graph capture requires
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale, workspace=ws)
+    rng = np.random.default_rng(5)
+    for rep in range(6):
+        lens = rng.integers(0 if rep == 3 else 1, 1025, size=4).astype(np.int32)
+        cl.copy_(torch.from_numpy(lens))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_bits(out)
+        # eager call on the same metadata must agree bitwise
+        eager = out_bits(pd.paged_decode_attention(q, k, v, bt, cl, scale=c.scale, workspace=
+                                                   torch.empty_like(ws)))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager), rep
+        c.context_lens[:] = lens
+        ref, _ = oracle.attention_case(c)
+        compare(got, ref, "bf16", what=f"graph replay {rep}")
+
+
+def test_wrong_dtype_and_shapes_are_rejected_by_the_binding():
+    c = workloads.tiny(0)
+    q, k, v, bt, cl = device_case(c)
+    with pytest.raises(ValueError):
+        pd.paged_decode_attention(q.float(), k, v, bt, cl)
+    with pytest.raises(ValueError):
+        pd.paged_decode_attention(q, k, v, bt.long(), cl)
+    with pytest.raises(pd.PagedDecodeError) as e:
+        pd.paged_decode_attention(q, k, v, bt, cl, q)  # out aliases q
+    assert e.value.code == 5
