@@ -19,8 +19,14 @@ struct Shape {
 struct Plan {
   int32_t splits;            // S: context partitions per (sequence, KV head)
   int32_t partition_tokens;  // P: tokens per partition, a multiple of block_size
-  int32_t waves;             // wavefronts per workgroup (1, 2 or 4)
+  int32_t waves;             // NW: wavefronts per workgroup (1, 2, 4 or 8)
+  int32_t wave_tokens;       // Pw: tokens per wave, a multiple of block_size,
+                             //     at most 64 blocks; NW * Pw >= P
 };
+
+// Most blocks one wave's range may span (one block id per lane).
+constexpr int kMaxWaveBlocks = 64;
+constexpr int kMaxWaves = 8;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.
 int32_t check_shape(const Shape& s);

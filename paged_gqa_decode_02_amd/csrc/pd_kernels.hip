@@ -6,30 +6,32 @@
 // pass over that head's K/V bytes, and a long context is cut into
 // partitions whose normalised partial outputs and log-sum-exps are merged.
 //
-// Decode kernel, one workgroup per (partition p, KV head g, sequence b):
-//   * lanes: 8 lanes per token row. A wave step covers 8 consecutive tokens;
-//     lane (tg = lane/8, sl = lane%8) owns token tg of the step and the
-//     16 head-dim elements [8sl, 8sl+8) and [64+8sl, 64+8sl+8). Each row is
-//     256 contiguous bytes, so one 128-bit load instruction of the wave reads
-//     eight whole 128-byte lines.
+// Decode kernel, one workgroup of NW wave64s per (partition p, KV head g,
+// sequence b); wave w owns a block-aligned range of at most 64 blocks:
+//   * lanes: 16 lanes per token row. A 4-token step gives lane
+//     (row = lane/16, sl = lane%16) token `row` of the step and head-dim
+//     elements [8sl, 8sl+8): each 128-bit load instruction of the wave reads
+//     four whole 256-byte rows (eight 128-byte lines).
 //   * K/V come straight from HBM into registers with bounds-checked buffer
 //     loads whose resource is the current physical block (base = pool +
-//     id * block bytes, size = block bytes). Lanes whose token lies past the
-//     context get an offset beyond the block: the hardware returns zeros and
-//     issues no memory access.
-//   * block ids: each lane of a wave loads one block-table entry of the
-//     wave's range up front; a step takes its (wave-uniform) id with
-//     v_readlane, so the address is scalar and known before the K/V loads.
+//     id * block bytes, size = block bytes), so an access cannot leave the
+//     block; lanes past the context get an offset beyond the block and read
+//     zeros with no memory access. Three 8-token stages of loads are kept in
+//     flight while the oldest is computed.
+//   * block ids: each lane loads one block-table entry of the wave's range
+//     before the context length is known; a stage takes its (wave-uniform)
+//     id with v_readlane, so addresses are scalar.
 //   * scores: q stays as packed 16-bit pairs; v_dot2_f32_{bf16,f16} gives
-//     fp32 products-and-sums with no conversion of K, then a 3-step DPP
-//     butterfly over the 8 lanes of a row, then one multiply by
-//     scale*log2(e) so the softmax runs in base 2 (v_exp_f32).
-//   * softmax: per head, a wave-uniform running maximum updated once per
-//     batch of steps (DPP + permlane16/32 swaps across the 8 token groups),
-//     each lane keeping its own partial sum l and accumulator acc[4][16].
-//   * end of range: a reduce-scatter over token groups (permlane32_swap,
-//     permlane16_swap, then DPP row_ror:8) leaves head r's 128 sums in row r
-//     of the wave; waves of a workgroup are merged through LDS.
+//     fp32 sums of products with no conversion of K, a 4-step DPP butterfly
+//     sums the 16 lanes of a row, and one multiply by scale*log2(e) puts the
+//     softmax in base 2 (v_exp_f32).
+//   * softmax: a wave-uniform running maximum per head that only moves when
+//     a ballot finds a score above it (then permlane16/32 swaps reduce over
+//     the 4 rows and the accumulators are rescaled); each lane keeps its own
+//     partial sum l and accumulator acc[4][8].
+//   * end of range: a reduce-scatter over the 4 rows (permlane32_swap, then
+//     permlane16_swap) leaves head r's 128 sums in row r; the waves of a
+//     workgroup are merged through LDS.
 //   * S == 1 writes `out` rounded to the dtype; S > 1 writes fp32 o_p and
 //     the partition's log2-sum-exp.
 // Merge kernel, one workgroup per (query head, sequence): the LSE merge over
@@ -49,10 +51,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = pd::kHeadDim;  // 128
+constexpr int kMaxWaveBlocks = pd::kMaxWaveBlocks;
 constexpr int G = pd::kGroup;    // 4
 constexpr uint32_t kRowBytes = D * 2;        // one token row of one KV head
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;        // raw 32-bit buffer, gfx9 data format
+constexpr int kStream = 2;                    // cache policy "nt": K/V bytes are read once
 
 struct KArgs {
   const uint16_t* q;
@@ -67,6 +71,7 @@ struct KArgs {
   int32_t MB;
   int32_t S;
   int32_t P;
+  int32_t Pw;          // tokens per wave, a multiple of the block size, <= 64 blocks
   float scale_log2;   // scale * log2(e)
   uint32_t blk_bytes;  // block_size * Hkv * D * 2
 };
@@ -114,15 +119,7 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;   // lane i <-> 7-i within each 8 lanes
-constexpr int kRowRor8 = 0x128;      // lane i <- (i+8) mod 16 within the row
-
-// Sum over the 8 lanes of a token row; every lane gets the total.
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kHalfMirror>(x);
-  return x;
-}
+constexpr int kRowMirror = 0x140;    // lane i <-> 15-i within the row
 
 __device__ __forceinline__ float swap16_lo(float a, float b, float* b_out) {
   auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
@@ -138,26 +135,6 @@ __device__ __forceinline__ float swap32_lo(float a, float b, float* b_out) {
   return __builtin_bit_cast(float, (uint32_t)r[0]);
 }
 
-// Maximum over the 8 token groups of the wave (lanes with equal lane%8).
-__device__ __forceinline__ float max_groups(float x) {
-  x = fmaxf(x, dpp<kRowRor8>(x));
-  float y;
-  float a = swap16_lo(x, x, &y);
-  x = fmaxf(a, y);
-  a = swap32_lo(x, x, &y);
-  return fmaxf(a, y);
-}
-
-// Sum over the 8 token groups of the wave.
-__device__ __forceinline__ float sum_groups(float x) {
-  x += dpp<kRowRor8>(x);
-  float y;
-  float a = swap16_lo(x, x, &y);
-  x = a + y;
-  a = swap32_lo(x, x, &y);
-  return a + y;
-}
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, int32_t id,
@@ -166,25 +143,137 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, i
       (void*)(base + (int64_t)id * (int64_t)blk_bytes), (short)0, (int)blk_bytes, kRsrcWord3);
 }
 
-// One workgroup of NW waves per (partition, KV head, sequence).
-// BS: block size (16 or 32). U: wave steps (8 tokens each) per batch.
-template <bool BF16, int BS, int NW, int U, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void pd_decode_kernel(const KArgs a) {
-  static_assert(BS % (8 * U) == 0, "a batch must stay inside one block");
-  constexpr int SPB = BS / 8;  // wave steps per block
+// Sum over the 16 lanes of a token row; every lane gets the total.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  return x;
+}
+
+// Maximum / sum over the 4 token rows of the wave (lanes with equal lane%16).
+__device__ __forceinline__ float max_rows(float x) {
+  float y;
+  float a = swap16_lo(x, x, &y);
+  x = fmaxf(a, y);
+  a = swap32_lo(x, x, &y);
+  return fmaxf(a, y);
+}
+
+__device__ __forceinline__ float sum_rows(float x) {
+  float y;
+  float a = swap16_lo(x, x, &y);
+  x = a + y;
+  a = swap32_lo(x, x, &y);
+  return a + y;
+}
+
+// Per-lane state of one wave's online softmax over its token range.
+// Lane (row r = lane/16, sub-lane sl = lane%16) owns token r of each 4-token
+// step and head-dim elements [8sl, 8sl+8) of the group's 4 query heads.
+template <bool BF16>
+struct WaveState {
+  u32x4 q[G];       // this lane's 8 q elements of each head, packed pairs
+  float acc[G][8];  // unnormalised PV sums of the lane's token row
+  float l[G];       // sum of weights of the lane's token row
+  float m[G];       // wave-uniform running maximum (log2 domain)
+};
+
+// One stage = two 4-token steps = 8 consecutive tokens of one block.
+// kb[i], vb[i]: this lane's 16 bytes of the K / V row of step i's token.
+template <bool BF16>
+__device__ __forceinline__ void stage_compute(WaveState<BF16>& st, const u32x4 (&kb)[2],
+                                              const u32x4 (&vb)[2], bool valid0, bool valid1,
+                                              float c) {
+  float s[2][G];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool ok = i == 0 ? valid0 : valid1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d = dot2<BF16>(st.q[h][e], kb[i][e], d);
+      d = sum16(d);
+      s[i][h] = ok ? d * c : -INFINITY;
+    }
+  }
+  // the running maximum only moves when some score exceeds it (wave vote)
+  uint64_t above = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < G; ++h) above |= __builtin_amdgcn_ballot_w64(s[i][h] > st.m[h]);
+  if (above != 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(st.m[h], max_rows(fmaxf(s[0][h], s[1][h])));
+      const float alpha = exp2_fast(st.m[h] - mn);  // 0 when m was -inf
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
+      st.m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                              __builtin_bit_cast(int, mn)));  // uniform
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // a token past the range reads zeros (out-of-block offset), and its
+    // weight is exp2(-inf) = 0, so it adds nothing
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = exp2_fast(s[i][h] - st.m[h]);
+      st.l[h] += pr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st.acc[h][2 * e] = fmaf(pr, lo_f<BF16>(vb[i][e]), st.acc[h][2 * e]);
+        st.acc[h][2 * e + 1] = fmaf(pr, hi_f<BF16>(vb[i][e]), st.acc[h][2 * e + 1]);
+      }
+    }
+  }
+}
+
+// Decode kernel: one workgroup of NW waves per (partition p, KV head g,
+// sequence b); wave w owns tokens [p*P + w*Pw, +Pw) of the partition, at most
+// 64 blocks. BS: block size. DEPTH: stages of loads kept in flight.
+template <bool BF16, int BS, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void pd_decode_kernel(const KArgs a) {
+  constexpr int DEPTH = 3;
+  constexpr int kStageTok = 8;
   const int p = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int Hq = a.Hkv * G;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tg = lane >> 3;
-  const int sl = lane & 7;
-  const int row = lane >> 4;  // head this lane holds after the final reduction
+  const int row = lane >> 4;
+  const int sl = lane & 15;
 
-  const int L = a.cl[b];
   const int t0 = p * a.P;
+  const int tw0 = t0 + w * a.Pw;
+  const int bi0 = tw0 / BS;
+  // block ids of the wave's whole range, fetched before the context length
+  // is known (entries past the live ones are loaded but never used)
+  const int nb_max = min(a.Pw / BS, a.MB - bi0);
+  const int myid = lane < nb_max ? a.bt[(size_t)b * a.MB + bi0 + lane] : 0;
 
+  WaveState<BF16> st;
+  const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G) * D + sl * 8;
+#pragma unroll
+  for (int h = 0; h < G; ++h) st.q[h] = *(const u32x4*)(qp + h * D);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.l[h] = 0.f;
+    st.m[h] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+  }
+
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // loop bounds and block addresses in scalar registers
+  const int L = __builtin_amdgcn_readfirstlane(a.cl[b]);
   if constexpr (!SPLIT) {
     if (L <= 0) {
       // empty context: a zero row for each of the group's heads
@@ -196,222 +285,129 @@ __global__ __launch_bounds__(NW * 64) void pd_decode_kernel(const KArgs a) {
   } else {
     if (t0 >= L) return;  // the merge reads only the ceil(L/P) non-empty partitions
   }
-  const int t1 = min(t0 + a.P, L);
-
-  // wave sub-range, block aligned
-  const int Pw = ((a.P + NW - 1) / NW + BS - 1) / BS * BS;
-  const int tw0 = t0 + w * Pw;
-  const int tw1 = min(tw0 + Pw, t1);
-
-  // q of the group's 4 heads: this lane's 16 elements of each, as packed pairs
-  const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G) * D;
-  u32x4 qa[G], qb[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    qa[h] = *(const u32x4*)(qp + h * D + sl * 8);
-    qb[h] = *(const u32x4*)(qp + h * D + 64 + sl * 8);
-  }
-
-  float acc[G][16];
-  float l[G], m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = 0.f;
-    m[h] = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
-  }
+  const int tw1 = min(min(tw0 + a.Pw, t0 + a.P), L);
+  const int nst = __builtin_amdgcn_readfirstlane(
+      tw0 < tw1 ? (tw1 - tw0 + kStageTok - 1) / kStageTok : 0);
   const float c = a.scale_log2;
+  const uint32_t lane_off = ((uint32_t)row * a.Hkv + g) * kRowBytes + sl * 16u;
+  const uint32_t tok_bytes = a.Hkv * kRowBytes;
 
-  if (tw0 < tw1) {
-    const int bi0 = tw0 / BS;
-    const int nblk = (tw1 - 1) / BS - bi0 + 1;
-    const int32_t* btrow = a.bt + (size_t)b * a.MB + bi0;
-    const uint32_t lane_off = ((uint32_t)tg * a.Hkv + g) * kRowBytes + sl * 16u;
-    const uint32_t step_bytes = 8u * a.Hkv * kRowBytes;
+  u32x4 kb[DEPTH][2], vb[DEPTH][2];
+  // Queue the loads of stage j. Straight-line code, always four loads, so
+  // the wait counts stay exact: past the range (j >= nst) every lane's token
+  // is >= tw1 and its offset is out of the block, and the block id is forced
+  // to 0, so those loads read nothing.
+  auto issue = [&](int j, u32x4(&kr)[2], u32x4(&vr)[2]) {
+    const int tok = kStageTok * j;                        // offset in the wave range
+    const int idx = min(tok / BS, kMaxWaveBlocks - 1);
+    const int id = __builtin_amdgcn_readlane(myid, idx) * (int)(j < nst);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, id, a.blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, id, a.blk_bytes);
+    const uint32_t base = (uint32_t)(tok % BS) * tok_bytes + lane_off;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = tw0 + tok + 4 * i + row < tw1;
+      // the whole offset goes in the vector operand, which the range check covers
+      const uint32_t vo = ok ? base + 4u * i * tok_bytes : kOutOfBlock;
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, kStream);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kStream);
+    }
+  };
 
-    for (int cb = 0; cb < nblk; cb += 64) {
-      const int nb_here = min(64, nblk - cb);
-      const int myid = lane < nb_here ? btrow[cb + lane] : 0;
-      for (int jb = 0; jb < nb_here; ++jb) {
-        const int id = __builtin_amdgcn_readlane(myid, jb);
-        const int blk_tok0 = (bi0 + cb + jb) * BS;
-        const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, id, a.blk_bytes);
-        const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, id, a.blk_bytes);
+  // The loads must leave in stage order, in the prologue as in the loop, so
+  // that the wait for stage j never has to drain the later stages.
 #pragma unroll
-        for (int ub = 0; ub < SPB; ub += U) {
-          if (blk_tok0 + ub * 8 >= tw1) break;  // rest of the block is past the range
-          u32x4 kr[U][2], vr[U][2];
-          bool valid[U];
+  for (int d = 0; d < DEPTH; ++d) {
+    issue(d, kb[d], vb[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int j0 = 0; j0 < nst; j0 += DEPTH) {
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int tok = blk_tok0 + (ub + u) * 8 + tg;
-            valid[u] = tok < tw1;
-            // the whole offset goes in the vector operand, which the range check covers
-            const uint32_t vo = (valid[u] ? lane_off : kOutOfBlock) + (ub + u) * step_bytes;
-            kr[u][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, 0);
-            kr[u][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo + 128u, 0, 0);
-          }
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const uint32_t vo = (valid[u] ? lane_off : kOutOfBlock) + (ub + u) * step_bytes;
-            vr[u][0] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, 0);
-            vr[u][1] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 128u, 0, 0);
-          }
-          // scores (log2 domain)
-          float s[U][G];
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              float d = 0.f;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) d = dot2<BF16>(qa[h][i], kr[u][0][i], d);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) d = dot2<BF16>(qb[h][i], kr[u][1][i], d);
-              d = sum8(d);
-              s[u][h] = valid[u] ? d * c : -INFINITY;
-            }
-          }
-          // running maximum, wave-uniform per head
-          bool grow = false;
-          float mn[G];
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float bm = s[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) bm = fmaxf(bm, s[u][h]);
-            bm = max_groups(bm);
-            mn[h] = fmaxf(m[h], bm);
-            grow |= mn[h] > m[h];
-          }
-          if (grow) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float alpha = exp2_fast(m[h] - mn[h]);
-              l[h] *= alpha;
-#pragma unroll
-              for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
-              m[h] = mn[h];
-            }
-          }
-          // weights and PV
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float pr = exp2_fast(s[u][h] - m[h]);
-              l[h] += pr;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                acc[h][2 * i] = fmaf(pr, lo_f<BF16>(vr[u][0][i]), acc[h][2 * i]);
-                acc[h][2 * i + 1] = fmaf(pr, hi_f<BF16>(vr[u][0][i]), acc[h][2 * i + 1]);
-                acc[h][8 + 2 * i] = fmaf(pr, lo_f<BF16>(vr[u][1][i]), acc[h][8 + 2 * i]);
-                acc[h][9 + 2 * i] = fmaf(pr, hi_f<BF16>(vr[u][1][i]), acc[h][9 + 2 * i]);
-              }
-            }
-          }
-        }
+    for (int d = 0; d < DEPTH; ++d) {
+      const int j = j0 + d;
+      if (j < nst) {
+        const int tok = tw0 + kStageTok * j + row;
+        stage_compute<BF16>(st, kb[d], vb[d], tok < tw1, tok + 4 < tw1, c);
       }
+      issue(j + DEPTH, kb[d], vb[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- reduce over the 8 token groups of the wave
+  // ---- reduce over the 4 token rows of the wave
 #pragma unroll
-  for (int h = 0; h < G; ++h) l[h] = sum_groups(l[h]);
+  for (int h = 0; h < G; ++h) st.l[h] = sum_rows(st.l[h]);
   // reduce-scatter: rows 0-1 keep heads {0,1}, rows 2-3 keep heads {2,3} ...
-  float r1[2][16];
+  float r1[2][8];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       float y;
-      const float x = swap32_lo(acc[hh][e], acc[hh + 2][e], &y);
+      const float x = swap32_lo(st.acc[hh][e], st.acc[hh + 2][e], &y);
       r1[hh][e] = x + y;
     }
-  // ... then row r keeps head r ...
-  float r2[16];
+  // ... then row r keeps head r.
+  float r2[8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 8; ++e) {
     float y;
     const float x = swap16_lo(r1[0][e], r1[1][e], &y);
     r2[e] = x + y;
   }
-  // ... and the two 8-lane halves of each row are summed.
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r2[e] += dpp<kRowRor8>(r2[e]);
+  float m_r = row == 0 ? st.m[0] : row == 1 ? st.m[1] : row == 2 ? st.m[2] : st.m[3];
+  float l_r = row == 0 ? st.l[0] : row == 1 ? st.l[1] : row == 2 ? st.l[2] : st.l[3];
 
-  const float m_r = row == 0 ? m[0] : row == 1 ? m[1] : row == 2 ? m[2] : m[3];
-  const float l_r = row == 0 ? l[0] : row == 1 ? l[1] : row == 2 ? l[2] : l[3];
-  const bool writer = (lane & 8) == 0;  // first 8 lanes of each row
-  const int h_out = g * G + row;
-
-  if constexpr (NW == 1) {
-    if (writer) {
-      if constexpr (!SPLIT) {
-        const float inv = 1.0f / l_r;
-        uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + h_out) * D;
-        u32x4 w0, w1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w0[i] = pack2<BF16>(r2[2 * i] * inv, r2[2 * i + 1] * inv);
-          w1[i] = pack2<BF16>(r2[8 + 2 * i] * inv, r2[9 + 2 * i] * inv);
-        }
-        *(u32x4*)(o + sl * 8) = w0;
-        *(u32x4*)(o + 64 + sl * 8) = w1;
-      } else {
-        const float inv = 1.0f / l_r;
-        const size_t slot = ((size_t)b * Hq + h_out) * a.S + p;
-        float* o = a.o_part + slot * D;
-        *(f32x4*)(o + sl * 8) = f32x4{r2[0] * inv, r2[1] * inv, r2[2] * inv, r2[3] * inv};
-        *(f32x4*)(o + sl * 8 + 4) = f32x4{r2[4] * inv, r2[5] * inv, r2[6] * inv, r2[7] * inv};
-        *(f32x4*)(o + 64 + sl * 8) =
-            f32x4{r2[8] * inv, r2[9] * inv, r2[10] * inv, r2[11] * inv};
-        *(f32x4*)(o + 64 + sl * 8 + 4) =
-            f32x4{r2[12] * inv, r2[13] * inv, r2[14] * inv, r2[15] * inv};
-        if (sl == 0) a.lse_part[slot] = m_r + __builtin_amdgcn_logf(l_r);
-      }
-    }
-  } else {
-    // ---- merge the NW waves through LDS
-    __shared__ float s_acc[NW][G][D];
+  if constexpr (NW > 1) {
+    // ---- merge the NW waves through LDS; wave 0 finishes
+    __shared__ f32x4 s_acc[NW][G][D / 4];
     __shared__ float s_m[NW][G];
     __shared__ float s_l[NW][G];
-    if (writer) {
-      float* dst = &s_acc[w][row][0];
-      *(f32x4*)(dst + sl * 8) = f32x4{r2[0], r2[1], r2[2], r2[3]};
-      *(f32x4*)(dst + sl * 8 + 4) = f32x4{r2[4], r2[5], r2[6], r2[7]};
-      *(f32x4*)(dst + 64 + sl * 8) = f32x4{r2[8], r2[9], r2[10], r2[11]};
-      *(f32x4*)(dst + 64 + sl * 8 + 4) = f32x4{r2[12], r2[13], r2[14], r2[15]};
-      if (sl == 0) {
-        s_m[w][row] = m_r;
-        s_l[w][row] = l_r;
-      }
+    s_acc[w][row][2 * sl] = f32x4{r2[0], r2[1], r2[2], r2[3]};
+    s_acc[w][row][2 * sl + 1] = f32x4{r2[4], r2[5], r2[6], r2[7]};
+    if (sl == 0) {
+      s_m[w][row] = m_r;
+      s_l[w][row] = l_r;
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < G * D; o += NW * 64) {
-      const int h = o / D;
-      const int d = o % D;
-      float M = s_m[0][h];
+    if (w != 0) return;
+    float M = s_m[0][row];
 #pragma unroll
-      for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i][h]);
-      float num = 0.f, den = 0.f;
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i][row]);
+    float den = 0.f;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const float wt = exp2_fast(s_m[i][h] - M);
-        num = fmaf(wt, s_acc[i][h][d], num);
-        den = fmaf(wt, s_l[i][h], den);
-      }
-      const int hq = g * G + h;
-      if constexpr (!SPLIT) {
-        uint16_t* out = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D;
-        out[d] = to_bits<BF16>(num / den);
-      } else {
-        const size_t slot = ((size_t)b * Hq + hq) * a.S + p;
-        a.o_part[slot * D + d] = num / den;
-        if (d == 0) a.lse_part[slot] = M + __builtin_amdgcn_logf(den);
+    for (int e = 0; e < 8; ++e) r2[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const float wt = exp2_fast(s_m[i][row] - M);  // 0 for a wave with no tokens
+      den = fmaf(wt, s_l[i][row], den);
+      const f32x4 x0 = s_acc[i][row][2 * sl];
+      const f32x4 x1 = s_acc[i][row][2 * sl + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r2[e] = fmaf(wt, x0[e], r2[e]);
+        r2[4 + e] = fmaf(wt, x1[e], r2[4 + e]);
       }
     }
+    m_r = M;
+    l_r = den;
+  }
+
+  // ---- epilogue: row r of wave 0 holds head g*G + r, elements [8sl, 8sl+8)
+  const int hq = g * G + row;
+  const float inv = 1.0f / l_r;
+  if constexpr (!SPLIT) {
+    uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8;
+    u32x4 wv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = pack2<BF16>(r2[2 * i] * inv, r2[2 * i + 1] * inv);
+    *(u32x4*)o = wv;
+  } else {
+    const size_t slot = ((size_t)b * Hq + hq) * a.S + p;
+    float* o = a.o_part + slot * D + sl * 8;
+    *(f32x4*)o = f32x4{r2[0] * inv, r2[1] * inv, r2[2] * inv, r2[3] * inv};
+    *(f32x4*)(o + 4) = f32x4{r2[4] * inv, r2[5] * inv, r2[6] * inv, r2[7] * inv};
+    if (sl == 0) a.lse_part[slot] = m_r + __builtin_amdgcn_logf(l_r);
   }
 }
 
@@ -444,15 +440,15 @@ __global__ __launch_bounds__(D) void pd_merge_kernel(const float* __restrict__ o
 
 template <bool BF16, int BS, int NW, bool SPLIT>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, hipStream_t st) {
-  constexpr int U = 2;
   void* args[] = {(void*)&ka};
-  return hipLaunchKernel((const void*)&pd_decode_kernel<BF16, BS, NW, U, SPLIT>, grid,
+  return hipLaunchKernel((const void*)&pd_decode_kernel<BF16, BS, NW, SPLIT>, grid,
                          dim3(NW * 64), args, 0, st);
 }
 
 template <bool BF16, int BS, bool SPLIT>
 hipError_t pick_waves(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   switch (nw) {
+    case 8: return launch_decode<BF16, BS, 8, SPLIT>(ka, grid, st);
     case 4: return launch_decode<BF16, BS, 4, SPLIT>(ka, grid, st);
     case 2: return launch_decode<BF16, BS, 2, SPLIT>(ka, grid, st);
     default: return launch_decode<BF16, BS, 1, SPLIT>(ka, grid, st);
@@ -504,6 +500,7 @@ int32_t launch(const Launch& l) {
   ka.MB = l.shape.max_blocks_per_seq;
   ka.S = l.plan.splits;
   ka.P = l.plan.partition_tokens;
+  ka.Pw = l.plan.wave_tokens;
   ka.scale_log2 = l.scale * 1.4426950408889634f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv * kRowBytes;
   hipStream_t st = (hipStream_t)l.stream;

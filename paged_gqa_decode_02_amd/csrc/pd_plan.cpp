@@ -15,13 +15,18 @@ namespace pd {
 
 namespace {
 
-constexpr int64_t kCUs = 256;              // MI355X compute units
-constexpr int64_t kTargetGroups = 4 * kCUs;  // workgroups that fill the chip
-constexpr int64_t kMinPartition = 64;      // fewest tokens worth a partition
-constexpr int64_t kMaxSplits = 1024;
+constexpr int64_t kCUs = 256;                 // MI355X compute units
+constexpr int64_t kWavesPerCU = 16;           // resident decode waves per CU (4 per SIMD)
+constexpr int64_t kTargetWaves = kCUs * kWavesPerCU;
+constexpr int64_t kMaxSplits = 1 << 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+int64_t pow2_ceil(int64_t x) {
+  int64_t r = 1;
+  while (r < x) r <<= 1;
+  return r;
+}
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -40,29 +45,50 @@ int32_t check_shape(const Shape& s) {
   return PD_OK;
 }
 
+// The plan cuts each sequence's context (up to cap = max_blocks_per_seq *
+// block_size tokens) into S partitions of P tokens, each served by one
+// workgroup of NW waves of Pw tokens. Pw is sized so that the whole grid is
+// about one full round of resident waves (kTargetWaves): long work keeps
+// every wave streaming, short work keeps every wave's loads in flight at
+// once. NW is the fewest waves (a power of two, at most 8) that cover the
+// context at that Pw; S follows. A forced S fixes P instead and sizes NW
+// and Pw to it.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
   const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
   const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
-  int64_t want;
+  const int64_t pw_max = kMaxWaveBlocks * bs;
+  int64_t pw_target = round_up(ceil_div(units * cap, kTargetWaves), bs);
+  if (pw_target > pw_max) pw_target = pw_max;
+  int64_t P, nw, pw;
   if (requested_splits > 0) {
-    want = requested_splits;
+    int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
+    P = round_up(ceil_div(cap, want), bs);
+    nw = pow2_ceil(ceil_div(P, pw_target));
+    if (nw > kMaxWaves) nw = kMaxWaves;
+    pw = round_up(ceil_div(P, nw), bs);
+    if (pw > pw_max) {  // a partition cannot exceed NW x 64 blocks: split more
+      pw = pw_max;
+      P = nw * pw;
+    }
   } else {
-    want = ceil_div(kTargetGroups, units);
-    const int64_t by_len = ceil_div(cap, kMinPartition);
-    if (want > by_len) want = by_len;
+    nw = pow2_ceil(ceil_div(cap, pw_target));
+    if (nw > kMaxWaves) nw = kMaxWaves;
+    pw = pw_target;
+    P = nw * pw;
+    if (P > cap) {  // one partition: trim the waves to the context
+      pw = round_up(ceil_div(cap, nw), bs);
+      P = nw * pw;
+    }
   }
-  if (want < 1) want = 1;
-  if (want > kMaxSplits) want = kMaxSplits;
-  int64_t P = round_up(ceil_div(cap, want), bs);
   int64_t S = ceil_div(cap, P);
+  if (S > kMaxSplits) return PD_ERR_SHAPE;
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
-  // wavefronts per workgroup: one wave per 64 tokens of partition, up to 4
-  int64_t w = P / 64;
-  plan->waves = w >= 4 ? 4 : (w >= 2 ? 2 : 1);
+  plan->waves = (int32_t)nw;
+  plan->wave_tokens = (int32_t)pw;
   return PD_OK;
 }
 
