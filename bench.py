@@ -306,7 +306,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_GBPS, 4),
             "traffic": None if traffic is None else traffic["traffic_bytes_per_launch"],
-            "kernel": DECODE_KERNEL + ("" if S == 1 else " + pd_merge_kernel"),
+            "kernel": DECODE_KERNEL,
             "algorithmic_bytes_per_launch": nbytes}
 
     res = {"metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,

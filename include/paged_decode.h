@@ -27,6 +27,7 @@
  *   block_table    int32 [B, max_blocks_per_seq]
  *   context_lens   int32 [B]
  *   workspace      caller-owned device scratch for the split-K partials
+ *                  and per-(sequence, head group) arrival counters
  *
  * Ownership: every pointer is borrowed device memory that the caller keeps
  * alive until the work queued on `stream` has finished. The library never
@@ -40,6 +41,15 @@
  * id the first ceil(L / block_size) entries of a row hold is in
  * [0, num_blocks). Entries past those, and cache slots at or after L in the
  * last block, are never read.
+ *
+ * Workspace contract (split plans, S > 1): the first 256 KiB of a
+ * workspace hold arrival counters, at every shape, and must be zero when a
+ * call starts. Zero the workspace once after allocating it
+ * (paged_decode_workspace_init, or any fill with zeros); every call leaves
+ * the counters zero, so the same workspace then serves any later shape.
+ * Calls that share a workspace must not overlap in time (issue them on one
+ * stream, or order them with events): the last workgroup to finish a
+ * (sequence, head group) does the merge, found through those counters.
  *
  * Errors: every entry point returns PD_OK or one of the codes below and
  * writes nothing when it fails before launching. No C++ exception crosses
@@ -96,20 +106,27 @@ int32_t paged_decode_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
 
 /*
  * Workspace bytes paged_decode_attention needs for this shape: 0 when the
- * plan has S = 1, else room for fp32 partial outputs [B, Hq, S, D] and fp32
- * partial log-sum-exps [B, Hq, S]. Returns 0 for an invalid shape too
- * (paged_decode_plan tells the two apart).
+ * plan has S = 1, else 256 KiB of counters plus room for fp32 partial
+ * outputs [B, Hq, S, D] and fp32 partial log-sum-exps [B, Hq, S]. Returns 0
+ * for an invalid shape too (paged_decode_plan tells the two apart).
  */
 size_t paged_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_blocks_per_seq, int32_t block_size,
                                     int32_t dtype);
 
 /*
- * Paged decode attention (see the top of this file). Queues one or two
- * kernels on `stream` (a hipStream_t; NULL is the null stream) and returns
- * without waiting. `workspace` may be NULL when
- * paged_decode_workspace_bytes(...) is 0. `scale` is usually
- * 1/sqrt(D) rounded to float.
+ * Zeroes `workspace_bytes` bytes (rounded down to a multiple of 4) of a
+ * workspace on `stream` with a fill kernel (no memset node, so it is safe
+ * to capture). `workspace` must be 256-byte aligned. PD_OK for 0 bytes.
+ */
+int32_t paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged decode attention (see the top of this file). Queues one kernel on
+ * `stream` (a hipStream_t; NULL is the null stream) and returns without
+ * waiting. `workspace` may be NULL when paged_decode_workspace_bytes(...)
+ * is 0; otherwise it must follow the workspace contract above. `scale` is
+ * usually 1/sqrt(D) rounded to float.
  */
 int32_t paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* context_lens,

@@ -1,7 +1,7 @@
 """MI355X-native paged GQA decode attention.
 
 A thin ctypes binding over the C ABI in ``include/paged_decode.h`` (built as
-``_lib/libpaged_decode.so`` by ``python -m paged_gqa_decode_02_amd.build``).
+``_lib/libpaged_decode.so`` by ``python paged_gqa_decode_02_amd/build.py``).
 The functions keep the C names; they only marshal torch tensors into pointers,
 sizes and the current HIP stream. Every step of the computation runs in the
 library's HIP kernels. Importing this package fails if the library has not
@@ -31,7 +31,7 @@ STATUS_NAMES = {
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"paged_gqa_decode_02_amd: HIP library not built ({LIB_PATH} missing); "
-        "run `python -m paged_gqa_decode_02_amd.build`")
+        "run `python paged_gqa_decode_02_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 _P, _I, _Z, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
@@ -49,6 +49,8 @@ lib.paged_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 lib.paged_decode_workspace_bytes.restype = _Z
 lib.paged_decode_workspace_bytes_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
 lib.paged_decode_workspace_bytes_splits.restype = _Z
+lib.paged_decode_workspace_init.argtypes = [_P, _Z, _P]
+lib.paged_decode_workspace_init.restype = _I
 _ATTN = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
 lib.paged_decode_attention.argtypes = _ATTN
 lib.paged_decode_attention.restype = _I
@@ -101,11 +103,23 @@ def _shape(q, k_cache, block_table):
     return int(B), int(Hq), int(Hkv), int(D), int(block_table.shape[1]), int(bs)
 
 
+def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero a workspace on the current (or given) stream with the library's fill kernel."""
+    st = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
+    rc = lib.paged_decode_workspace_init(workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), handle)
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+
+
 def alloc_workspace(q, k_cache, block_table, num_splits=None) -> torch.Tensor:
-    """A device workspace of the size the call needs (possibly 0 bytes)."""
+    """A zeroed device workspace of the size the call needs (at least 256 bytes)."""
     B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
     n = paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, bs, q.dtype, num_splits)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    paged_decode_workspace_init(ws)
+    return ws
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=None, *,

@@ -1,6 +1,8 @@
 """Build the in-tree HIP library ``_lib/libpaged_decode.so`` for gfx950.
 
-    python -m paged_gqa_decode_02_amd.build
+    python paged_gqa_decode_02_amd/build.py
+
+(run as a file: importing the package would load the library it rebuilds)
 
 Compiles the kernels (``csrc/pd_kernels.hip``) and the host side
 (``csrc/pd_api.cpp``, ``csrc/pd_plan.cpp``) with hipcc into one shared
@@ -38,7 +40,8 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function",
+           "-Wall", "-Wno-unused-function", "-Werror=float-conversion",
+           "-Werror=implicit-int-float-conversion",
            "-I", os.path.join(ROOT, "include")]
     cmd += list(extra_flags or [])
     cmd += [os.path.join(CSRC, s) for s in SOURCES]

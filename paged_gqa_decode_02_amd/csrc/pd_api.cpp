@@ -145,6 +145,17 @@ size_t paged_decode_workspace_bytes_splits(int32_t B, int32_t Hq, int32_t Hkv, i
   }
 }
 
+int32_t paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (workspace_bytes < 4) return PD_OK;
+    if (!workspace) return PD_ERR_NULL;
+    if (!aligned(workspace, 256)) return PD_ERR_ALIGN;
+    return pd::zero_workspace(workspace, workspace_bytes & ~size_t(3), stream);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
 int32_t paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* context_lens,
                                int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,

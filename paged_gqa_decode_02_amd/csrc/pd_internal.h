@@ -15,18 +15,22 @@ struct Shape {
   int32_t B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype;
 };
 
-// How one call is laid out on the GPU.
+// How one call is laid out on the GPU: a grid of (S, Hkv/NH, B) workgroups
+// of NH x NT waves; wave w serves KV head w % NH of its group over token
+// slice w / NH (Pw tokens) of its partition (P tokens).
 struct Plan {
   int32_t splits;            // S: context partitions per (sequence, KV head)
   int32_t partition_tokens;  // P: tokens per partition, a multiple of block_size
-  int32_t waves;             // NW: wavefronts per workgroup (1, 2, 4 or 8)
-  int32_t wave_tokens;       // Pw: tokens per wave, a multiple of block_size,
-                             //     at most 64 blocks; NW * Pw >= P
+  int32_t heads_per_group;   // NH: KV heads per workgroup (1, 2, 4 or 8)
+  int32_t slices;            // NT: token slices per workgroup, NH * NT <= 16
+  int32_t wave_tokens;       // Pw: tokens per slice, a multiple of block_size,
+                             //     at most 256 blocks; NT * Pw >= P
 };
 
-// Most blocks one wave's range may span (one block id per lane).
-constexpr int kMaxWaveBlocks = 64;
-constexpr int kMaxWaves = 8;
+// Most blocks one wave's slice may span (four block ids per lane).
+constexpr int kMaxWaveBlocks = 256;
+// Most waves in a workgroup.
+constexpr int kMaxWaves = 16;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.
 int32_t check_shape(const Shape& s);
@@ -34,9 +38,15 @@ int32_t check_shape(const Shape& s);
 // Split plan: requested_splits <= 0 runs the heuristic, else S is forced.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan);
 
-// Workspace layout for S > 1: fp32 partial outputs [B, Hq, S, D] first,
-// then fp32 partial log2-sum-exps [B, Hq, S], each 256-byte aligned.
+// Workspace layout for S > 1: a fixed region of int32 arrival counters
+// [B, Hkv / NH] (kCounterBytes, the same at every shape, so it only ever
+// holds counters), then fp32 partial outputs [B, Hq, S, D], then fp32
+// partial log2-sum-exps [B, Hq, S], each 256-byte aligned. The counters
+// must be zero when a call starts; every call leaves them zero.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
 size_t partials_bytes(const Shape& s, const Plan& p);
+size_t lse_bytes(const Shape& s, const Plan& p);
 size_t workspace_bytes(const Shape& s, const Plan& p);
 
 // Everything a launch needs, all validated by the caller.
@@ -54,7 +64,10 @@ struct Launch {
   void* stream;
 };
 
-// Queues the decode (and, for S > 1, the merge) kernel; PD_* status code.
+// Queues the decode kernel; PD_* status code.
 int32_t launch(const Launch& l);
+
+// Queues a kernel that zeroes `bytes` (a multiple of 4) at `ws`.
+int32_t zero_workspace(void* ws, size_t bytes, void* stream);
 
 }  // namespace pd

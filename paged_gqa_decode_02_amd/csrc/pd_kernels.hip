@@ -1,4 +1,4 @@
-// Paged GQA decode attention kernels for gfx950 (CDNA4, wave64).
+// Paged GQA decode attention kernel for gfx950 (CDNA4, wave64).
 //
 // Method (Loom Kernels home page, "Supported now": paged MQA/GQA decode with
 // GQA packing and local split-K/LSE): one query token per head attends over
@@ -6,21 +6,26 @@
 // pass over that head's K/V bytes, and a long context is cut into
 // partitions whose normalised partial outputs and log-sum-exps are merged.
 //
-// Decode kernel, one workgroup of NW wave64s per (partition p, KV head g,
-// sequence b); wave w owns a block-aligned range of at most 64 blocks:
+// One kernel. Workgroup (partition p, KV-head group hg, sequence b) has
+// NH x NT wave64s: wave w serves KV head hg*NH + w%NH over token slice w/NH
+// of the partition (a block-aligned range of at most 256 blocks). Waves of
+// the same slice read the same physical blocks, so a workgroup sweeps whole
+// blocks (all heads of a token are one contiguous 2 KiB row group) rather
+// than 256-byte slivers of them.
 //   * lanes: 16 lanes per token row. A 4-token step gives lane
 //     (row = lane/16, sl = lane%16) token `row` of the step and head-dim
 //     elements [8sl, 8sl+8): each 128-bit load instruction of the wave reads
-//     four whole 256-byte rows (eight 128-byte lines).
+//     four whole 256-byte rows.
 //   * K/V come straight from HBM into registers with bounds-checked buffer
 //     loads whose resource is the current physical block (base = pool +
 //     id * block bytes, size = block bytes), so an access cannot leave the
 //     block; lanes past the context get an offset beyond the block and read
-//     zeros with no memory access. Three 8-token stages of loads are kept in
-//     flight while the oldest is computed.
-//   * block ids: each lane loads one block-table entry of the wave's range
-//     before the context length is known; a stage takes its (wave-uniform)
-//     id with v_readlane, so addresses are scalar.
+//     zeros with no memory access. Three 8-token stages of loads stay in
+//     flight while the oldest is computed; the loads use the streaming (nt)
+//     cache policy since every K/V byte is read once.
+//   * block ids: each lane loads up to four block-table entries of the
+//     wave's range before the context length is known; a stage takes its
+//     (wave-uniform) id with v_readlane, so addresses are scalar.
 //   * scores: q stays as packed 16-bit pairs; v_dot2_f32_{bf16,f16} gives
 //     fp32 sums of products with no conversion of K, a 4-step DPP butterfly
 //     sums the 16 lanes of a row, and one multiply by scale*log2(e) puts the
@@ -29,13 +34,16 @@
 //     a ballot finds a score above it (then permlane16/32 swaps reduce over
 //     the 4 rows and the accumulators are rescaled); each lane keeps its own
 //     partial sum l and accumulator acc[4][8].
-//   * end of range: a reduce-scatter over the 4 rows (permlane32_swap, then
-//     permlane16_swap) leaves head r's 128 sums in row r; the waves of a
-//     workgroup are merged through LDS.
-//   * S == 1 writes `out` rounded to the dtype; S > 1 writes fp32 o_p and
-//     the partition's log2-sum-exp.
-// Merge kernel, one workgroup per (query head, sequence): the LSE merge over
-// the ceil(L/P) non-empty partitions in fixed order p = 0..n-1.
+//   * end of slice: a reduce-scatter over the 4 rows (permlane32_swap, then
+//     permlane16_swap) leaves query head r's 128 sums in row r; the NT slices
+//     of a head are merged through LDS.
+//   * S == 1: the workgroup writes `out`, rounded to the dtype.
+//   * S > 1: the workgroup writes its fp32 partial output and log2-sum-exp
+//     with write-through (device-coherent) stores, then bumps a per
+//     (sequence, head group) counter; the workgroup that brings it to the
+//     number of non-empty partitions merges them in fixed order p = 0..n-1
+//     with L2-bypassing loads, writes `out` and resets the counter to zero.
+//     No device-wide cache flush is involved.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -51,12 +59,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = pd::kHeadDim;  // 128
-constexpr int kMaxWaveBlocks = pd::kMaxWaveBlocks;
 constexpr int G = pd::kGroup;    // 4
-constexpr uint32_t kRowBytes = D * 2;        // one token row of one KV head
+constexpr int kMaxWaves = pd::kMaxWaves;
+constexpr int kIdRegs = pd::kMaxWaveBlocks / 64;  // block ids per lane
+constexpr uint32_t kRowBytes = D * 2;          // one token row of one KV head
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
-constexpr int kRsrcWord3 = 0x00020000;        // raw 32-bit buffer, gfx9 data format
-constexpr int kStream = 2;                    // cache policy "nt": K/V bytes are read once
+constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 data format
+constexpr int kStream = 2;                     // cache policy "nt": read once
+constexpr int kCoherent = 16;                  // cache policy "sc1": device-coherent
 
 struct KArgs {
   const uint16_t* q;
@@ -65,14 +75,17 @@ struct KArgs {
   const int32_t* bt;
   const int32_t* cl;
   void* out;
-  float* o_part;    // [B, Hq, S, D]
-  float* lse_part;  // [B, Hq, S], log2 domain
+  float* o_part;      // [B, Hq, S, D]
+  float* lse_part;    // [B, Hq, S], log2 domain
+  int32_t* counters;  // [B, Hkv / NH], at the start of the workspace
   int32_t Hkv;
   int32_t MB;
   int32_t S;
   int32_t P;
-  int32_t Pw;          // tokens per wave, a multiple of the block size, <= 64 blocks
-  float scale_log2;   // scale * log2(e)
+  int32_t Pw;  // tokens per slice, a multiple of the block size, <= 256 blocks
+  int32_t NH;  // KV heads per workgroup
+  int32_t NT;  // token slices per workgroup
+  float scale_log2;    // scale * log2(e)
   uint32_t blk_bytes;  // block_size * Hkv * D * 2
 };
 
@@ -116,10 +129,19 @@ __device__ __forceinline__ float dpp(float x) {
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
                                                         0xf, 0xf, false));
 }
-constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141;   // lane i <-> 7-i within each 8 lanes
-constexpr int kRowMirror = 0x140;    // lane i <-> 15-i within the row
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;   // lane i <-> 15-i within the row
+
+// Sum over the 16 lanes of a token row; every lane gets the total.
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  return x;
+}
 
 __device__ __forceinline__ float swap16_lo(float a, float b, float* b_out) {
   auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
@@ -133,23 +155,6 @@ __device__ __forceinline__ float swap32_lo(float a, float b, float* b_out) {
                                             __builtin_bit_cast(uint32_t, b), false, false);
   *b_out = __builtin_bit_cast(float, (uint32_t)r[1]);
   return __builtin_bit_cast(float, (uint32_t)r[0]);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, int32_t id,
-                                                             uint32_t blk_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + (int64_t)id * (int64_t)blk_bytes), (short)0, (int)blk_bytes, kRsrcWord3);
-}
-
-// Sum over the 16 lanes of a token row; every lane gets the total.
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kHalfMirror>(x);
-  x += dpp<kRowMirror>(x);
-  return x;
 }
 
 // Maximum / sum over the 4 token rows of the wave (lanes with equal lane%16).
@@ -169,9 +174,17 @@ __device__ __forceinline__ float sum_rows(float x) {
   return a + y;
 }
 
-// Per-lane state of one wave's online softmax over its token range.
-// Lane (row r = lane/16, sub-lane sl = lane%16) owns token r of each 4-token
-// step and head-dim elements [8sl, 8sl+8) of the group's 4 query heads.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Per-lane state of one wave's online softmax over its token slice.
 template <bool BF16>
 struct WaveState {
   u32x4 q[G];       // this lane's 8 q elements of each head, packed pairs
@@ -213,8 +226,7 @@ __device__ __forceinline__ void stage_compute(WaveState<BF16>& st, const u32x4 (
       st.l[h] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
-      st.m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                              __builtin_bit_cast(int, mn)));  // uniform
+      st.m[h] = uniform_f(mn);
     }
   }
 #pragma unroll
@@ -234,30 +246,55 @@ __device__ __forceinline__ void stage_compute(WaveState<BF16>& st, const u32x4 (
   }
 }
 
-// Decode kernel: one workgroup of NW waves per (partition p, KV head g,
-// sequence b); wave w owns tokens [p*P + w*Pw, +Pw) of the partition, at most
-// 64 blocks. BS: block size. DEPTH: stages of loads kept in flight.
-template <bool BF16, int BS, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+// Block id number idx (< 256, wave-uniform) of the wave's range.
+__device__ __forceinline__ int pick_id(const int (&ids)[kIdRegs], int idx) {
+  const int l = idx & 63;
+  const int c = idx >> 6;
+  int r = __builtin_amdgcn_readlane(ids[0], l);
+#pragma unroll
+  for (int i = 1; i < kIdRegs; ++i) {
+    const int x = __builtin_amdgcn_readlane(ids[i], l);
+    r = c == i ? x : r;
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_row(uint16_t* o, const float (&r)[8], float inv) {
+  u32x4 wv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = pack2<BF16>(r[2 * i] * inv, r[2 * i + 1] * inv);
+  *(u32x4*)o = wv;
+}
+
+template <bool BF16, int BS, bool SPLIT>
+__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void pd_decode_kernel(const KArgs a) {
   constexpr int DEPTH = 3;
   constexpr int kStageTok = 8;
   const int p = blockIdx.x;
-  const int g = blockIdx.y;
+  const int hg = blockIdx.y;
   const int b = blockIdx.z;
   const int Hq = a.Hkv * G;
+  const int nw = a.NH * a.NT;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = w % a.NH;  // KV head within the workgroup's group
+  const int ts = w / a.NH;  // token slice
+  const int g = hg * a.NH + hl;
   const int row = lane >> 4;
   const int sl = lane & 15;
 
   const int t0 = p * a.P;
-  const int tw0 = t0 + w * a.Pw;
+  const int tw0 = t0 + ts * a.Pw;
   const int bi0 = tw0 / BS;
-  // block ids of the wave's whole range, fetched before the context length
+  // block ids of the wave's whole slice, fetched before the context length
   // is known (entries past the live ones are loaded but never used)
   const int nb_max = min(a.Pw / BS, a.MB - bi0);
-  const int myid = lane < nb_max ? a.bt[(size_t)b * a.MB + bi0 + lane] : 0;
+  const int32_t* btrow = a.bt + (size_t)b * a.MB + bi0;
+  int ids[kIdRegs];
+#pragma unroll
+  for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
 
   WaveState<BF16> st;
   const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G) * D + sl * 8;
@@ -276,14 +313,22 @@ void pd_decode_kernel(const KArgs a) {
   const int L = __builtin_amdgcn_readfirstlane(a.cl[b]);
   if constexpr (!SPLIT) {
     if (L <= 0) {
-      // empty context: a zero row for each of the group's heads
-      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G) * D;
-      for (int i = threadIdx.x; i < G * D / 8; i += NW * 64)
+      // empty context: zero rows for every query head of the group
+      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * a.NH * G) * D;
+      for (int i = threadIdx.x; i < a.NH * G * D / 8; i += nw * 64)
         *(u32x4*)(o + i * 8) = u32x4{0u, 0u, 0u, 0u};
       return;
     }
   } else {
-    if (t0 >= L) return;  // the merge reads only the ceil(L/P) non-empty partitions
+    if (t0 >= L) {  // empty partition: neither counted nor merged
+      if (L <= 0 && p == 0) {
+        // empty context: partition 0 writes the zero rows, no merge runs
+        uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * a.NH * G) * D;
+        for (int i = threadIdx.x; i < a.NH * G * D / 8; i += nw * 64)
+          *(u32x4*)(o + i * 8) = u32x4{0u, 0u, 0u, 0u};
+      }
+      return;
+    }
   }
   const int tw1 = min(min(tw0 + a.Pw, t0 + a.P), L);
   const int nst = __builtin_amdgcn_readfirstlane(
@@ -294,15 +339,15 @@ void pd_decode_kernel(const KArgs a) {
 
   u32x4 kb[DEPTH][2], vb[DEPTH][2];
   // Queue the loads of stage j. Straight-line code, always four loads, so
-  // the wait counts stay exact: past the range (j >= nst) every lane's token
+  // the wait counts stay exact: past the slice (j >= nst) every lane's token
   // is >= tw1 and its offset is out of the block, and the block id is forced
   // to 0, so those loads read nothing.
   auto issue = [&](int j, u32x4(&kr)[2], u32x4(&vr)[2]) {
-    const int tok = kStageTok * j;                        // offset in the wave range
-    const int idx = min(tok / BS, kMaxWaveBlocks - 1);
-    const int id = __builtin_amdgcn_readlane(myid, idx) * (int)(j < nst);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, id, a.blk_bytes);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, id, a.blk_bytes);
+    const int tok = kStageTok * j;  // offset in the slice
+    const int idx = min(tok / BS, kIdRegs * 64 - 1);
+    const int id = pick_id(ids, idx) * (int)(j < nst);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (int64_t)id * a.blk_bytes, a.blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const uint32_t base = (uint32_t)(tok % BS) * tok_bytes + lane_off;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -358,124 +403,152 @@ void pd_decode_kernel(const KArgs a) {
   float m_r = row == 0 ? st.m[0] : row == 1 ? st.m[1] : row == 2 ? st.m[2] : st.m[3];
   float l_r = row == 0 ? st.l[0] : row == 1 ? st.l[1] : row == 2 ? st.l[2] : st.l[3];
 
-  if constexpr (NW > 1) {
-    // ---- merge the NW waves through LDS; wave 0 finishes
-    __shared__ f32x4 s_acc[NW][G][D / 4];
-    __shared__ float s_m[NW][G];
-    __shared__ float s_l[NW][G];
-    s_acc[w][row][2 * sl] = f32x4{r2[0], r2[1], r2[2], r2[3]};
-    s_acc[w][row][2 * sl + 1] = f32x4{r2[4], r2[5], r2[6], r2[7]};
+  // ---- merge the NT slices of each head through LDS; slice 0 keeps the result
+  if (a.NT > 1) {
+    // dynamic LDS, sized by the host to the workgroup's waves:
+    // acc [nw][G][D] floats, then m [nw][G], then l [nw][G]
+    extern __shared__ __align__(16) float pd_lds[];
+    f32x4* s_acc = (f32x4*)pd_lds;                  // [(w*G + row)*(D/4) + i]
+    float* s_m = pd_lds + nw * G * D;               // [w*G + row]
+    float* s_l = s_m + nw * G;
+    s_acc[(w * G + row) * (D / 4) + 2 * sl] = f32x4{r2[0], r2[1], r2[2], r2[3]};
+    s_acc[(w * G + row) * (D / 4) + 2 * sl + 1] = f32x4{r2[4], r2[5], r2[6], r2[7]};
     if (sl == 0) {
-      s_m[w][row] = m_r;
-      s_l[w][row] = l_r;
+      s_m[w * G + row] = m_r;
+      s_l[w * G + row] = l_r;
     }
     __syncthreads();
-    if (w != 0) return;
-    float M = s_m[0][row];
+    if (ts == 0) {
+      float M = m_r;
+      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + row]);
+      float den = 0.f;
 #pragma unroll
-    for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i][row]);
-    float den = 0.f;
+      for (int e = 0; e < 8; ++e) r2[e] = 0.f;
+      for (int i = 0; i < a.NT; ++i) {
+        const int wi = (i * a.NH + hl) * G + row;
+        const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
+        den = fmaf(wt, s_l[wi], den);
+        const f32x4 x0 = s_acc[wi * (D / 4) + 2 * sl];
+        const f32x4 x1 = s_acc[wi * (D / 4) + 2 * sl + 1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r2[e] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          r2[e] = fmaf(wt, x0[e], r2[e]);
+          r2[4 + e] = fmaf(wt, x1[e], r2[4 + e]);
+        }
+      }
+      m_r = M;
+      l_r = den;
+    }
+  }
+  const bool owner = ts == 0;
+  const int hq = g * G + row;  // query head of this lane's row
+
+  if constexpr (!SPLIT) {
+    if (owner)
+      store_row<BF16>((uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8, r2, 1.0f / l_r);
+    return;
+  } else {
+    // ---- publish this partition's (o_p, lse_p), write-through
+    const size_t slot0 = ((size_t)b * Hq + (size_t)g * G) * a.S;  // (row 0, partition 0)
+    const uint32_t rows_bytes = (uint32_t)G * a.S * D * 4;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o_part + slot0 * D, rows_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse_part + slot0, (uint32_t)G * a.S * 4);
+    if (owner) {
+      // the raw buffer builtins move 32-bit words: floats go through bit casts
+      const float inv = 1.0f / l_r;
+      const uint32_t off = ((uint32_t)(row * a.S + p) * D + sl * 8) * 4;
+      const f32x4 o0 = {r2[0] * inv, r2[1] * inv, r2[2] * inv, r2[3] * inv};
+      const f32x4 o1 = {r2[4] * inv, r2[5] * inv, r2[6] * inv, r2[7] * inv};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), ro, off, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), ro, off + 16, 0,
+                                             kCoherent);
+      if (sl == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r)), rl,
+            (uint32_t)(row * a.S + p) * 4, 0, kCoherent);
+    }
+    // the stores are complete (and past every non-coherent cache) before the
+    // counter moves
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
+    const int n_live = (L + a.P - 1) / a.P;
+    if (threadIdx.x == 0) {
+      int32_t* cnt = a.counters + (size_t)b * (a.Hkv / a.NH) + hg;
+      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == n_live - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last || !owner) return;
+
+    // ---- last workgroup: LSE merge over the n_live partitions, in order
+    constexpr int kBatch = 8;
+    float M = -INFINITY, den = 0.f, acc[8];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const float wt = exp2_fast(s_m[i][row] - M);  // 0 for a wave with no tokens
-      den = fmaf(wt, s_l[i][row], den);
-      const f32x4 x0 = s_acc[i][row][2 * sl];
-      const f32x4 x1 = s_acc[i][row][2 * sl + 1];
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int i0 = 0; i0 < n_live; i0 += kBatch) {
+      float lse[kBatch];
+      f32x4 o0[kBatch], o1[kBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r2[e] = fmaf(wt, x0[e], r2[e]);
-        r2[4 + e] = fmaf(wt, x1[e], r2[4 + e]);
+      for (int u = 0; u < kBatch; ++u) {
+        // partitions past n_live read zeros and are skipped below
+        const bool ok = i0 + u < n_live;
+        const uint32_t slot = (uint32_t)(row * a.S + i0 + u);
+        const uint32_t off = ok ? (slot * D + sl * 8) * 4 : kOutOfBlock;
+        o0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
+                                                                                kCoherent));
+        o1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16, 0,
+                                                                                kCoherent));
+        lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
+      }
+      float bm = M;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
+      const float alpha = exp2_fast(M - bm);  // 0 on the first batch
+      den *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      M = bm;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (i0 + u < n_live) {
+          const float wt = exp2_fast(lse[u] - M);
+          den += wt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] = fmaf(wt, o0[u][e], acc[e]);
+            acc[4 + e] = fmaf(wt, o1[u][e], acc[4 + e]);
+          }
+        }
       }
     }
-    m_r = M;
-    l_r = den;
-  }
-
-  // ---- epilogue: row r of wave 0 holds head g*G + r, elements [8sl, 8sl+8)
-  const int hq = g * G + row;
-  const float inv = 1.0f / l_r;
-  if constexpr (!SPLIT) {
-    uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8;
-    u32x4 wv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = pack2<BF16>(r2[2 * i] * inv, r2[2 * i + 1] * inv);
-    *(u32x4*)o = wv;
-  } else {
-    const size_t slot = ((size_t)b * Hq + hq) * a.S + p;
-    float* o = a.o_part + slot * D + sl * 8;
-    *(f32x4*)o = f32x4{r2[0] * inv, r2[1] * inv, r2[2] * inv, r2[3] * inv};
-    *(f32x4*)(o + 4) = f32x4{r2[4] * inv, r2[5] * inv, r2[6] * inv, r2[7] * inv};
-    if (sl == 0) a.lse_part[slot] = m_r + __builtin_amdgcn_logf(l_r);
+    store_row<BF16>((uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8, acc, 1.0f / den);
   }
 }
 
-// LSE merge: one workgroup of D threads per (query head, sequence).
-template <bool BF16>
-__global__ __launch_bounds__(D) void pd_merge_kernel(const float* __restrict__ o_part,
-                                                     const float* __restrict__ lse_part,
-                                                     const int32_t* __restrict__ cl,
-                                                     void* __restrict__ out, int32_t S,
-                                                     int32_t P) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int Hq = gridDim.x;
-  const int d = threadIdx.x;
-  const int L = cl[b];
-  const int n = L > 0 ? (L + P - 1) / P : 0;
-  const size_t rowi = (size_t)b * Hq + h;
-  const float* lp = lse_part + rowi * S;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, lp[i]);
-  float num = 0.f, den = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float wt = exp2_fast(lp[i] - M);
-    den += wt;
-    num = fmaf(wt, o_part[(rowi * S + i) * D + d], num);
-  }
-  const float r = n > 0 ? num / den : 0.f;
-  ((uint16_t*)out)[rowi * D + d] = to_bits<BF16>(r);
-}
-
-template <bool BF16, int BS, int NW, bool SPLIT>
-hipError_t launch_decode(const KArgs& ka, dim3 grid, hipStream_t st) {
-  void* args[] = {(void*)&ka};
-  return hipLaunchKernel((const void*)&pd_decode_kernel<BF16, BS, NW, SPLIT>, grid,
-                         dim3(NW * 64), args, 0, st);
+// Zero the workspace (the split path's counters must start at zero).
+__global__ void pd_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
 template <bool BF16, int BS, bool SPLIT>
-hipError_t pick_waves(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
-  switch (nw) {
-    case 8: return launch_decode<BF16, BS, 8, SPLIT>(ka, grid, st);
-    case 4: return launch_decode<BF16, BS, 4, SPLIT>(ka, grid, st);
-    case 2: return launch_decode<BF16, BS, 2, SPLIT>(ka, grid, st);
-    default: return launch_decode<BF16, BS, 1, SPLIT>(ka, grid, st);
-  }
+hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
+  void* args[] = {(void*)&ka};
+  const size_t lds = ka.NT > 1 ? (size_t)nw * G * (D + 2) * sizeof(float) : 0;
+  return hipLaunchKernel((const void*)&pd_decode_kernel<BF16, BS, SPLIT>, grid, dim3(nw * 64),
+                         args, lds, st);
 }
 
 template <bool BF16, bool SPLIT>
 hipError_t pick_block(const KArgs& ka, dim3 grid, int bs, int nw, hipStream_t st) {
-  return bs == 32 ? pick_waves<BF16, 32, SPLIT>(ka, grid, nw, st)
-                  : pick_waves<BF16, 16, SPLIT>(ka, grid, nw, st);
-}
-
-template <bool BF16>
-hipError_t launch_all(const KArgs& ka, const pd::Launch& l, hipStream_t st) {
-  const dim3 grid(l.plan.splits, l.shape.Hkv, l.shape.B);
-  if (l.plan.splits == 1)
-    return pick_block<BF16, false>(ka, grid, l.shape.block_size, l.plan.waves, st);
-  hipError_t e = pick_block<BF16, true>(ka, grid, l.shape.block_size, l.plan.waves, st);
-  if (e != hipSuccess) return e;
-  const float* op = ka.o_part;
-  const float* lp = ka.lse_part;
-  const int32_t* cl = ka.cl;
-  void* out = ka.out;
-  int32_t S = l.plan.splits, P = l.plan.partition_tokens;
-  void* args[] = {(void*)&op, (void*)&lp, (void*)&cl, (void*)&out, (void*)&S, (void*)&P};
-  return hipLaunchKernel((const void*)&pd_merge_kernel<BF16>, dim3(l.shape.Hq, l.shape.B),
-                         dim3(D), args, 0, st);
+  return bs == 32 ? launch_decode<BF16, 32, SPLIT>(ka, grid, nw, st)
+                  : launch_decode<BF16, 16, SPLIT>(ka, grid, nw, st);
 }
 
 }  // namespace
@@ -492,20 +565,46 @@ int32_t launch(const Launch& l) {
   ka.out = l.out;
   ka.o_part = nullptr;
   ka.lse_part = nullptr;
+  ka.counters = nullptr;
   if (l.plan.splits > 1) {
-    ka.o_part = (float*)l.workspace;
-    ka.lse_part = (float*)((char*)l.workspace + partials_bytes(l.shape, l.plan));
+    char* ws = (char*)l.workspace;
+    ka.counters = (int32_t*)ws;
+    ka.o_part = (float*)(ws + kCounterBytes);
+    ka.lse_part = (float*)(ws + kCounterBytes + partials_bytes(l.shape, l.plan));
   }
   ka.Hkv = l.shape.Hkv;
   ka.MB = l.shape.max_blocks_per_seq;
   ka.S = l.plan.splits;
   ka.P = l.plan.partition_tokens;
   ka.Pw = l.plan.wave_tokens;
+  ka.NH = l.plan.heads_per_group;
+  ka.NT = l.plan.slices;
   ka.scale_log2 = l.scale * 1.4426950408889634f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv * kRowBytes;
+  const dim3 grid(l.plan.splits, l.shape.Hkv / l.plan.heads_per_group, l.shape.B);
+  const int nw = l.plan.heads_per_group * l.plan.slices;
   hipStream_t st = (hipStream_t)l.stream;
-  hipError_t e = l.shape.dtype == PD_DTYPE_BF16 ? launch_all<true>(ka, l, st)
-                                                : launch_all<false>(ka, l, st);
+  const bool split = l.plan.splits > 1;
+  hipError_t e;
+  if (l.shape.dtype == PD_DTYPE_BF16)
+    e = split ? pick_block<true, true>(ka, grid, l.shape.block_size, nw, st)
+              : pick_block<true, false>(ka, grid, l.shape.block_size, nw, st);
+  else
+    e = split ? pick_block<false, true>(ka, grid, l.shape.block_size, nw, st)
+              : pick_block<false, false>(ka, grid, l.shape.block_size, nw, st);
+  return e == hipSuccess ? PD_OK : PD_ERR_HIP;
+}
+
+int32_t zero_workspace(void* ws, size_t bytes, void* stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return PD_OK;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  uint32_t* p = (uint32_t*)ws;
+  size_t nn = n;
+  void* args[] = {(void*)&p, (void*)&nn};
+  hipError_t e = hipLaunchKernel((const void*)&pd_zero_kernel, dim3((unsigned)blocks), dim3(256),
+                                 args, 0, (hipStream_t)stream);
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

@@ -15,9 +15,11 @@ namespace pd {
 
 namespace {
 
-constexpr int64_t kCUs = 256;                 // MI355X compute units
-constexpr int64_t kWavesPerCU = 16;           // resident decode waves per CU (4 per SIMD)
-constexpr int64_t kTargetWaves = kCUs * kWavesPerCU;
+#ifndef PD_WAVES_PER_CU
+#define PD_WAVES_PER_CU 16  // resident decode waves per CU (4 per SIMD at 128 VGPRs)
+#endif
+constexpr int64_t kCUs = 256;  // MI355X compute units
+constexpr int64_t kTargetWaves = kCUs * PD_WAVES_PER_CU;
 constexpr int64_t kMaxSplits = 1 << 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -46,48 +48,58 @@ int32_t check_shape(const Shape& s) {
 }
 
 // The plan cuts each sequence's context (up to cap = max_blocks_per_seq *
-// block_size tokens) into S partitions of P tokens, each served by one
-// workgroup of NW waves of Pw tokens. Pw is sized so that the whole grid is
-// about one full round of resident waves (kTargetWaves): long work keeps
-// every wave streaming, short work keeps every wave's loads in flight at
-// once. NW is the fewest waves (a power of two, at most 8) that cover the
-// context at that Pw; S follows. A forced S fixes P instead and sizes NW
-// and Pw to it.
+// block_size tokens) into S partitions of P tokens, each served by
+// workgroups of NH KV heads x NT token slices of Pw tokens. Pw is sized so
+// that the whole grid is about one full round of resident waves
+// (kTargetWaves): long work keeps every wave streaming, short work keeps
+// every wave's loads in flight at once. Slices of one head merge in LDS,
+// partitions merge across workgroups, so the plan first gives a head all the
+// slices it needs inside one workgroup (NT up to 16, S = 1 when they fit),
+// then fills the rest of the 16-wave workgroup with more KV heads (NH, a
+// power of two dividing Hkv, at most 8) so that its waves read whole blocks.
+// A forced S fixes P instead and sizes NT and Pw to it.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
   const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
   const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
+  int64_t nh_max = 8;
+  while (s.Hkv % nh_max != 0) nh_max >>= 1;
   const int64_t pw_max = kMaxWaveBlocks * bs;
   int64_t pw_target = round_up(ceil_div(units * cap, kTargetWaves), bs);
   if (pw_target > pw_max) pw_target = pw_max;
-  int64_t P, nw, pw;
+  int64_t P, nt, pw;
   if (requested_splits > 0) {
-    int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
+    const int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
     P = round_up(ceil_div(cap, want), bs);
-    nw = pow2_ceil(ceil_div(P, pw_target));
-    if (nw > kMaxWaves) nw = kMaxWaves;
-    pw = round_up(ceil_div(P, nw), bs);
-    if (pw > pw_max) {  // a partition cannot exceed NW x 64 blocks: split more
-      pw = pw_max;
-      P = nw * pw;
-    }
+    nt = pow2_ceil(ceil_div(P, pw_target));
   } else {
-    nw = pow2_ceil(ceil_div(cap, pw_target));
-    if (nw > kMaxWaves) nw = kMaxWaves;
-    pw = pw_target;
-    P = nw * pw;
-    if (P > cap) {  // one partition: trim the waves to the context
-      pw = round_up(ceil_div(cap, nw), bs);
-      P = nw * pw;
-    }
+    nt = pow2_ceil(ceil_div(cap, pw_target));
+    if (nt > kMaxWaves) nt = kMaxWaves;
+    const int64_t s0 = ceil_div(cap, nt * pw_target);
+    P = round_up(ceil_div(cap, s0), bs);
   }
-  int64_t S = ceil_div(cap, P);
+  if (nt > kMaxWaves) nt = kMaxWaves;
+  pw = round_up(ceil_div(P, nt), bs);
+  if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more
+    pw = pw_max;
+    P = nt * pw;
+  }
+  nt = ceil_div(P, pw);  // drop slices that would start past the partition
+  int64_t nh = nh_max;
+  while (nh > 1 && nh * nt > kMaxWaves) nh >>= 1;
+#ifdef PD_FORCE_NH
+  if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0 && PD_FORCE_NH * nt <= kMaxWaves) nh = PD_FORCE_NH;
+#endif
+  const int64_t S = ceil_div(cap, P);
   if (S > kMaxSplits) return PD_ERR_SHAPE;
+  // the split path keeps one arrival counter per (sequence, head group)
+  if (S > 1 && (int64_t)s.B * (s.Hkv / nh) > kMaxCounters) return PD_ERR_UNSUPPORTED;
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
-  plan->waves = (int32_t)nw;
+  plan->heads_per_group = (int32_t)nh;
+  plan->slices = (int32_t)nt;
   plan->wave_tokens = (int32_t)pw;
   return PD_OK;
 }
@@ -96,9 +108,13 @@ size_t partials_bytes(const Shape& s, const Plan& p) {
   return align256((size_t)s.B * s.Hq * p.splits * s.D * sizeof(float));
 }
 
+size_t lse_bytes(const Shape& s, const Plan& p) {
+  return align256((size_t)s.B * s.Hq * p.splits * sizeof(float));
+}
+
 size_t workspace_bytes(const Shape& s, const Plan& p) {
   if (p.splits <= 1) return 0;
-  return partials_bytes(s, p) + align256((size_t)s.B * s.Hq * p.splits * sizeof(float));
+  return kCounterBytes + partials_bytes(s, p) + lse_bytes(s, p);
 }
 
 }  // namespace pd

@@ -108,7 +108,8 @@ BASE = 1 << 32
 
 
 def call(**over):
-    B, Hq, Hkv, D, MB, bs = 2, 32, 8, 128, 4, 16
+    # one block per sequence: the plan has S = 1, so no workspace is needed
+    B, Hq, Hkv, D, MB, bs = 2, 32, 8, 128, 1, 16
     a = dict(q=BASE, k=BASE + (1 << 24), v=BASE + (2 << 24), bt=BASE + (3 << 24),
              cl=BASE + (3 << 24) + 4096, MB=MB, out=BASE + (4 << 24), B=B, Hq=Hq, Hkv=Hkv,
              D=D, bs=bs, scale=0.0883883, dtype=BF16, ws=0, ws_bytes=0, stream=0, splits=None)
@@ -170,3 +171,21 @@ def test_split_path_needs_a_big_enough_aligned_disjoint_workspace():
 def test_empty_batch_is_a_no_op():
     # B = 0: nothing to compute, no pointer needed, nothing launched
     assert call(B=0, q=0, k=0, v=0, bt=0, cl=0, out=0) == CODES["PD_OK"]
+
+
+def test_workspace_init_argument_errors():
+    f = pd.lib.paged_decode_workspace_init
+    assert f(0, 0, 0) == CODES["PD_OK"]          # nothing to do
+    assert f(BASE, 3, 0) == CODES["PD_OK"]       # under one word: nothing to do
+    assert f(0, 1024, 0) == CODES["PD_ERR_NULL"]
+    assert f(BASE + 128, 1024, 0) == CODES["PD_ERR_ALIGN"]
+
+
+@pytest.mark.parametrize("B,L,bs", SHAPES)
+def test_workspace_holds_partials_lse_and_counters(B, L, bs):
+    MB = -(-L // bs)
+    S, P = pd.paged_decode_plan(B, 32, 8, 128, MB, bs, BF16)
+    if S > 1:
+        a256 = lambda x: (x + 255) // 256 * 256
+        need = 256 * 1024 + a256(B * 32 * S * 128 * 4) + a256(B * 32 * S * 4)
+        assert pd.paged_decode_workspace_bytes(B, 32, 8, 128, MB, bs, BF16) >= need

@@ -52,6 +52,7 @@ def test_only_out_is_written_and_canaries_survive():
 def test_out_and_workspace_reuse_across_shapes():
     out = None
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    pd.paged_decode_workspace_init(ws)
     for B, L in ((8, 1024), (1, 128), (8, 1024), (2, 512)):
         c = workloads.splitk(B, L, seed=23 + B + L)
         q, k, v, bt, cl = device_case(c)
@@ -89,8 +90,8 @@ def test_graph_replay_reads_context_lens_at_replay_time():
         torch.cuda.synchronize()
         got = out_bits(out)
         # eager call on the same metadata must agree bitwise
-        eager = out_bits(pd.paged_decode_attention(q, k, v, bt, cl, scale=c.scale, workspace=
-                                                   torch.empty_like(ws)))
+        eager = out_bits(pd.paged_decode_attention(q, k, v, bt, cl, scale=c.scale,
+                                                   workspace=pd.alloc_workspace(q, k, bt)))
         torch.cuda.synchronize()
         assert np.array_equal(got, eager), rep
         c.context_lens[:] = lens
@@ -108,3 +109,41 @@ def test_wrong_dtype_and_shapes_are_rejected_by_the_binding():
     with pytest.raises(pd.PagedDecodeError) as e:
         pd.paged_decode_attention(q, k, v, bt, cl, q)  # out aliases q
     assert e.value.code == 5
+
+
+def _counter_region(ws):
+    """The first 256 KiB of a workspace: the split path's arrival counters."""
+    return ws[:256 * 1024]
+
+
+@pytest.mark.parametrize("splits", [None, 2, 7, 32])
+def test_split_counters_return_to_zero_and_partials_never_go_stale(splits):
+    # back-to-back calls on one workspace with different data and different
+    # context lengths (so a different workgroup finishes last each time):
+    # each must match its own oracle, and the counters must end at zero
+    cases = [workloads.make_case("stale", 6, lens, dtype="bf16", block_size=16, seed=40 + i,
+                                 max_blocks_per_seq=64)
+             for i, lens in enumerate([[1024, 1000, 513, 64, 17, 1], [700, 1024, 1, 900, 333, 1024],
+                                       [1, 2, 3, 1024, 1023, 512]])]
+    S, _ = pd.paged_decode_plan(6, 32, 8, 128, 64, 16, torch.bfloat16, splits)
+    assert S > 1
+    ws = torch.empty(pd.paged_decode_workspace_bytes(6, 32, 8, 128, 64, 16, torch.bfloat16, splits)
+                     + 4096, dtype=torch.uint8, device="cuda")
+    pd.paged_decode_workspace_init(ws)
+    outs = []
+    for c in cases * 2:
+        q, k, v, bt, cl = device_case(c)
+        outs.append((c, pd.paged_decode_attention(q, k, v, bt, cl, scale=c.scale, workspace=ws,
+                                                  num_splits=splits)))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(_counter_region(ws)).item() == 0
+    for c, o in outs:
+        ref, _ = oracle.attention_case(c)
+        compare(out_bits(o), ref, "bf16", what=f"stale S={splits}")
+
+
+def test_workspace_init_zeroes_the_whole_workspace():
+    ws = torch.full((3 << 20,), 0xAB, dtype=torch.uint8, device="cuda")
+    pd.paged_decode_workspace_init(ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws).item() == 0
