@@ -321,7 +321,8 @@ def main():
            "roofline": roof}
     if not args.no_others:
         others = {}
-        for name in ("splitk_B8_L1024", "splitk_B1_L1024", "ragged", "short_B32_L64_bf16_bs16"):
+        for name in ("splitk_B8_L1024", "splitk_B8_L4096", "splitk_B32_L1024", "splitk_B1_L1024",
+                     "ragged", "short_B32_L64_bf16_bs16", "tiny"):
             others[name] = bench_other(name, torch, pd)
         res["others"] = others
     if not args.no_cpu_baseline:

@@ -15,11 +15,11 @@ namespace pd {
 
 namespace {
 
-#ifndef PD_WAVES_PER_CU
-#define PD_WAVES_PER_CU 16  // resident decode waves per CU (4 per SIMD at 128 VGPRs)
-#endif
-constexpr int64_t kCUs = 256;  // MI355X compute units
-constexpr int64_t kTargetWaves = kCUs * PD_WAVES_PER_CU;
+constexpr int64_t kWavesSmall = 1024;       // waves for latency-bound calls
+constexpr int64_t kWavesLarge = 2048;       // waves for streaming calls
+constexpr int64_t kSmallWork = 128 * 1024;  // token-heads up to which a call is latency-bound
+constexpr int64_t kPairWork = 256 * 1024;   // token-heads from which KV heads go in pairs
+constexpr int64_t kSlices = 4;              // token slices per head in a workgroup
 constexpr int64_t kMaxSplits = 1 << 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -48,48 +48,56 @@ int32_t check_shape(const Shape& s) {
 }
 
 // The plan cuts each sequence's context (up to cap = max_blocks_per_seq *
-// block_size tokens) into S partitions of P tokens, each served by
-// workgroups of NH KV heads x NT token slices of Pw tokens. Pw is sized so
-// that the whole grid is about one full round of resident waves
-// (kTargetWaves): long work keeps every wave streaming, short work keeps
-// every wave's loads in flight at once. Slices of one head merge in LDS,
-// partitions merge across workgroups, so the plan first gives a head all the
-// slices it needs inside one workgroup (NT up to 16, S = 1 when they fit),
-// then fills the rest of the 16-wave workgroup with more KV heads (NH, a
-// power of two dividing Hkv, at most 8) so that its waves read whole blocks.
-// A forced S fixes P instead and sizes NT and Pw to it.
+// block_size tokens) into S partitions of P tokens, each served by one
+// workgroup per group of NH KV heads, made of NH x NT waves; a wave covers
+// one slice of Pw tokens (block aligned, at most 256 blocks) of one head.
+// Slices of a head merge in LDS, partitions merge across workgroups.
+//
+// The rule was fitted to sweeps of every (NH, NT, S) on an MI355X over the
+// decode workloads (batch 1..64, contexts 16..4,096, block sizes 16/32):
+//   * work = B * Hkv * cap token-heads sets the number of waves: about
+//     kWavesSmall for work up to kSmallWork (latency-bound calls: all of a
+//     wave's loads go out at once), kWavesLarge beyond (streaming calls:
+//     two resident waves per SIMD, each with a long slice, beat four with
+//     short ones), so Pw = work / waves, at least one block;
+//   * NT = 4 slices per head (NT = 8 or 16 only added waiting for the
+//     slowest wave; NT = 1 or 2 added cross-workgroup merges);
+//   * NH = 2 heads per workgroup once work reaches kPairWork (the pair reads
+//     512 contiguous bytes per token), else 1.
+// S and P follow from NT * Pw. A forced S fixes P instead and cuts it into
+// up to NT slices.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
   const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
   const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
-  int64_t nh_max = 8;
-  while (s.Hkv % nh_max != 0) nh_max >>= 1;
+  const int64_t work = units * cap;
   const int64_t pw_max = kMaxWaveBlocks * bs;
-  int64_t pw_target = round_up(ceil_div(units * cap, kTargetWaves), bs);
-  if (pw_target > pw_max) pw_target = pw_max;
-  int64_t P, nt, pw;
+  const int64_t waves = work <= kSmallWork ? kWavesSmall : kWavesLarge;
+  int64_t nh = work >= kPairWork && s.Hkv % 2 == 0 ? 2 : 1;
+  int64_t nt = kSlices;
+  int64_t pw, P;
   if (requested_splits > 0) {
     const int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
     P = round_up(ceil_div(cap, want), bs);
-    nt = pow2_ceil(ceil_div(P, pw_target));
   } else {
-    nt = pow2_ceil(ceil_div(cap, pw_target));
-    if (nt > kMaxWaves) nt = kMaxWaves;
-    const int64_t s0 = ceil_div(cap, nt * pw_target);
-    P = round_up(ceil_div(cap, s0), bs);
+    pw = round_up(ceil_div(work, waves), bs);
+    if (pw > pw_max) pw = pw_max;
+    P = nt * pw;
+    if (P > cap) P = cap;  // one partition
   }
-  if (nt > kMaxWaves) nt = kMaxWaves;
+#ifdef PD_FORCE_NT  // tuning builds only: fix the slices per workgroup
+  if (PD_FORCE_NT > 0) nt = PD_FORCE_NT;
+#endif
+  if (nt > P / bs) nt = P / bs;  // every slice at least one block
   pw = round_up(ceil_div(P, nt), bs);
   if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more
     pw = pw_max;
     P = nt * pw;
   }
   nt = ceil_div(P, pw);  // drop slices that would start past the partition
-  int64_t nh = nh_max;
-  while (nh > 1 && nh * nt > kMaxWaves) nh >>= 1;
-#ifdef PD_FORCE_NH
+#ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
   if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0 && PD_FORCE_NH * nt <= kMaxWaves) nh = PD_FORCE_NH;
 #endif
   const int64_t S = ceil_div(cap, P);
