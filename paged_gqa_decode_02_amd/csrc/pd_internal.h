@@ -29,8 +29,13 @@ struct Plan {
 
 // Most blocks one wave's slice may span (four block ids per lane).
 constexpr int kMaxWaveBlocks = 256;
-// Most waves in a workgroup.
-constexpr int kMaxWaves = 16;
+// Waves per SIMD the decode kernel's registers are sized for (4: 128
+// VGPRs, 2: 256 VGPRs), and with it the most waves in a workgroup (a
+// workgroup must fit on one CU of 4 SIMDs).
+#ifndef PD_WAVES_PER_SIMD
+#define PD_WAVES_PER_SIMD 4
+#endif
+constexpr int kMaxWaves = 4 * PD_WAVES_PER_SIMD;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.
 int32_t check_shape(const Shape& s);

@@ -267,10 +267,17 @@ __device__ __forceinline__ void store_row(uint16_t* o, const float (&r)[8], floa
   *(u32x4*)o = wv;
 }
 
+// Stages of K/V loads in flight per wave (the waves per SIMD the register
+// budget is sized for, and with it the largest workgroup, is in pd_internal.h).
+#ifndef PD_DEPTH
+#define PD_DEPTH 3
+#endif
+
 template <bool BF16, int BS, bool SPLIT>
-__global__ __launch_bounds__(kMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(kMaxWaves * 64)
+__attribute__((amdgpu_waves_per_eu(PD_WAVES_PER_SIMD, 8)))
 void pd_decode_kernel(const KArgs a) {
-  constexpr int DEPTH = 3;
+  constexpr int DEPTH = PD_DEPTH;
   constexpr int kStageTok = 8;
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
