@@ -22,20 +22,16 @@ struct Plan {
   int32_t splits;            // S: context partitions per (sequence, KV head)
   int32_t partition_tokens;  // P: tokens per partition, a multiple of block_size
   int32_t heads_per_group;   // NH: KV heads per workgroup (1, 2, 4 or 8)
-  int32_t slices;            // NT: token slices per workgroup, NH * NT <= 16
+  int32_t slices;            // NT: token slices per workgroup, NH * NT <= 8
   int32_t wave_tokens;       // Pw: tokens per slice, a multiple of block_size,
                              //     at most 256 blocks; NT * Pw >= P
 };
 
 // Most blocks one wave's slice may span (four block ids per lane).
 constexpr int kMaxWaveBlocks = 256;
-// Waves per SIMD the decode kernel's registers are sized for (4: 128
-// VGPRs, 2: 256 VGPRs), and with it the most waves in a workgroup (a
-// workgroup must fit on one CU of 4 SIMDs).
-#ifndef PD_WAVES_PER_SIMD
-#define PD_WAVES_PER_SIMD 4
-#endif
-constexpr int kMaxWaves = 4 * PD_WAVES_PER_SIMD;
+// Most waves in a workgroup: each wave holds two 16-token K/V tiles in LDS
+// (17 KiB), so 8 waves fill 136 KiB of a CU's 160 KiB.
+constexpr int kMaxWaves = 8;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.
 int32_t check_shape(const Shape& s);

@@ -12,28 +12,27 @@
 // the same slice read the same physical blocks, so a workgroup sweeps whole
 // blocks (all heads of a token are one contiguous 2 KiB row group) rather
 // than 256-byte slivers of them.
-//   * lanes: 16 lanes per token row. A 4-token step gives lane
-//     (row = lane/16, sl = lane%16) token `row` of the step and head-dim
-//     elements [8sl, 8sl+8): each 128-bit load instruction of the wave reads
-//     four whole 256-byte rows.
-//   * K/V come straight from HBM into registers with bounds-checked buffer
-//     loads whose resource is the current physical block (base = pool +
-//     id * block bytes, size = block bytes), so an access cannot leave the
-//     block; lanes past the context get an offset beyond the block and read
-//     zeros with no memory access. Three 8-token stages of loads stay in
-//     flight while the oldest is computed; the loads use the streaming (nt)
-//     cache policy since every K/V byte is read once.
+//   * K/V move in tiles of 16 tokens from HBM straight into LDS with
+//     bounds-checked buffer loads whose resource is the current physical
+//     block (base = pool + id * block bytes, size = block bytes), so an
+//     access cannot leave the block; lanes past the context get an offset
+//     beyond the block and read nothing. Each 128-bit load instruction of a
+//     wave reads four whole 256-byte rows. One or two tiles stay in flight
+//     while the oldest is computed; the loads use the streaming (nt) cache
+//     policy since every K/V byte is read once.
 //   * block ids: each lane loads up to four block-table entries of the
-//     wave's range before the context length is known; a stage takes its
+//     wave's range before the context length is known; a tile takes its
 //     (wave-uniform) id with v_readlane, so addresses are scalar.
-//   * scores: q stays as packed 16-bit pairs; v_dot2_f32_{bf16,f16} gives
-//     fp32 sums of products with no conversion of K, a 4-step DPP butterfly
-//     sums the 16 lanes of a row, and one multiply by scale*log2(e) puts the
-//     softmax in base 2 (v_exp_f32).
-//   * softmax: a wave-uniform running maximum per head that only moves when
-//     a ballot finds a score above it (then permlane16/32 swaps reduce over
-//     the 4 rows and the accumulators are rescaled); each lane keeps its own
-//     partial sum l and accumulator acc[4][8].
+//   * scores: q . k for the 16 tokens of a tile and the 4 query heads of the
+//     KV head are one 16x16 output of four v_mfma_f32_16x16x32 (bf16 or
+//     f16 inputs, exact products, fp32 sums), read from LDS in the operand
+//     order; one multiply by scale*log2(e) puts the softmax in base 2
+//     (v_exp_f32).
+//   * softmax: per head, a running maximum that only moves when a ballot
+//     finds a tile maximum above it (then the accumulators are rescaled);
+//     each lane keeps its own partial sum of weights.
+//   * PV: fp32 FMA of each weight with the 16-bit V values widened exactly,
+//     acc[4 heads][8 dims] per lane.
 //   * end of slice: a reduce-scatter over the 4 rows (permlane32_swap, then
 //     permlane16_swap) leaves query head r's 128 sums in row r; the NT slices
 //     of a head are merged through LDS.
@@ -55,12 +54,13 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = pd::kHeadDim;  // 128
 constexpr int G = pd::kGroup;    // 4
-constexpr int kMaxWaves = pd::kMaxWaves;
 constexpr int kIdRegs = pd::kMaxWaveBlocks / 64;  // block ids per lane
 constexpr uint32_t kRowBytes = D * 2;          // one token row of one KV head
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
@@ -88,16 +88,6 @@ struct KArgs {
   float scale_log2;    // scale * log2(e)
   uint32_t blk_bytes;  // block_size * Hkv * D * 2
 };
-
-template <bool BF16>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-  else
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
-                                  __builtin_bit_cast(f16x2_t, b), c, false);
-}
 
 template <bool BF16>
 __device__ __forceinline__ float lo_f(uint32_t u) {
@@ -128,19 +118,6 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
                                                         0xf, 0xf, false));
-}
-constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
-constexpr int kRowMirror = 0x140;   // lane i <-> 15-i within the row
-
-// Sum over the 16 lanes of a token row; every lane gets the total.
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kHalfMirror>(x);
-  x += dpp<kRowMirror>(x);
-  return x;
 }
 
 __device__ __forceinline__ float swap16_lo(float a, float b, float* b_out) {
@@ -184,63 +161,121 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kRsrcWord3);
 }
 
-// Per-lane state of one wave's online softmax over its token slice.
+// Tiles of 16 tokens of one KV head go from HBM straight into LDS (buffer
+// loads with the LDS destination, no VGPRs held while in flight). Within a
+// tile, load instruction n moves tokens 4n..4n+3: lane (row, sl) reads 16
+// bytes of token 4n + row, chunk (sl - row) mod 16 of its 256-byte row, so
+// every 16 lanes still read one whole row, and the LDS copy of the row is
+// rotated by `row` chunks; the four 1 KiB groups of a tile are 1088 bytes
+// apart. With that placement both LDS read patterns below touch 16 (and any
+// 8 consecutive lanes 8) distinct 16-byte bank groups.
+constexpr int kTileTok = 16;
+constexpr uint32_t kLdsGroup = 4 * kRowBytes + 64;  // 4 token rows + pad
+constexpr uint32_t kLdsTensor = 4 * kLdsGroup;      // one tile of K or of V
+constexpr uint32_t kLdsTile = 2 * kLdsTensor;       // K then V
+
+// Tile buffers per wave (tiles in flight while one is computed: kNBuf - 1).
+#ifndef PD_NBUF
+#define PD_NBUF 2
+#endif
+constexpr int kNBuf = PD_NBUF;
+static_assert(kNBuf >= 2 && kNBuf <= 3, "two or three tile buffers");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that waits for vmcnt <= n and nothing else.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * 8);
+
 template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// x of lane H of the caller's lane quad (DPP quad_perm [H,H,H,H]).
+template <int H>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp<H * 0x55>(x);
+}
+
+// Per-lane state of one wave's online softmax over its token slice.
 struct WaveState {
-  u32x4 q[G];       // this lane's 8 q elements of each head, packed pairs
-  float acc[G][8];  // unnormalised PV sums of the lane's token row
-  float l[G];       // sum of weights of the lane's token row
-  float m[G];       // wave-uniform running maximum (log2 domain)
+  float acc[G][8];  // unnormalised PV sums: head h, dims [8sl, 8sl+8), this row's tokens
+  float lsum;       // sum of weights of head lane%4 over this row's tokens
+  float m;          // running maximum (log2 domain) of head lane%4
 };
 
-// One stage = two 4-token steps = 8 consecutive tokens of one block.
-// kb[i], vb[i]: this lane's 16 bytes of the K / V row of step i's token.
+// One 16-token tile, already in LDS at kt (K) and vt (V).
+//   scores: the tile is the A operand of four 16x16x32 MFMAs (row = token
+//     lane%16, k = head dims 32s + 8(lane/16) .. +8), q the B operand (column
+//     = lane%16, query head (lane%16)%4, the 4 heads repeated 4 times), so
+//     lane l gets the scores of tokens 4(l/16) + i, i < 4, for head l%4, the
+//     same in all four lanes of a quad position;
+//   softmax: per head, max over the tile (4 registers, then the 4 rows), the
+//     running maximum only moves when a ballot finds a tile maximum above it;
+//   PV: step k gives row r token 4r + k, lane (r, sl) its dims [8sl, 8sl+8);
+//     the weight of head h is broadcast from lane h of the quad. fp32 FMA.
 template <bool BF16>
-__device__ __forceinline__ void stage_compute(WaveState<BF16>& st, const u32x4 (&kb)[2],
-                                              const u32x4 (&vb)[2], bool valid0, bool valid1,
-                                              float c) {
-  float s[2][G];
+__device__ __forceinline__ void tile_compute(WaveState& st, const char* kt, const char* vt,
+                                             const u32x4 (&qb)[4], const uint32_t (&koff)[4],
+                                             const uint32_t (&voff)[4], int tok_row0, int tw1,
+                                             bool partial, float c) {
+  u32x4 ka[4], vv[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const bool ok = i == 0 ? valid0 : valid1;
+  for (int s = 0; s < 4; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d = 0.f;
+  for (int k = 0; k < 4; ++k) vv[k] = *(const u32x4*)(vt + voff[k]);
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d = dot2<BF16>(st.q[h][e], kb[i][e], d);
-      d = sum16(d);
-      s[i][h] = ok ? d * c : -INFINITY;
+  for (int s = 0; s < 4; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[s], sc);
+  float s_[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
+  if (partial) {
+    // tokens past the slice: no weight, and whatever their LDS rows hold is
+    // never multiplied in
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tok_row0 + i < tw1;
+      s_[i] = ok ? s_[i] : -INFINITY;
+      vv[i] = ok ? vv[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // the running maximum only moves when some score exceeds it (wave vote)
-  uint64_t above = 0;
+  const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
+  if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
+    const float mn = fmaxf(st.m, tm);
+    const float alpha = exp2_fast(st.m - mn);  // 1 where the maximum stays, 0 from -inf
+    st.m = mn;
+    st.lsum *= alpha;
+    const float al[G] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
+                         quad_bcast<3>(alpha)};
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h) above |= __builtin_amdgcn_ballot_w64(s[i][h] > st.m[h]);
-  if (above != 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = fmaxf(st.m[h], max_rows(fmaxf(s[0][h], s[1][h])));
-      const float alpha = exp2_fast(st.m[h] - mn);  // 0 when m was -inf
-      st.l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
-      st.m[h] = uniform_f(mn);
-    }
+      for (int e = 0; e < 8; ++e) st.acc[h][e] *= al[h];
   }
+  float pr[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    // a token past the range reads zeros (out-of-block offset), and its
-    // weight is exp2(-inf) = 0, so it adds nothing
+  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m);
+  st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float pr = exp2_fast(s[i][h] - st.m[h]);
-      st.l[h] += pr;
+  for (int k = 0; k < 4; ++k) {
+    const float ph[G] = {quad_bcast<0>(pr[k]), quad_bcast<1>(pr[k]), quad_bcast<2>(pr[k]),
+                         quad_bcast<3>(pr[k])};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        st.acc[h][2 * e] = fmaf(pr, lo_f<BF16>(vb[i][e]), st.acc[h][2 * e]);
-        st.acc[h][2 * e + 1] = fmaf(pr, hi_f<BF16>(vb[i][e]), st.acc[h][2 * e + 1]);
+    for (int e = 0; e < 4; ++e) {
+      const float v0 = lo_f<BF16>(vv[k][e]);
+      const float v1 = hi_f<BF16>(vv[k][e]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        st.acc[h][2 * e] = fmaf(ph[h], v0, st.acc[h][2 * e]);
+        st.acc[h][2 * e + 1] = fmaf(ph[h], v1, st.acc[h][2 * e + 1]);
       }
     }
   }
@@ -267,18 +302,14 @@ __device__ __forceinline__ void store_row(uint16_t* o, const float (&r)[8], floa
   *(u32x4*)o = wv;
 }
 
-// Stages of K/V loads in flight per wave (the waves per SIMD the register
-// budget is sized for, and with it the largest workgroup, is in pd_internal.h).
-#ifndef PD_DEPTH
-#define PD_DEPTH 3
-#endif
-
-template <bool BF16, int BS, bool SPLIT>
-__global__ __launch_bounds__(kMaxWaves * 64)
-__attribute__((amdgpu_waves_per_eu(PD_WAVES_PER_SIMD, 8)))
+template <bool BF16, int BS, bool SPLIT, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
-  constexpr int DEPTH = PD_DEPTH;
-  constexpr int kStageTok = 8;
+  // one array per tile buffer, so the compiler can wait for exactly the
+  // loads of the buffer about to be read
+  __shared__ __align__(16) char lds0[NW * kLdsTile];
+  __shared__ __align__(16) char lds1[NW * kLdsTile];
+  __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kLdsTile : 16];
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int b = blockIdx.z;
@@ -291,10 +322,22 @@ void pd_decode_kernel(const KArgs a) {
   const int g = hg * a.NH + hl;
   const int row = lane >> 4;
   const int sl = lane & 15;
+  auto tile_buf = [&](int d) -> char* {
+    char* base = d == 0 ? lds0 : d == 1 ? lds1 : lds2;
+    return base + w * kLdsTile;
+  };
 
   const int t0 = p * a.P;
   const int tw0 = t0 + ts * a.Pw;
   const int bi0 = tw0 / BS;
+  // q as the MFMA B operand: head lane%4, dims 32s + 8(lane/16) .. +8.
+  // Loaded before the block ids, so that waiting for the ids (which the
+  // first K/V addresses need) also covers q, and no later wait has to drain
+  // the tile loads.
+  u32x4 qb[4];
+  const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G + (lane & 3)) * D + 8 * row;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qb[s] = *(const u32x4*)(qp + 32 * s);
   // block ids of the wave's whole slice, fetched before the context length
   // is known (entries past the live ones are loaded but never used)
   const int nb_max = min(a.Pw / BS, a.MB - bi0);
@@ -302,18 +345,13 @@ void pd_decode_kernel(const KArgs a) {
   int ids[kIdRegs];
 #pragma unroll
   for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
-
-  WaveState<BF16> st;
-  const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G) * D + sl * 8;
+  WaveState st;
+  st.lsum = 0.f;
+  st.m = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) st.q[h] = *(const u32x4*)(qp + h * D);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.l[h] = 0.f;
-    st.m[h] = -INFINITY;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
-  }
 
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // loop bounds and block addresses in scalar registers
@@ -339,56 +377,88 @@ void pd_decode_kernel(const KArgs a) {
   }
   const int tw1 = min(min(tw0 + a.Pw, t0 + a.P), L);
   const int nst = __builtin_amdgcn_readfirstlane(
-      tw0 < tw1 ? (tw1 - tw0 + kStageTok - 1) / kStageTok : 0);
+      tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
-  const uint32_t lane_off = ((uint32_t)row * a.Hkv + g) * kRowBytes + sl * 16u;
   const uint32_t tok_bytes = a.Hkv * kRowBytes;
+  // global offset of this lane's 16 bytes in load instruction 0 of a tile
+  const uint32_t lane_off = (uint32_t)row * tok_bytes + (uint32_t)g * kRowBytes +
+                            (uint32_t)((sl - row) & 15) * 16u;
+  // LDS offsets of the two read patterns (see the tile layout above)
+  uint32_t koff[4], voff[4];
+  {
+    const int t = lane & 15, r = t & 3;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      koff[s] = (uint32_t)(t >> 2) * kLdsGroup + (uint32_t)r * kRowBytes +
+                16u * (uint32_t)((4 * s + row + r) & 15);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      voff[k] = kLdsTensor + (uint32_t)row * kLdsGroup + (uint32_t)k * kRowBytes +
+                16u * (uint32_t)((sl + k) & 15);
+  }
 
-  u32x4 kb[DEPTH][2], vb[DEPTH][2];
-  // Queue the loads of stage j. Straight-line code, always four loads, so
-  // the wait counts stay exact: past the slice (j >= nst) every lane's token
-  // is >= tw1 and its offset is out of the block, and the block id is forced
-  // to 0, so those loads read nothing.
-  auto issue = [&](int j, u32x4(&kr)[2], u32x4(&vr)[2]) {
-    const int tok = kStageTok * j;  // offset in the slice
+  // Queue the 8 loads of tile j into buffer d. Straight-line, always eight
+  // loads, so the wait counts stay exact: past the slice (j >= nst) every
+  // lane's token is >= tw1 and its offset is out of the block, and the block
+  // id is forced to 0, so those loads read nothing.
+  auto issue = [&](int j, int d) {
+    const int tok = kTileTok * j;  // offset in the slice
     const int idx = min(tok / BS, kIdRegs * 64 - 1);
     const int id = pick_id(ids, idx) * (int)(j < nst);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const uint32_t base = (uint32_t)(tok % BS) * tok_bytes + lane_off;
+    char* kt = tile_buf(d);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = tw0 + tok + 4 * i + row < tw1;
-      // the whole offset goes in the vector operand, which the range check covers
-      const uint32_t vo = ok ? base + 4u * i * tok_bytes : kOutOfBlock;
-      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, vo, 0, kStream);
-      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kStream);
+    for (int n = 0; n < 4; ++n) {
+      const bool ok = tw0 + tok + 4 * n + row < tw1;
+      const uint32_t vo = ok ? base + 4u * n * tok_bytes : kOutOfBlock;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + n * kLdsGroup), 16, vo, 0, 0,
+                                               kStream);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + kLdsTensor + n * kLdsGroup),
+                                               16, vo, 0, 0, kStream);
     }
   };
 
-  // The loads must leave in stage order, in the prologue as in the loop, so
-  // that the wait for stage j never has to drain the later stages.
+  // The loads leave in tile order, in the prologue as in the loop, so that
+  // the wait for tile j never has to drain the later tiles.
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    issue(d, kb[d], vb[d]);
+  for (int d = 0; d < kNBuf; ++d) {
+    issue(d, d);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int j0 = 0; j0 < nst; j0 += DEPTH) {
+  for (int j0 = 0; j0 < nst; j0 += kNBuf) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
+    for (int d = 0; d < kNBuf; ++d) {
       const int j = j0 + d;
+      // tile j's loads are the oldest in flight: wait until only the later
+      // tiles' (kNBuf - 1) * 8 loads are outstanding. Explicit, because the
+      // compiler does not always see that these LDS reads depend on them.
+      __builtin_amdgcn_s_waitcnt(kWaitTile);
+      __builtin_amdgcn_sched_barrier(0);
       if (j < nst) {
-        const int tok = tw0 + kStageTok * j + row;
-        stage_compute<BF16>(st, kb[d], vb[d], tok < tw1, tok + 4 < tw1, c);
+        const int tile0 = tw0 + kTileTok * j;
+        const char* kt = tile_buf(d);
+        tile_compute<BF16>(st, kt, kt, qb, koff, voff, tile0 + 4 * row, tw1,
+                           tile0 + kTileTok > tw1, c);
       }
-      issue(j + DEPTH, kb[d], vb[d]);
+      issue(j + kNBuf, d);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // every tile load (the trailing ones read nothing) has landed before the
+  // tile buffers are reused below
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- reduce over the 4 token rows of the wave
+  const float lt = sum_rows(st.lsum);
+  float mh[G], lh[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) st.l[h] = sum_rows(st.l[h]);
+  for (int h = 0; h < G; ++h) {
+    // lane h holds head h (every lane with lane%4 == h does)
+    mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.m), h));
+    lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt), h));
+  }
   // reduce-scatter: rows 0-1 keep heads {0,1}, rows 2-3 keep heads {2,3} ...
   float r1[2][8];
 #pragma unroll
@@ -407,16 +477,15 @@ void pd_decode_kernel(const KArgs a) {
     const float x = swap16_lo(r1[0][e], r1[1][e], &y);
     r2[e] = x + y;
   }
-  float m_r = row == 0 ? st.m[0] : row == 1 ? st.m[1] : row == 2 ? st.m[2] : st.m[3];
-  float l_r = row == 0 ? st.l[0] : row == 1 ? st.l[1] : row == 2 ? st.l[2] : st.l[3];
+  float m_r = row == 0 ? mh[0] : row == 1 ? mh[1] : row == 2 ? mh[2] : mh[3];
+  float l_r = row == 0 ? lh[0] : row == 1 ? lh[1] : row == 2 ? lh[2] : lh[3];
 
-  // ---- merge the NT slices of each head through LDS; slice 0 keeps the result
+  // ---- merge the NT slices of each head through LDS (the first tile
+  // buffer); slice 0 keeps the result
   if (a.NT > 1) {
-    // dynamic LDS, sized by the host to the workgroup's waves:
-    // acc [nw][G][D] floats, then m [nw][G], then l [nw][G]
-    extern __shared__ __align__(16) float pd_lds[];
-    f32x4* s_acc = (f32x4*)pd_lds;                  // [(w*G + row)*(D/4) + i]
-    float* s_m = pd_lds + nw * G * D;               // [w*G + row]
+    __syncthreads();  // every wave is done with its tile buffers
+    f32x4* s_acc = (f32x4*)lds0;                    // [(w*G + row)*(D/4) + i]
+    float* s_m = (float*)lds0 + nw * G * D;         // [w*G + row]
     float* s_l = s_m + nw * G;
     s_acc[(w * G + row) * (D / 4) + 2 * sl] = f32x4{r2[0], r2[1], r2[2], r2[3]};
     s_acc[(w * G + row) * (D / 4) + 2 * sl + 1] = f32x4{r2[4], r2[5], r2[6], r2[7]};
@@ -547,9 +616,10 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
 template <bool BF16, int BS, bool SPLIT>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   void* args[] = {(void*)&ka};
-  const size_t lds = ka.NT > 1 ? (size_t)nw * G * (D + 2) * sizeof(float) : 0;
-  return hipLaunchKernel((const void*)&pd_decode_kernel<BF16, BS, SPLIT>, grid, dim3(nw * 64),
-                         args, lds, st);
+  // the LDS tile buffers are sized for the largest workgroup of the instance
+  const void* f = nw <= 4 ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4>
+                          : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8>;
+  return hipLaunchKernel(f, grid, dim3(nw * 64), args, 0, st);
 }
 
 template <bool BF16, bool SPLIT>
@@ -590,6 +660,9 @@ int32_t launch(const Launch& l) {
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv * kRowBytes;
   const dim3 grid(l.plan.splits, l.shape.Hkv / l.plan.heads_per_group, l.shape.B);
   const int nw = l.plan.heads_per_group * l.plan.slices;
+  // each wave owns kLdsTile bytes of every tile buffer of its workgroup
+  if (nw < 1 || nw > kMaxWaves || l.shape.Hkv % l.plan.heads_per_group != 0)
+    return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;
   hipError_t e;
