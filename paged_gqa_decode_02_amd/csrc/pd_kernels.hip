@@ -164,29 +164,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Tiles of 16 tokens of one KV head go from HBM straight into LDS (buffer
 // loads with the LDS destination, no VGPRs held while in flight). Within a
 // tile, load instruction n moves tokens 4n..4n+3: lane (row, sl) reads 16
-// bytes of token 4n + row, chunk (sl - row) mod 16 of its 256-byte row, so
-// every 16 lanes still read one whole row, and the LDS copy of the row is
-// rotated by `row` chunks; the four 1 KiB groups of a tile are 1088 bytes
-// apart. With that placement both LDS read patterns below touch 16 (and any
-// 8 consecutive lanes 8) distinct 16-byte bank groups.
+// bytes of token 4n + row, so every 16 lanes read one whole 256-byte row.
+// Which 16-byte chunk a lane takes is rotated per row, and the four 1 KiB
+// groups of a tile are padded apart, so that the LDS reads below touch
+// distinct bank groups:
+//   K: lane sl takes chunk (sl - row) mod 16, groups 1088 bytes apart; read
+//      back 16 bytes per lane in MFMA operand order (token lane%16, chunk
+//      4s + lane/16): any 16 (and any 8 consecutive) lanes hit distinct
+//      16-byte bank groups;
+//   V: lane sl takes chunk (sl - 2 row) mod 16, groups 1152 bytes apart;
+//      read back with the transposing ds_read_b64_tr_b16, 8 bytes per lane
+//      (token 4(lane/16) + (lane%16)/4, dims 4(lane%4) of a 16-dim block):
+//      each 32 lanes hit distinct 8-byte bank slots.
 constexpr int kTileTok = 16;
-constexpr uint32_t kLdsGroup = 4 * kRowBytes + 64;  // 4 token rows + pad
-constexpr uint32_t kLdsTensor = 4 * kLdsGroup;      // one tile of K or of V
-constexpr uint32_t kLdsTile = 2 * kLdsTensor;       // K then V
+constexpr uint32_t kKGroup = 4 * kRowBytes + 64;
+constexpr uint32_t kVGroup = 4 * kRowBytes + 128;
+constexpr uint32_t kKTile = 4 * kKGroup;             // 4352
+constexpr uint32_t kLdsTile = kKTile + 4 * kVGroup;  // K then V: 8960
 
-// Tile buffers per wave (tiles in flight while one is computed: kNBuf - 1).
+// Tile buffers per wave (tiles in flight while one is computed: buffers - 1),
+// as many as fit the 160 KiB of LDS for the workgroup size, up to PD_NBUF.
 #ifndef PD_NBUF
 #define PD_NBUF 2
 #endif
-constexpr int kNBuf = PD_NBUF;
-static_assert(kNBuf >= 2 && kNBuf <= 3, "two or three tile buffers");
+constexpr uint32_t kLdsBytes = 160 * 1024;
+constexpr int tile_buffers(int nw) {
+  return PD_NBUF >= 3 && 3 * nw * kLdsTile <= kLdsBytes ? 3 : 2;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr_t;
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8) that waits for vmcnt <= n and nothing else.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * 8);
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -198,39 +210,70 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// x of lane H of the caller's lane quad (DPP quad_perm [H,H,H,H]).
-template <int H>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return dpp<H * 0x55>(x);
+// Softmax weights enter the PV products as a sum of 16-bit terms: hi =
+// round(p), lo = round(p - hi), and for bf16 a third term lo2 = round(p - hi
+// - lo) (each difference is exact in fp32), so p is carried to about 2^-27
+// (bf16, three 8-bit terms) or 2^-22 (f16, two 11-bit terms) relative, the
+// level of the fp32 arithmetic around it. For f16 the weights are scaled by
+// 2^8 (the scale cancels in acc / l), which keeps lo of small weights out of
+// the subnormal range.
+template <bool BF16>
+struct Weights {
+  u32x4 hi_lo;   // k 0..3: hi of the lane's 4 tokens, k 4..7: lo
+  uint32_t lo2[2];  // bf16 only: the third term of the 4 tokens
+};
+template <bool BF16>
+__device__ __forceinline__ Weights<BF16> split_weights(const float (&p)[4]) {
+  Weights<BF16> w;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t hi = pack2<BF16>(p[2 * i], p[2 * i + 1]);
+    const float r0 = p[2 * i] - lo_f<BF16>(hi);
+    const float r1 = p[2 * i + 1] - hi_f<BF16>(hi);
+    const uint32_t lo = pack2<BF16>(r0, r1);
+    w.hi_lo[i] = hi;
+    w.hi_lo[2 + i] = lo;
+    if constexpr (BF16) w.lo2[i] = pack2<BF16>(r0 - lo_f<BF16>(lo), r1 - hi_f<BF16>(lo));
+  }
+  return w;
 }
-
-// Per-lane state of one wave's online softmax over its token slice.
-struct WaveState {
-  float acc[G][8];  // unnormalised PV sums: head h, dims [8sl, 8sl+8), this row's tokens
-  float lsum;       // sum of weights of head lane%4 over this row's tokens
-  float m;          // running maximum (log2 domain) of head lane%4
+template <bool BF16>
+struct WeightBias {
+  static constexpr float log2 = BF16 ? 0.f : 8.f;
 };
 
-// One 16-token tile, already in LDS at kt (K) and vt (V).
-//   scores: the tile is the A operand of four 16x16x32 MFMAs (row = token
-//     lane%16, k = head dims 32s + 8(lane/16) .. +8), q the B operand (column
-//     = lane%16, query head (lane%16)%4, the 4 heads repeated 4 times), so
-//     lane l gets the scores of tokens 4(l/16) + i, i < 4, for head l%4, the
-//     same in all four lanes of a quad position;
-//   softmax: per head, max over the tile (4 registers, then the 4 rows), the
+// Per-lane state of one wave's online softmax over its token slice. Lane l
+// follows query head l%4 of the KV head; acc[m][i] is its unnormalised PV
+// sum for dim 16m + 4(l/16) + i (the four lane quads of a row hold copies).
+struct WaveState {
+  f32x4 acc[8];
+  float lsum;  // sum of weights over the tokens of this lane's row
+  float m;     // running maximum (log2 domain)
+};
+
+// One 16-token tile, already in LDS at kt (K) and kt + kKTile (V).
+//   scores: the K tile is the A operand of four 16x16x32 MFMAs (row = token
+//     lane%16, k = dims 32s + 8(lane/16) .. +8), q the B operand (column =
+//     lane%16 -> query head (lane%16)%4, the 4 heads repeated 4 times): lane
+//     l gets the scores of tokens 4(l/16) + i, i < 4, for head l%4;
+//   softmax: the tile maximum per head (4 registers, then the 4 rows); the
 //     running maximum only moves when a ballot finds a tile maximum above it;
-//   PV: step k gives row r token 4r + k, lane (r, sl) its dims [8sl, 8sl+8);
-//     the weight of head h is broadcast from lane h of the quad. fp32 FMA.
+//   PV: per 16-dim block, one 16x16x32 MFMA with A = V^T (row = dim, k = the
+//     lane's 4 tokens, twice) and B = those tokens' weights (hi in k 0..3,
+//     lo in k 4..7), which is the layout the scores came out in; for bf16 a
+//     second one adds the third weight term.
 template <bool BF16>
-__device__ __forceinline__ void tile_compute(WaveState& st, const char* kt, const char* vt,
+__device__ __forceinline__ void tile_compute(WaveState& st, const char* kt,
                                              const u32x4 (&qb)[4], const uint32_t (&koff)[4],
-                                             const uint32_t (&voff)[4], int tok_row0, int tw1,
+                                             const uint32_t (&voff)[8], int tok_row0, int tw1,
                                              bool partial, float c) {
-  u32x4 ka[4], vv[4];
+  u32x4 ka[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
+  v4i16_t vt[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) vv[k] = *(const u32x4*)(vt + voff[k]);
+  for (int m = 0; m < 8; ++m)
+    vt[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr_t)(kt + voff[m]));
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[s], sc);
@@ -238,14 +281,15 @@ __device__ __forceinline__ void tile_compute(WaveState& st, const char* kt, cons
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
   if (partial) {
-    // tokens past the slice: no weight, and whatever their LDS rows hold is
-    // never multiplied in
+    // tokens past the slice get no weight, and their V rows (whatever the
+    // LDS holds there) are replaced by zeros
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = tok_row0 + i < tw1;
-      s_[i] = ok ? s_[i] : -INFINITY;
-      vv[i] = ok ? vv[i] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
+    // V^T element i of every block is token 4(lane/16) + i as well
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vt[m][i] = tok_row0 + i < tw1 ? vt[m][i] : (short)0;
   }
   const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
   if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
@@ -253,31 +297,22 @@ __device__ __forceinline__ void tile_compute(WaveState& st, const char* kt, cons
     const float alpha = exp2_fast(st.m - mn);  // 1 where the maximum stays, 0 from -inf
     st.m = mn;
     st.lsum *= alpha;
-    const float al[G] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha),
-                         quad_bcast<3>(alpha)};
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[h][e] *= al[h];
+    for (int m = 0; m < 8; ++m) st.acc[m] *= alpha;
   }
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m);
+  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m + WeightBias<BF16>::log2);
   st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  const Weights<BF16> wb = split_weights<BF16>(pr);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float ph[G] = {quad_bcast<0>(pr[k]), quad_bcast<1>(pr[k]), quad_bcast<2>(pr[k]),
-                         quad_bcast<3>(pr[k])};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v0 = lo_f<BF16>(vv[k][e]);
-      const float v1 = hi_f<BF16>(vv[k][e]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        st.acc[h][2 * e] = fmaf(ph[h], v0, st.acc[h][2 * e]);
-        st.acc[h][2 * e + 1] = fmaf(ph[h], v1, st.acc[h][2 * e + 1]);
-      }
-    }
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
+    const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
+    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[m]);
+    if constexpr (BF16)  // k 4..7 of this one are zero on both sides
+      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
+                                      u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[m]);
   }
 }
 
@@ -294,17 +329,18 @@ __device__ __forceinline__ int pick_id(const int (&ids)[kIdRegs], int idx) {
   return r;
 }
 
+// Four consecutive output elements, rounded to the dtype (8 bytes).
 template <bool BF16>
-__device__ __forceinline__ void store_row(uint16_t* o, const float (&r)[8], float inv) {
-  u32x4 wv;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = pack2<BF16>(r[2 * i] * inv, r[2 * i + 1] * inv);
-  *(u32x4*)o = wv;
+__device__ __forceinline__ void store4(uint16_t* o, f32x4 r, float inv) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *(u32x2*)o = u32x2{pack2<BF16>(r[0] * inv, r[1] * inv), pack2<BF16>(r[2] * inv, r[3] * inv)};
 }
 
 template <bool BF16, int BS, bool SPLIT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
+  constexpr int kNBuf = tile_buffers(NW);
+  constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * 8);
   // one array per tile buffer, so the compiler can wait for exactly the
   // loads of the buffer about to be read
   __shared__ __align__(16) char lds0[NW * kLdsTile];
@@ -345,13 +381,12 @@ void pd_decode_kernel(const KArgs a) {
   int ids[kIdRegs];
 #pragma unroll
   for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
+
   WaveState st;
   st.lsum = 0.f;
   st.m = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+  for (int m = 0; m < 8; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // loop bounds and block addresses in scalar registers
@@ -380,21 +415,25 @@ void pd_decode_kernel(const KArgs a) {
       tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
   const uint32_t tok_bytes = a.Hkv * kRowBytes;
-  // global offset of this lane's 16 bytes in load instruction 0 of a tile
-  const uint32_t lane_off = (uint32_t)row * tok_bytes + (uint32_t)g * kRowBytes +
-                            (uint32_t)((sl - row) & 15) * 16u;
+  // global offsets of this lane's 16 bytes in load instruction 0 of a tile
+  const uint32_t head_off = (uint32_t)row * tok_bytes + (uint32_t)g * kRowBytes;
+  const uint32_t koff_g = head_off + (uint32_t)((sl - row) & 15) * 16u;
+  const uint32_t voff_g = head_off + (uint32_t)((sl - 2 * row) & 15) * 16u;
   // LDS offsets of the two read patterns (see the tile layout above)
-  uint32_t koff[4], voff[4];
+  uint32_t koff[4], voff[8];
   {
     const int t = lane & 15, r = t & 3;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      koff[s] = (uint32_t)(t >> 2) * kLdsGroup + (uint32_t)r * kRowBytes +
+      koff[s] = (uint32_t)(t >> 2) * kKGroup + (uint32_t)r * kRowBytes +
                 16u * (uint32_t)((4 * s + row + r) & 15);
+    // source lane of the transposing read: token 4(lane/16) + (lane%16)/4,
+    // dims 16m + 4(lane%4) .. +4, i.e. chunk 2m + (lane%4)/2, half lane%2
+    const int k = (lane & 15) >> 2, a4 = lane & 3;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      voff[k] = kLdsTensor + (uint32_t)row * kLdsGroup + (uint32_t)k * kRowBytes +
-                16u * (uint32_t)((sl + k) & 15);
+    for (int m = 0; m < 8; ++m)
+      voff[m] = kKTile + (uint32_t)row * kVGroup + (uint32_t)k * kRowBytes +
+                16u * (uint32_t)((2 * m + (a4 >> 1) + 2 * k) & 15) + 8u * (uint32_t)(a4 & 1);
   }
 
   // Queue the 8 loads of tile j into buffer d. Straight-line, always eight
@@ -407,16 +446,22 @@ void pd_decode_kernel(const KArgs a) {
     const int id = pick_id(ids, idx) * (int)(j < nst);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (int64_t)id * a.blk_bytes, a.blk_bytes);
-    const uint32_t base = (uint32_t)(tok % BS) * tok_bytes + lane_off;
+    const uint32_t tb = (uint32_t)(tok % BS) * tok_bytes;
     char* kt = tile_buf(d);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const bool ok = tw0 + tok + 4 * n + row < tw1;
-      const uint32_t vo = ok ? base + 4u * n * tok_bytes : kOutOfBlock;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + n * kLdsGroup), 16, vo, 0, 0,
+      const uint32_t nb = tb + 4u * n * tok_bytes;
+      uint32_t ko = ok ? nb + koff_g : kOutOfBlock;
+      uint32_t vo = ok ? nb + voff_g : kOutOfBlock;
+      // the offsets are plain register values to the optimizer, so it cannot
+      // turn the selects into a divergent branch around the loads (which
+      // would issue a load twice and break the exact wait counts)
+      asm("" : "+v"(ko), "+v"(vo));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + n * kKGroup), 16, ko, 0, 0,
                                                kStream);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + kLdsTensor + n * kLdsGroup),
-                                               16, vo, 0, 0, kStream);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + kKTile + n * kVGroup), 16, vo,
+                                               0, 0, kStream);
     }
   };
 
@@ -438,8 +483,7 @@ void pd_decode_kernel(const KArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (j < nst) {
         const int tile0 = tw0 + kTileTok * j;
-        const char* kt = tile_buf(d);
-        tile_compute<BF16>(st, kt, kt, qb, koff, voff, tile0 + 4 * row, tw1,
+        tile_compute<BF16>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
                            tile0 + kTileTok > tw1, c);
       }
       issue(j + kNBuf, d);
@@ -450,66 +494,46 @@ void pd_decode_kernel(const KArgs a) {
   // tile buffers are reused below
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- reduce over the 4 token rows of the wave
-  const float lt = sum_rows(st.lsum);
-  float mh[G], lh[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    // lane h holds head h (every lane with lane%4 == h does)
-    mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, st.m), h));
-    lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt), h));
-  }
-  // reduce-scatter: rows 0-1 keep heads {0,1}, rows 2-3 keep heads {2,3} ...
-  float r1[2][8];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float y;
-      const float x = swap32_lo(st.acc[hh][e], st.acc[hh + 2][e], &y);
-      r1[hh][e] = x + y;
-    }
-  // ... then row r keeps head r.
-  float r2[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float y;
-    const float x = swap16_lo(r1[0][e], r1[1][e], &y);
-    r2[e] = x + y;
-  }
-  float m_r = row == 0 ? mh[0] : row == 1 ? mh[1] : row == 2 ? mh[2] : mh[3];
-  float l_r = row == 0 ? lh[0] : row == 1 ? lh[1] : row == 2 ? lh[2] : lh[3];
+  // ---- this lane's share of the result: query head h of the KV head, the
+  // 8 dims [d0, d0+4) and [d0+16, d0+20) (one of the 4 copies of each)
+  const int h = lane & 3;
+  const int qd = (lane >> 2) & 3;
+  const int d0 = 32 * qd + 4 * row;
+  f32x4 o0 = qd == 0 ? st.acc[0] : qd == 1 ? st.acc[2] : qd == 2 ? st.acc[4] : st.acc[6];
+  f32x4 o1 = qd == 0 ? st.acc[1] : qd == 1 ? st.acc[3] : qd == 2 ? st.acc[5] : st.acc[7];
+  float m_r = st.m;
+  float l_r = sum_rows(st.lsum);
 
   // ---- merge the NT slices of each head through LDS (the first tile
   // buffer); slice 0 keeps the result
   if (a.NT > 1) {
     __syncthreads();  // every wave is done with its tile buffers
-    f32x4* s_acc = (f32x4*)lds0;                    // [(w*G + row)*(D/4) + i]
-    float* s_m = (float*)lds0 + nw * G * D;         // [w*G + row]
+    float* s_acc = (float*)lds0;            // [(w*G + h)*D + dim]
+    float* s_m = (float*)lds0 + nw * G * D;  // [w*G + h]
     float* s_l = s_m + nw * G;
-    s_acc[(w * G + row) * (D / 4) + 2 * sl] = f32x4{r2[0], r2[1], r2[2], r2[3]};
-    s_acc[(w * G + row) * (D / 4) + 2 * sl + 1] = f32x4{r2[4], r2[5], r2[6], r2[7]};
-    if (sl == 0) {
-      s_m[w * G + row] = m_r;
-      s_l[w * G + row] = l_r;
+    *(f32x4*)(s_acc + (w * G + h) * D + d0) = o0;
+    *(f32x4*)(s_acc + (w * G + h) * D + d0 + 16) = o1;
+    if ((lane >> 2) == 0) {
+      s_m[w * G + h] = m_r;
+      s_l[w * G + h] = l_r;
     }
     __syncthreads();
     if (ts == 0) {
       float M = m_r;
-      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + row]);
+      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
       float den = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r2[e] = 0.f;
+      o0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      o1 = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int i = 0; i < a.NT; ++i) {
-        const int wi = (i * a.NH + hl) * G + row;
+        const int wi = (i * a.NH + hl) * G + h;
         const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
         den = fmaf(wt, s_l[wi], den);
-        const f32x4 x0 = s_acc[wi * (D / 4) + 2 * sl];
-        const f32x4 x1 = s_acc[wi * (D / 4) + 2 * sl + 1];
+        const f32x4 x0 = *(const f32x4*)(s_acc + wi * D + d0);
+        const f32x4 x1 = *(const f32x4*)(s_acc + wi * D + d0 + 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          r2[e] = fmaf(wt, x0[e], r2[e]);
-          r2[4 + e] = fmaf(wt, x1[e], r2[4 + e]);
+          o0[e] = fmaf(wt, x0[e], o0[e]);
+          o1[e] = fmaf(wt, x1[e], o1[e]);
         }
       }
       m_r = M;
@@ -517,31 +541,35 @@ void pd_decode_kernel(const KArgs a) {
     }
   }
   const bool owner = ts == 0;
-  const int hq = g * G + row;  // query head of this lane's row
+  const int hq = g * G + h;  // query head of this lane
 
   if constexpr (!SPLIT) {
-    if (owner)
-      store_row<BF16>((uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8, r2, 1.0f / l_r);
+    if (owner) {
+      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
+      const float inv = 1.0f / l_r;
+      store4<BF16>(o, o0, inv);
+      store4<BF16>(o + 16, o1, inv);
+    }
     return;
   } else {
     // ---- publish this partition's (o_p, lse_p), write-through
-    const size_t slot0 = ((size_t)b * Hq + (size_t)g * G) * a.S;  // (row 0, partition 0)
+    const size_t slot0 = ((size_t)b * Hq + (size_t)g * G) * a.S;  // (head 0, partition 0)
     const uint32_t rows_bytes = (uint32_t)G * a.S * D * 4;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o_part + slot0 * D, rows_bytes);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse_part + slot0, (uint32_t)G * a.S * 4);
     if (owner) {
       // the raw buffer builtins move 32-bit words: floats go through bit casts
       const float inv = 1.0f / l_r;
-      const uint32_t off = ((uint32_t)(row * a.S + p) * D + sl * 8) * 4;
-      const f32x4 o0 = {r2[0] * inv, r2[1] * inv, r2[2] * inv, r2[3] * inv};
-      const f32x4 o1 = {r2[4] * inv, r2[5] * inv, r2[6] * inv, r2[7] * inv};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), ro, off, 0, kCoherent);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), ro, off + 16, 0,
+      const uint32_t off = ((uint32_t)(h * a.S + p) * D + d0) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0 * inv), ro, off, 0,
                                              kCoherent);
-      if (sl == 0)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1 * inv), ro, off + 64,
+                                             0, kCoherent);
+      if ((lane >> 2) == 0)
         __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r)), rl,
-            (uint32_t)(row * a.S + p) * 4, 0, kCoherent);
+            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r) -
+                                             WeightBias<BF16>::log2),
+            rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
     }
     // the stores are complete (and past every non-coherent cache) before the
     // counter moves
@@ -561,22 +589,21 @@ void pd_decode_kernel(const KArgs a) {
 
     // ---- last workgroup: LSE merge over the n_live partitions, in order
     constexpr int kBatch = 8;
-    float M = -INFINITY, den = 0.f, acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float M = -INFINITY, den = 0.f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < n_live; i0 += kBatch) {
       float lse[kBatch];
-      f32x4 o0[kBatch], o1[kBatch];
+      f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         // partitions past n_live read zeros and are skipped below
         const bool ok = i0 + u < n_live;
-        const uint32_t slot = (uint32_t)(row * a.S + i0 + u);
-        const uint32_t off = ok ? (slot * D + sl * 8) * 4 : kOutOfBlock;
-        o0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
+        const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
+        const uint32_t off = ok ? (slot * D + d0) * 4 : kOutOfBlock;
+        x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
                                                                                 kCoherent));
-        o1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 16, 0,
-                                                                                kCoherent));
+        x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ro, ok ? off + 64 : kOutOfBlock, 0, kCoherent));
         lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
       }
@@ -586,8 +613,8 @@ void pd_decode_kernel(const KArgs a) {
         if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
       const float alpha = exp2_fast(M - bm);  // 0 on the first batch
       den *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      acc0 *= alpha;
+      acc1 *= alpha;
       M = bm;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -596,13 +623,16 @@ void pd_decode_kernel(const KArgs a) {
           den += wt;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[e] = fmaf(wt, o0[u][e], acc[e]);
-            acc[4 + e] = fmaf(wt, o1[u][e], acc[4 + e]);
+            acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
+            acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
           }
         }
       }
     }
-    store_row<BF16>((uint16_t*)a.out + ((size_t)b * Hq + hq) * D + sl * 8, acc, 1.0f / den);
+    uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
+    const float inv = 1.0f / den;
+    store4<BF16>(o, acc0, inv);
+    store4<BF16>(o + 16, acc1, inv);
   }
 }
 

@@ -15,20 +15,16 @@ namespace pd {
 
 namespace {
 
-constexpr int64_t kWavesSmall = 1024;       // waves for latency-bound calls
-constexpr int64_t kWavesLarge = 2048;       // waves for streaming calls
-constexpr int64_t kSmallWork = 128 * 1024;  // token-heads up to which a call is latency-bound
-constexpr int64_t kPairWork = 256 * 1024;   // token-heads from which KV heads go in pairs
-constexpr int64_t kSlices = 4;              // token slices per head in a workgroup
+constexpr int64_t kFillWaves = 1024;  // one wave per SIMD of the 256 CUs
+constexpr int64_t kWaves = 4;         // waves per workgroup
+constexpr int64_t kTileTok = 16;      // tokens per K/V tile of a wave
+constexpr int64_t kMinSplitTiles = 2;  // tiles per wave a split must leave
+constexpr int64_t kNoSplitTiles = 4;   // tiles per wave below which a split never pays
+constexpr int64_t kPairTiles = 16;     // tiles per wave from which split KV heads go in pairs
 constexpr int64_t kMaxSplits = 1 << 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
-int64_t pow2_ceil(int64_t x) {
-  int64_t r = 1;
-  while (r < x) r <<= 1;
-  return r;
-}
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -49,57 +45,67 @@ int32_t check_shape(const Shape& s) {
 
 // The plan cuts each sequence's context (up to cap = max_blocks_per_seq *
 // block_size tokens) into S partitions of P tokens, each served by one
-// workgroup per group of NH KV heads, made of NH x NT waves; a wave covers
-// one slice of Pw tokens (block aligned, at most 256 blocks) of one head.
+// workgroup of 4 waves per group of NH KV heads; a wave covers one slice of
+// Pw tokens (block aligned, at most 256 blocks) of one head, in tiles of 16.
 // Slices of a head merge in LDS, partitions merge across workgroups.
 //
 // The rule was fitted to sweeps of every (NH, NT, S) on an MI355X over the
 // decode workloads (batch 1..64, contexts 16..4,096, block sizes 16/32):
-//   * work = B * Hkv * cap token-heads sets the number of waves: about
-//     kWavesSmall for work up to kSmallWork (latency-bound calls: all of a
-//     wave's loads go out at once), kWavesLarge beyond (streaming calls:
-//     two resident waves per SIMD, each with a long slice, beat four with
-//     short ones), so Pw = work / waves, at least one block;
-//   * NT = 4 slices per head (NT = 8 or 16 only added waiting for the
-//     slowest wave; NT = 1 or 2 added cross-workgroup merges);
-//   * NH = 2 heads per workgroup once work reaches kPairWork (the pair reads
-//     512 contiguous bytes per token), else 1.
-// S and P follow from NT * Pw. A forced S fixes P instead and cuts it into
-// up to NT slices.
+//   * a call runs best with about one wave per SIMD (kFillWaves) in
+//     workgroups of 4 waves: NH = 1, NT = 4 while B * Hkv < 512, else KV
+//     heads in pairs (NH = 2, NT = 2, the pair reads 512 contiguous bytes
+//     per token);
+//   * when B * Hkv * NT / NH waves would leave SIMDs idle, the context is
+//     split until they are filled, keeping at least kMinSplitTiles tiles per
+//     wave; a split costs a cross-workgroup merge (about three memory round
+//     trips), so it is not used when a wave would have at most
+//     kNoSplitTiles tiles without it;
+//   * a split call whose waves still have kPairTiles or more tiles each
+//     does better with KV heads in pairs and twice the partitions.
+// A forced S fixes P instead and cuts it into up to NT slices.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
   const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
   const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
-  const int64_t work = units * cap;
   const int64_t pw_max = kMaxWaveBlocks * bs;
-  const int64_t waves = work <= kSmallWork ? kWavesSmall : kWavesLarge;
-  int64_t nh = work >= kPairWork && s.Hkv % 2 == 0 ? 2 : 1;
-  int64_t nt = kSlices;
-  int64_t pw, P;
+  const bool pairs = s.Hkv % 2 == 0;
+  int64_t nh = pairs && units >= 2 * kFillWaves / kWaves ? 2 : 1;
+  int64_t nt = kWaves / nh;
+  int64_t P;
   if (requested_splits > 0) {
     const int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
     P = round_up(ceil_div(cap, want), bs);
   } else {
-    pw = round_up(ceil_div(work, waves), bs);
-    if (pw > pw_max) pw = pw_max;
-    P = nt * pw;
-    if (P > cap) P = cap;  // one partition
+    int64_t S = 1;
+    if (units * nt < kFillWaves && ceil_div(cap, nt * kTileTok) > kNoSplitTiles) {
+      S = ceil_div(kFillWaves, units * nt);
+      const int64_t s_max = cap / (nt * kMinSplitTiles * kTileTok);
+      if (S > s_max) S = s_max;
+      if (S < 1) S = 1;
+      if (S > 1 && pairs && nh == 1 && cap / (S * nt) >= kPairTiles * kTileTok) {
+        nh = 2;
+        nt = kWaves / nh;
+        S *= 2;
+      }
+    }
+    P = round_up(ceil_div(cap, S), bs);
   }
 #ifdef PD_FORCE_NT  // tuning builds only: fix the slices per workgroup
   if (PD_FORCE_NT > 0) nt = PD_FORCE_NT;
 #endif
+#ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
+  if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
+#endif
+  if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
-  pw = round_up(ceil_div(P, nt), bs);
+  int64_t pw = round_up(ceil_div(P, nt), bs);
   if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more
     pw = pw_max;
     P = nt * pw;
   }
   nt = ceil_div(P, pw);  // drop slices that would start past the partition
-#ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
-  if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0 && PD_FORCE_NH * nt <= kMaxWaves) nh = PD_FORCE_NH;
-#endif
   const int64_t S = ceil_div(cap, P);
   if (S > kMaxSplits) return PD_ERR_SHAPE;
   // the split path keeps one arrival counter per (sequence, head group)
