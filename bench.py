@@ -171,22 +171,50 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
     return res
 
 
-def cpu_baseline(case, nseq: int):
-    """Time the fp64 oracle on the first `nseq` sequences of the workload."""
+def cpu_baseline(case, nseq: int, min_seconds: float = 10.0, max_calls: int = 25):
+    """Time the fp64 oracle on the first `nseq` sequences of the workload,
+    repeating the call until at least `min_seconds` have passed."""
     import oracle
     share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     nthreads = max(1, min(16, share or 1))
     sub_cl = case.context_lens[:nseq]
+    calls, used = 0, 0
     t0 = time.perf_counter()
-    _, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
-                                  case.block_table[:nseq], sub_cl, scale=case.scale,
-                                  dtype=case.dtype, nthreads=nthreads, return_threads=True)
-    dt = time.perf_counter() - t0
+    while calls < max_calls and (calls == 0 or time.perf_counter() - t0 < min_seconds):
+        _, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
+                                      case.block_table[:nseq], sub_cl, scale=case.scale,
+                                      dtype=case.dtype, nthreads=nthreads, return_threads=True)
+        calls += 1
+    dt = (time.perf_counter() - t0) / calls
     nbytes = 4096 * int(sub_cl.astype("int64").sum()) + 16384 * nseq
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": calls,
             "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
-                      f"one oracle call, fp64, {used} threads"}
+                      f"{calls} oracle calls, fp64, {used} threads"}
+
+
+def launch_floor(torch, pd, iters=200):
+    """Time per launch of the library's smallest kernel (its one-block fill of a
+    256-byte workspace) on a stream and in a HIP graph: the per-call floor."""
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        pd.paged_decode_workspace_init(ws)
+
+    return {"kernel": "pd_zero_kernel (1 block)",
+            "us_per_launch": round(time_calls(call, iters, 20, torch) * 1e3, 3),
+            "us_per_launch_graph": round(time_graph(call, iters, torch) * 1e3, 3)}
+
+
+def copy_roof(torch, nbytes=COPY_BYTES, iters=20):
+    """Device-to-device copy of 1 GiB (torch's copy kernel): bytes read + written / time."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    ms = time_calls(lambda i: b.copy_(a), iters, 3, torch)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def load_traffic(workload: str):
@@ -298,7 +326,10 @@ def main():
         print(json.dumps({"metric": METRIC, "error": "parity check failed", **err}))
         sys.exit(1)
 
+    first = out.clone()
     ms = time_calls(call, args.steps, args.warmup, torch)
+    torch.cuda.synchronize()
+    stable = bool(torch.equal(first.view(torch.int16), out.view(torch.int16)))
     nbytes = case.algorithmic_bytes()
     gbps = nbytes / (ms * 1e-3) / 1e9
 
@@ -317,12 +348,15 @@ def main():
                       "Hq": case.Hq, "Hkv": case.Hkv, "head_dim": case.D,
                       "block_size": case.block_size, "splits": S, "partition_tokens": P,
                       "algorithmic_bytes": nbytes},
-           "parity": {"ok": ok, **{k2: round(v2, 6) for k2, v2 in err.items()}},
+           "parity": {"ok": ok, "bitwise_stable_over_timed_calls": stable,
+                      **{k2: round(v2, 6) for k2, v2 in err.items()}},
            "roofline": roof}
     if not args.no_others:
+        res["context"] = {"launch_floor": launch_floor(torch, pd), "d2d_copy_roof": copy_roof(torch)}
         others = {}
-        for name in ("splitk_B8_L1024", "splitk_B8_L4096", "splitk_B32_L1024", "splitk_B1_L1024",
-                     "ragged", "short_B32_L64_bf16_bs16", "tiny"):
+        for name in ("splitk_B8_L1024", "splitk_B8_L4096", "splitk_B32_L1024", "splitk_B64_L1024",
+                     "splitk_B1_L1024", "ragged", "short_B32_L64_bf16_bs16",
+                     "short_B32_L64_f16_bs32", "tiny"):
             others[name] = bench_other(name, torch, pd)
         res["others"] = others
     if not args.no_cpu_baseline:
