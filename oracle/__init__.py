@@ -9,7 +9,9 @@ The arithmetic lives in ``pd_oracle.c`` (plain C, fp64, threaded over
 What it computes follows the Loom Kernels home page ("Supported now": paged
 MQA/GQA decode with GQA packing and local split-K/LSE): the exact softmax
 attention of one query token per head over the paged cache, plus the
-per-partition results and their log-sum-exp merge.
+per-partition results and their log-sum-exp merge; and, for an FP8 cache
+(same page, "Next boundaries": FP8 KV-cache compression), the same over
+E4M3FN codes times a float32 scale per tensor.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (closed forms, invariants and brute-force identities; see that file).
@@ -69,6 +71,14 @@ def _load():
         lib.pdo_round.restype = None
         lib.pdo_widen.argtypes = [P, i64, i32, P]
         lib.pdo_widen.restype = None
+        lib.pdo_widen_fp8.argtypes = [P, i64, P]
+        lib.pdo_widen_fp8.restype = None
+        lib.pdo_attention_fp8kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
+                                            f64, i32, f64, f64, P, P, i32]
+        lib.pdo_attention_fp8kv.restype = i32
+        lib.pdo_partials_fp8kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
+                                           f64, i32, f64, f64, i32, i32, P, P, i32]
+        lib.pdo_partials_fp8kv.restype = i32
         _lib = lib
         return lib
 
@@ -93,10 +103,10 @@ def _check(rc):
     return rc
 
 
-def _inputs(q, k_cache, v_cache, block_table, context_lens):
+def _inputs(q, k_cache, v_cache, block_table, context_lens, kv=np.uint16):
     q, qp = _c(q, np.uint16)
-    k, kp = _c(k_cache, np.uint16)
-    v, vp = _c(v_cache, np.uint16)
+    k, kp = _c(k_cache, kv)
+    v, vp = _c(v_cache, kv)
     bt, btp = _c(block_table, np.int32)
     cl, clp = _c(context_lens, np.int32)
     if k.shape != v.shape or k.ndim != 4 or q.ndim != 3 or bt.ndim != 2:
@@ -180,7 +190,65 @@ def widen(bits, dtype) -> np.ndarray:
     return out
 
 
+def widen_fp8(codes) -> np.ndarray:
+    """E4M3FN byte code -> exact fp64 value (NaN for the two NaN codes)."""
+    lib = _load()
+    a, ap = _c(codes, np.uint8)
+    out = np.empty(a.shape, np.float64)
+    lib.pdo_widen_fp8(ap, a.size, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def attention_fp8(q, k_cache, v_cache, block_table, context_lens, *, scale, dtype, k_scale,
+                  v_scale, nthreads: int = 0, return_threads: bool = False):
+    """``attention`` over an FP8 cache: k_cache/v_cache are uint8 E4M3FN codes
+    [NB,bs,Hkv,D] standing for code * k_scale and code * v_scale (float32
+    scales, widened exactly); q stays 16-bit."""
+    lib = _load()
+    keep, (qp, kp, vp, btp, clp) = _inputs(q, k_cache, v_cache, block_table, context_lens,
+                                           kv=np.uint8)
+    qa, k, _, bt, _ = keep
+    B, Hq, D = qa.shape
+    NB, bs, Hkv, Dk = k.shape
+    if Dk != D or bt.shape[0] != B:
+        raise OracleError("bad shape")
+    out = np.empty((B, Hq, D), np.float64)
+    lse = np.empty((B, Hq), np.float64)
+    rc = lib.pdo_attention_fp8kv(qp, kp, vp, btp, clp, B, Hq, Hkv, D, bs, bt.shape[1], NB,
+                                 float(np.float32(scale)), _DT[dtype],
+                                 float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                 out.ctypes.data_as(ctypes.c_void_p),
+                                 lse.ctypes.data_as(ctypes.c_void_p), int(nthreads))
+    nt = _check(rc)
+    return (out, lse, nt) if return_threads else (out, lse)
+
+
+def partials_fp8(q, k_cache, v_cache, block_table, context_lens, *, scale, dtype, k_scale,
+                 v_scale, partition_tokens: int, num_splits: int, nthreads: int = 0):
+    """``partials`` over an FP8 cache."""
+    lib = _load()
+    keep, (qp, kp, vp, btp, clp) = _inputs(q, k_cache, v_cache, block_table, context_lens,
+                                           kv=np.uint8)
+    qa, k, _, bt, _ = keep
+    B, Hq, D = qa.shape
+    NB, bs, Hkv, _ = k.shape
+    S = int(num_splits)
+    o = np.empty((B, Hq, S, D), np.float64)
+    lse = np.empty((B, Hq, S), np.float64)
+    rc = lib.pdo_partials_fp8kv(qp, kp, vp, btp, clp, B, Hq, Hkv, D, bs, bt.shape[1], NB,
+                                float(np.float32(scale)), _DT[dtype],
+                                float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                int(partition_tokens), S, o.ctypes.data_as(ctypes.c_void_p),
+                                lse.ctypes.data_as(ctypes.c_void_p), int(nthreads))
+    _check(rc)
+    return o, lse
+
+
 def attention_case(case, **kw):
-    """``attention`` over a ``workloads.Case``."""
+    """``attention`` (or ``attention_fp8`` for an FP8 cache) over a ``workloads.Case``."""
+    if getattr(case, "kv_dtype", "") == "fp8":
+        return attention_fp8(case.q, case.k_cache, case.v_cache, case.block_table,
+                             case.context_lens, scale=case.scale, dtype=case.dtype,
+                             k_scale=case.k_scale, v_scale=case.v_scale, **kw)
     return attention(case.q, case.k_cache, case.v_cache, case.block_table,
                      case.context_lens, scale=case.scale, dtype=case.dtype, **kw)

@@ -31,6 +31,11 @@
  *   M = max_p lse_p,  w_p = exp(lse_p - M),  out = sum_p w_p o_p / sum_p w_p
  * taken in order p = 0..n-1.
  *
+ * FP8 cache (Loom Kernels home page, "Next boundaries": FP8 KV-cache
+ * compression): K and V hold OCP FP8 E4M3FN codes with one float32 scale per
+ * tensor; the value of a code c is decode(c) * scale, widened exactly, and
+ * everything else is the definition above.
+ *
  * Status codes: 0 ok, -1 bad shape, -2 a live block id outside the pool,
  * -3 a context length outside [0, max_blocks_per_seq * block_size],
  * -4 out of memory, -5 bad dtype.
@@ -66,6 +71,22 @@ static double widen_bf16(uint16_t b) {
 
 static double widen(uint16_t b, int dtype) {
     return dtype == PDO_BF16 ? widen_bf16(b) : widen_f16(b);
+}
+
+/* OCP 8-bit floating point, E4M3FN: 1 sign, 4 exponent (bias 7), 3 fraction
+ * bits; no infinities; exponent and fraction all ones is NaN, so the largest
+ * finite magnitude is 1.75 * 2^8 = 448; exponent 0 is subnormal (f * 2^-9). */
+static double widen_e4m3(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 0xf, f = b & 7;
+    double v;
+    if (e == 15 && f == 7) return NAN;
+    if (e == 0) v = ldexp((double)f, -9);
+    else v = ldexp((double)(8 + f), e - 10);
+    return s ? -v : v;
+}
+
+void pdo_widen_fp8(const uint8_t* x, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = widen_e4m3(x[i]);
 }
 
 void pdo_widen(const uint16_t* x, int64_t n, int32_t dtype, double* out) {
@@ -112,6 +133,8 @@ void pdo_round(const double* x, int64_t n, int32_t dtype, uint16_t* out) {
 
 typedef struct {
     const uint16_t *q, *k, *v;
+    const uint8_t *k8, *v8;  /* FP8 codes instead of k, v when non-null */
+    double k_scale, v_scale;
     const int32_t *bt, *cl;
     int32_t B, Hq, Hkv, D, bs, MB;
     int64_t num_blocks;
@@ -143,9 +166,14 @@ static int attend(const job_t* J, int b, int h, int t0, int t1, double* s,
     for (int t = t0; t < t1; ++t) {
         int32_t blk = J->bt[(int64_t)b * J->MB + t / J->bs];
         if (blk < 0 || blk >= J->num_blocks) return -2;
-        const uint16_t* kt = J->k + (((int64_t)blk * J->bs + t % J->bs) * J->Hkv + g) * D;
+        const int64_t row = (((int64_t)blk * J->bs + t % J->bs) * J->Hkv + g) * D;
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += widen(qh[d], J->dtype) * widen(kt[d], J->dtype);
+        if (J->k8) {
+            for (int d = 0; d < D; ++d)
+                dot += widen(qh[d], J->dtype) * (widen_e4m3(J->k8[row + d]) * J->k_scale);
+        } else {
+            for (int d = 0; d < D; ++d) dot += widen(qh[d], J->dtype) * widen(J->k[row + d], J->dtype);
+        }
         s[t - t0] = J->scale * dot;
     }
     double m = -INFINITY;
@@ -155,9 +183,13 @@ static int attend(const job_t* J, int b, int h, int t0, int t1, double* s,
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     for (int t = t0; t < t1; ++t) {
         int32_t blk = J->bt[(int64_t)b * J->MB + t / J->bs];
-        const uint16_t* vt = J->v + (((int64_t)blk * J->bs + t % J->bs) * J->Hkv + g) * D;
+        const int64_t row = (((int64_t)blk * J->bs + t % J->bs) * J->Hkv + g) * D;
         double w = exp(s[t - t0] - m);
-        for (int d = 0; d < D; ++d) o[d] += w * widen(vt[d], J->dtype);
+        if (J->v8) {
+            for (int d = 0; d < D; ++d) o[d] += w * (widen_e4m3(J->v8[row + d]) * J->v_scale);
+        } else {
+            for (int d = 0; d < D; ++d) o[d] += w * widen(J->v[row + d], J->dtype);
+        }
     }
     for (int d = 0; d < D; ++d) o[d] /= Z;
     *lse = m + log(Z);
@@ -292,4 +324,43 @@ int32_t pdo_merge(const double* o_part, const double* lse_part, const int32_t* c
         }
     }
     return 0;
+}
+
+/* pdo_attention / pdo_partials over an FP8 E4M3FN cache: k8, v8 hold byte
+ * codes in the same [num_blocks, block_size, Hkv, D] layout; q (and the
+ * dtype argument) stay 16-bit. */
+int32_t pdo_attention_fp8kv(const uint16_t* q, const uint8_t* k8, const uint8_t* v8,
+                            const int32_t* block_table, const int32_t* context_lens,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                            int32_t max_blocks_per_seq, int64_t num_blocks, double scale,
+                            int32_t dtype, double k_scale, double v_scale, double* out,
+                            double* lse, int32_t nthreads) {
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k8 = k8; J.v8 = v8; J.k_scale = k_scale; J.v_scale = v_scale;
+    J.bt = block_table; J.cl = context_lens;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = block_size; J.MB = max_blocks_per_seq;
+    J.num_blocks = num_blocks; J.scale = scale; J.dtype = dtype;
+    J.P = 0; J.S = 1; J.out = out; J.lse = lse; J.nthreads = nthreads;
+    if (!k8 || !v8) return -1;
+    int st = run(&J);
+    return st ? st : J.nthreads;
+}
+
+int32_t pdo_partials_fp8kv(const uint16_t* q, const uint8_t* k8, const uint8_t* v8,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, double scale,
+                           int32_t dtype, double k_scale, double v_scale, int32_t P, int32_t S,
+                           double* o_part, double* lse_part, int32_t nthreads) {
+    if (P <= 0 || S <= 0 || !k8 || !v8) return -1;
+    job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.k8 = k8; J.v8 = v8; J.k_scale = k_scale; J.v_scale = v_scale;
+    J.bt = block_table; J.cl = context_lens;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.D = D; J.bs = block_size; J.MB = max_blocks_per_seq;
+    J.num_blocks = num_blocks; J.scale = scale; J.dtype = dtype;
+    J.P = P; J.S = S; J.out = o_part; J.lse = lse_part; J.nthreads = nthreads;
+    int st = run(&J);
+    return st ? st : J.nthreads;
 }

@@ -397,3 +397,133 @@ def test_large_logits_stay_finite_in_single_pass_and_merge():
                                partition_tokens=8, num_splits=4)
     merged = oracle.merge(o_p, l_p, c["context_lens"], partition_tokens=8)
     assert np.max(np.abs(merged - out)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3FN) cache
+
+def fp8_codes(x):
+    """float values -> E4M3FN byte codes (torch CPU cast, RNE)."""
+    return torch.as_tensor(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def small_fp8_case(k_scale, v_scale, dtype="bf16", seed=3, **kw):
+    c, _ = small_case(dtype=dtype, seed=seed, **kw)
+    g = np.random.default_rng(seed + 100)
+    shape = c["k_cache"].shape
+    c["k_cache"] = fp8_codes(g.standard_normal(shape) * 40)
+    c["v_cache"] = fp8_codes(g.standard_normal(shape) * 40)
+    return c
+
+
+def run_fp8(c, dtype, k_scale, v_scale, scale=0.25, **kw):
+    return oracle.attention_fp8(c["q"], c["k_cache"], c["v_cache"], c["block_table"],
+                                c["context_lens"], scale=scale, dtype=dtype, k_scale=k_scale,
+                                v_scale=v_scale, **kw)
+
+
+def test_fp8_widen_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.widen_fp8(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.nonzero(nan)[0].tolist() == [0x7F, 0xFF]
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # the format's landmarks: largest finite, smallest normal and subnormal, one
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8_cache_equals_the_16bit_oracle_on_the_same_values(dtype):
+    # power-of-two scales keep code * scale exact in the 16-bit dtype, so the
+    # FP8 path must give the 16-bit oracle's fp64 result on those values
+    ks, vs = 2.0 ** -5, 2.0 ** -6
+    c = small_fp8_case(ks, vs, dtype=dtype)
+    c16 = dict(c)
+    c16["k_cache"] = bits(oracle.widen_fp8(c["k_cache"]) * ks, dtype)
+    c16["v_cache"] = bits(oracle.widen_fp8(c["v_cache"]) * vs, dtype)
+    assert np.array_equal(vals(c16["k_cache"], dtype), oracle.widen_fp8(c["k_cache"]) * ks)
+    assert np.array_equal(vals(c16["v_cache"], dtype), oracle.widen_fp8(c["v_cache"]) * vs)
+    o8, l8 = run_fp8(c, dtype, ks, vs)
+    o16, l16 = run(c16, dtype)
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+
+
+def test_fp8_one_token_returns_its_scaled_v_exactly():
+    ks, vs = 0.0123, 0.0371  # not powers of two
+    c = small_fp8_case(ks, vs, ctx=(1, 1, 1))
+    o, lse = run_fp8(c, "bf16", ks, vs)
+    for b in range(3):
+        blk = c["block_table"][b, 0]
+        for h in range(8):
+            v = oracle.widen_fp8(c["v_cache"][blk, 0, h // 4]) * float(np.float32(vs))
+            assert np.array_equal(o[b, h], v)
+
+
+def test_fp8_scales_enter_where_the_definition_puts_them():
+    # two tokens: out = sigma(s0 - s1) v0 + sigma(s1 - s0) v1 with
+    # s_i = scale * q . (k_i * k_scale) and v_i * v_scale
+    ks, vs, scale = 0.05, 0.02, 0.3
+    c = small_fp8_case(ks, vs, ctx=(2, 2, 2))
+    o, _ = run_fp8(c, "bf16", ks, vs, scale=scale)
+    ksf, vsf, sf = (float(np.float32(x)) for x in (ks, vs, scale))
+    for b in range(3):
+        blk = c["block_table"][b, 0]
+        for h in range(8):
+            g = h // 4
+            q = vals(c["q"][b, h], "bf16")
+            k = oracle.widen_fp8(c["k_cache"][blk, :2, g]) * ksf
+            v = oracle.widen_fp8(c["v_cache"][blk, :2, g]) * vsf
+            s = sf * (k @ q)
+            w1 = 1.0 / (1.0 + math.exp(s[0] - s[1]))
+            want = (1.0 - w1) * v[0] + w1 * v[1]
+            assert np.allclose(o[b, h], want, rtol=1e-12, atol=1e-15)
+    # swapping the two scales must change the result
+    o2, _ = run_fp8(c, "bf16", vs, ks, scale=scale)
+    assert not np.allclose(o, o2)
+
+
+def test_fp8_nan_codes_outside_the_valid_tokens_are_never_read():
+    ks, vs = 0.01, 0.01
+    c = small_fp8_case(ks, vs, ctx=(5, 9, 1), extra_pool=2)
+    clean, _ = run_fp8(c, "bf16", ks, vs)
+    bs = c["k_cache"].shape[1]
+    live = set()
+    for b, L in enumerate(c["context_lens"]):
+        n = -(-int(L) // bs)
+        live.update(int(x) for x in c["block_table"][b, :n])
+        last = c["block_table"][b, n - 1]
+        c["k_cache"][last, int(L) - (n - 1) * bs:] = 0x7F
+        c["v_cache"][last, int(L) - (n - 1) * bs:] = 0xFF
+    for i in range(c["k_cache"].shape[0]):
+        if i not in live:
+            c["k_cache"][i] = 0x7F
+            c["v_cache"][i] = 0xFF
+    got, _ = run_fp8(c, "bf16", ks, vs)
+    assert np.all(np.isfinite(got)) and np.array_equal(got, clean)
+
+
+def test_fp8_split_merge_equals_single_pass():
+    ks, vs = 0.013, 0.021
+    c = small_fp8_case(ks, vs, ctx=(13, 20, 7))
+    ref, lse = run_fp8(c, "bf16", ks, vs)
+    for P in (4, 8, 12):
+        S = -(-20 // P)
+        o, l = oracle.partials_fp8(c["q"], c["k_cache"], c["v_cache"], c["block_table"],
+                                   c["context_lens"], scale=0.25, dtype="bf16", k_scale=ks,
+                                   v_scale=vs, partition_tokens=P, num_splits=S)
+        got = oracle.merge(o, l, c["context_lens"], partition_tokens=P)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_workload_codes_stand_for_scaled_normal_draws():
+    c = workloads.splitk(2, 256, seed=5, kv_dtype="fp8")
+    for codes, scale in ((c.k_cache, c.k_scale), (c.v_cache, c.v_scale)):
+        x = oracle.widen_fp8(codes) * scale
+        assert np.isfinite(x).all()
+        assert abs(float(np.abs(x).max()) / scale - 448.0) < 1e-9   # amax maps to the top code
+        assert abs(float(x.std()) - 1.0) < 0.01

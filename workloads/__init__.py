@@ -21,6 +21,10 @@ dim 128. The pages give no random-number recipe, so this module fixes one:
   physical block is shared between sequences.
 * Ragged context lengths come from a third generator seeded with
   ``seed + 2``, uniform over the stated integer range.
+* An FP8 cache (``kv_dtype="fp8"``, the OCP E4M3FN format) draws K and V the
+  same way in float32, takes one float32 scale per tensor, amax / 448 (the
+  largest finite code), and stores round-to-nearest-even(x / scale) as byte
+  codes (torch's CPU cast); the value a code stands for is code * scale.
 
 Layouts (row-major, contiguous):
   q, out       [B, Hq, D]
@@ -39,6 +43,7 @@ import torch
 
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 DTYPE_CODE = {"f16": 0, "bf16": 1}
+FP8_MAX = 448.0  # largest finite E4M3FN value
 
 # 1/sqrt(128) rounded to float32, the scale every workload uses.
 SCALE_D128 = float(np.float32(1.0 / math.sqrt(128.0)))
@@ -57,12 +62,19 @@ class Case:
     dtype: str
     scale: float
     q: np.ndarray            # uint16 [B, Hq, D]
-    k_cache: np.ndarray      # uint16 [NB, bs, Hkv, D]
-    v_cache: np.ndarray      # uint16 [NB, bs, Hkv, D]
+    k_cache: np.ndarray      # uint16 (uint8 codes for an FP8 cache) [NB, bs, Hkv, D]
+    v_cache: np.ndarray      # uint16 (uint8 codes for an FP8 cache) [NB, bs, Hkv, D]
     block_table: np.ndarray  # int32 [B, MB]
     context_lens: np.ndarray # int32 [B]
     seed: int
     q_sigma: float = 1.0
+    kv_dtype: str = ""       # "" = the dtype of q; "fp8" = E4M3FN codes with scales
+    k_scale: float = 1.0     # float32 scale of the FP8 K codes
+    v_scale: float = 1.0     # float32 scale of the FP8 V codes
+
+    @property
+    def fp8(self) -> bool:
+        return self.kv_dtype == "fp8"
 
     @property
     def num_blocks(self) -> int:
@@ -77,8 +89,9 @@ class Case:
         return DTYPE_CODE[self.dtype]
 
     def algorithmic_bytes(self) -> int:
-        """K+V over valid tokens, plus Q and O, in bytes (2-byte dtypes)."""
-        kv = 2 * self.Hkv * self.D * 2 * int(self.context_lens.astype(np.int64).sum())
+        """K+V over valid tokens, plus Q and O, in bytes."""
+        es = 1 if self.fp8 else 2
+        kv = 2 * self.Hkv * self.D * es * int(self.context_lens.astype(np.int64).sum())
         qo = 2 * self.B * self.Hq * self.D * 2
         return kv + qo
 
@@ -91,15 +104,21 @@ class Case:
         return out
 
     def torch_views(self):
-        """(q, k_cache, v_cache) as CPU torch tensors of the 16-bit dtype."""
+        """(q, k_cache, v_cache) as CPU torch tensors: q in the 16-bit dtype, the
+        caches in it too, or as float8_e4m3fn for an FP8 cache."""
         dt = DTYPES[self.dtype]
-        return tuple(torch.from_numpy(a.view(np.int16)).view(dt)
-                     for a in (self.q, self.k_cache, self.v_cache))
+        q = torch.from_numpy(self.q.view(np.int16)).view(dt)
+        if self.fp8:
+            return (q,) + tuple(torch.from_numpy(a).view(torch.float8_e4m3fn)
+                                for a in (self.k_cache, self.v_cache))
+        return (q,) + tuple(torch.from_numpy(a.view(np.int16)).view(dt)
+                            for a in (self.k_cache, self.v_cache))
 
     def describe(self) -> str:
         L = self.context_lens
+        kv = f" kv=fp8(k_scale={self.k_scale:.6g},v_scale={self.v_scale:.6g})" if self.fp8 else ""
         return (f"{self.name}: B={self.B} Hq={self.Hq} Hkv={self.Hkv} D={self.D} "
-                f"bs={self.block_size} {self.dtype} ctx[min={int(L.min())},max={int(L.max())}] "
+                f"bs={self.block_size} {self.dtype}{kv} ctx[min={int(L.min())},max={int(L.max())}] "
                 f"pool={self.num_blocks} MB={self.max_blocks_per_seq} seed={self.seed}")
 
 
@@ -122,6 +141,30 @@ def normal_bits(shape, dtype: str, seed: int, sigma: float = 1.0,
     return out.view(torch.int16).numpy().view(np.uint16).reshape(shape)
 
 
+def normal_fp8(shape, seed: int, sigma: float = 1.0, chunk: int = 1 << 26):
+    """N(0, sigma^2) float32 draws (the same stream as ``normal_bits``) stored
+    as E4M3FN codes with one float32 scale, amax / 448: returns (uint8 codes,
+    scale). Two passes over the stream, so no float32 copy is kept."""
+    n = int(np.prod(shape))
+
+    def draws():
+        g = torch.Generator().manual_seed(int(seed))
+        for s in range(0, n, chunk):
+            x = torch.randn(min(n, s + chunk) - s, generator=g, dtype=torch.float32)
+            if sigma != 1.0:
+                x.mul_(sigma)
+            yield s, x
+
+    amax = 0.0
+    for _, x in draws():
+        amax = max(amax, float(x.abs().max()))
+    scale = float(np.float32(amax / FP8_MAX)) if amax > 0 else 1.0
+    out = torch.empty(n, dtype=torch.uint8)
+    for s, x in draws():
+        out[s:s + x.numel()] = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out.numpy().reshape(shape), scale
+
+
 def _perm(n: int, seed: int) -> np.ndarray:
     g = torch.Generator().manual_seed(int(seed))
     return torch.randperm(n, generator=g).numpy().astype(np.int32)
@@ -131,7 +174,7 @@ def make_case(name: str, B: int, ctx, *, dtype: str = "bf16", block_size: int = 
               Hq: int = 32, Hkv: int = 8, D: int = 128, seed: int = 0,
               pool_blocks: int | None = None, max_blocks_per_seq: int | None = None,
               q_sigma: float = 1.0, kv_sigma: float = 1.0,
-              scale: float = SCALE_D128) -> Case:
+              scale: float = SCALE_D128, kv_dtype: str = "") -> Case:
     """Build a case with per-sequence contexts ``ctx`` (int or sequence of ints).
 
     The physical pool defaults to twice the blocks the batch needs; block ids
@@ -163,8 +206,17 @@ def make_case(name: str, B: int, ctx, *, dtype: str = "bf16", block_size: int = 
             bt[b, i] = spare[j % len(spare)]
             j += 1
     q = normal_bits((B, Hq, D), dtype, seed * 7919 + 11, q_sigma)
-    k = normal_bits((pool, block_size, Hkv, D), dtype, seed * 7919 + 12, kv_sigma)
-    v = normal_bits((pool, block_size, Hkv, D), dtype, seed * 7919 + 13, kv_sigma)
+    kshape = (pool, block_size, Hkv, D)
+    if kv_dtype == "fp8":
+        k, ks = normal_fp8(kshape, seed * 7919 + 12, kv_sigma)
+        v, vs = normal_fp8(kshape, seed * 7919 + 13, kv_sigma)
+        return Case(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size,
+                    dtype=dtype, scale=scale, q=q, k_cache=k, v_cache=v,
+                    block_table=bt, context_lens=lens, seed=seed, q_sigma=q_sigma,
+                    kv_dtype="fp8", k_scale=ks, v_scale=vs)
+    assert kv_dtype in ("", dtype), kv_dtype
+    k = normal_bits(kshape, dtype, seed * 7919 + 12, kv_sigma)
+    v = normal_bits(kshape, dtype, seed * 7919 + 13, kv_sigma)
     return Case(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size,
                 dtype=dtype, scale=scale, q=q, k_cache=k, v_cache=v,
                 block_table=bt, context_lens=lens, seed=seed, q_sigma=q_sigma)
@@ -173,18 +225,28 @@ def make_case(name: str, B: int, ctx, *, dtype: str = "bf16", block_size: int = 
 # ---------------------------------------------------------------------------
 # The five workloads.
 
-def tiny(seed: int = 0) -> Case:
+def _suffix(kv_dtype: str) -> str:
+    return "_fp8" if kv_dtype == "fp8" else ""
+
+
+def tiny(seed: int = 0, kv_dtype: str = "") -> Case:
     """Batch 1, context 16 (one block of 16), bf16; pool of 4 blocks whose
     block-table row is a random permutation of {0..3}, only entry 0 live."""
     B, bs, pool = 1, 16, 4
     perm = _perm(pool, seed + 1)
     q = normal_bits((B, 32, 128), "bf16", seed * 7919 + 11)
-    k = normal_bits((pool, bs, 8, 128), "bf16", seed * 7919 + 12)
-    v = normal_bits((pool, bs, 8, 128), "bf16", seed * 7919 + 13)
-    return Case(name="tiny", B=B, Hq=32, Hkv=8, D=128, block_size=bs, dtype="bf16",
-                scale=SCALE_D128, q=q, k_cache=k, v_cache=v,
+    kw = {}
+    if kv_dtype == "fp8":
+        k, ks = normal_fp8((pool, bs, 8, 128), seed * 7919 + 12)
+        v, vs = normal_fp8((pool, bs, 8, 128), seed * 7919 + 13)
+        kw = dict(kv_dtype="fp8", k_scale=ks, v_scale=vs)
+    else:
+        k = normal_bits((pool, bs, 8, 128), "bf16", seed * 7919 + 12)
+        v = normal_bits((pool, bs, 8, 128), "bf16", seed * 7919 + 13)
+    return Case(name="tiny" + _suffix(kv_dtype), B=B, Hq=32, Hkv=8, D=128, block_size=bs,
+                dtype="bf16", scale=SCALE_D128, q=q, k_cache=k, v_cache=v,
                 block_table=perm.reshape(1, pool).copy(),
-                context_lens=np.array([16], dtype=np.int32), seed=seed)
+                context_lens=np.array([16], dtype=np.int32), seed=seed, **kw)
 
 
 SHORT_BATCHES = (1, 8, 32)
@@ -193,19 +255,20 @@ SHORT_DTYPES = ("f16", "bf16")
 SHORT_BLOCKS = (16, 32)
 
 
-def short(B: int, L: int, dtype: str, block_size: int, seed: int = 0) -> Case:
+def short(B: int, L: int, dtype: str, block_size: int, seed: int = 0,
+          kv_dtype: str = "") -> Case:
     """Short-context route: all sequences of length L, pool twice the need."""
-    return make_case(f"short_B{B}_L{L}_{dtype}_bs{block_size}", B, L, dtype=dtype,
-                     block_size=block_size, seed=seed)
+    return make_case(f"short_B{B}_L{L}_{dtype}_bs{block_size}{_suffix(kv_dtype)}", B, L,
+                     dtype=dtype, block_size=block_size, seed=seed, kv_dtype=kv_dtype)
 
 
-def short_cases(seed: int = 0) -> Iterator[Case]:
+def short_cases(seed: int = 0, kv_dtype: str = "") -> Iterator[Case]:
     i = 0
     for B in SHORT_BATCHES:
         for L in SHORT_CONTEXTS:
             for dt in SHORT_DTYPES:
                 for bs in SHORT_BLOCKS:
-                    yield short(B, L, dt, bs, seed + 100 * i)
+                    yield short(B, L, dt, bs, seed + 100 * i, kv_dtype)
                     i += 1
 
 
@@ -213,35 +276,38 @@ SPLITK_BATCHES = (1, 2, 4, 8)
 SPLITK_CONTEXTS = (128, 256, 512, 1024)
 
 
-def splitk(B: int, L: int, seed: int = 0) -> Case:
+def splitk(B: int, L: int, seed: int = 0, kv_dtype: str = "") -> Case:
     """Split-K/LSE sweep point: bf16, block size 16, pool twice the need."""
-    return make_case(f"splitk_B{B}_L{L}", B, L, dtype="bf16", block_size=16, seed=seed)
+    return make_case(f"splitk_B{B}_L{L}{_suffix(kv_dtype)}", B, L, dtype="bf16", block_size=16,
+                     seed=seed, kv_dtype=kv_dtype)
 
 
-def splitk_cases(seed: int = 0) -> Iterator[Case]:
+def splitk_cases(seed: int = 0, kv_dtype: str = "") -> Iterator[Case]:
     i = 0
     for B in SPLITK_BATCHES:
         for L in SPLITK_CONTEXTS:
-            yield splitk(B, L, seed + 100 * i)
+            yield splitk(B, L, seed + 100 * i, kv_dtype)
             i += 1
 
 
-def ragged(seed: int = 0, B: int = 32, max_ctx: int = 1024, q_sigma: float = math.sqrt(2.0)) -> Case:
+def ragged(seed: int = 0, B: int = 32, max_ctx: int = 1024, q_sigma: float = math.sqrt(2.0),
+           kv_dtype: str = "") -> Case:
     """Ragged batch: per-sequence contexts uniform in [1, max_ctx], bf16,
     block size 32, pool of B * max_ctx/32 blocks (one block-table row per
     sequence, no reuse), Q ~ N(0, 2) read as variance 2 (sigma = sqrt 2)."""
     g = torch.Generator().manual_seed(int(seed) + 2)
     lens = torch.randint(1, max_ctx + 1, (B,), generator=g).numpy().astype(np.int32)
     MB = max_ctx // 32
-    return make_case("ragged_B32", B, lens, dtype="bf16", block_size=32, seed=seed,
-                     pool_blocks=B * MB, max_blocks_per_seq=MB, q_sigma=q_sigma)
+    return make_case("ragged_B32" + _suffix(kv_dtype), B, lens, dtype="bf16", block_size=32,
+                     seed=seed, pool_blocks=B * MB, max_blocks_per_seq=MB, q_sigma=q_sigma,
+                     kv_dtype=kv_dtype)
 
 
-def large(seed: int = 0, B: int = 64, L: int = 4096) -> Case:
+def large(seed: int = 0, B: int = 64, L: int = 4096, kv_dtype: str = "") -> Case:
     """Bandwidth-bound decode: batch 64, context 4096, bf16, block size 16;
     the pool is exactly the blocks needed and the block table is a random
     permutation of it (K+V = 1 GiB read per call)."""
     bs = 16
     MB = L // bs
-    return make_case(f"large_B{B}_L{L}", B, L, dtype="bf16", block_size=bs, seed=seed,
-                     pool_blocks=B * MB, max_blocks_per_seq=MB)
+    return make_case(f"large_B{B}_L{L}{_suffix(kv_dtype)}", B, L, dtype="bf16", block_size=bs,
+                     seed=seed, pool_blocks=B * MB, max_blocks_per_seq=MB, kv_dtype=kv_dtype)
