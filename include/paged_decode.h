@@ -163,6 +163,36 @@ size_t paged_decode_workspace_bytes_splits(int32_t B, int32_t Hq, int32_t Hkv, i
                                            int32_t max_blocks_per_seq, int32_t block_size,
                                            int32_t dtype, int32_t requested_splits);
 
+/* Paged decode attention over an FP8 KV cache (Loom Kernels home page,
+ * "Next boundaries": FP8 KV-cache compression, which halves the cache bytes
+ * the bandwidth-bound path reads).
+ *
+ * k_cache and v_cache hold one byte per element in the same
+ * [num_blocks, block_size, Hkv, D] layout: OCP FP8 E4M3FN codes (1 sign, 4
+ * exponent bits with bias 7, 3 fraction bits; 0x7F and 0xFF are NaN; largest
+ * finite 448). The element a code stands for is code * k_scale (K) or
+ * code * v_scale (V), one float32 scale per tensor. q and out stay 16-bit of
+ * `dtype` (PD_DTYPE_F16 or PD_DTYPE_BF16); every other argument, the layout,
+ * ownership, workspace and error rules are those of paged_decode_attention,
+ * and the plan and workspace size are paged_decode_plan's and
+ * paged_decode_workspace_bytes' for the same shape and dtype (num_splits = 0)
+ * or their _splits forms (num_splits > 0 forces S).
+ *
+ * The codes are widened exactly; the scales are applied in fp32 to the scores
+ * (k_scale * scale) and to the normalised output (v_scale).
+ *
+ * Errors as paged_decode_attention, plus PD_ERR_VALUE when k_scale or
+ * v_scale is not finite and positive, and PD_ERR_SHAPE for num_splits < 0.
+ */
+int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   int32_t max_blocks_per_seq, void* out,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t block_size, float scale, int32_t dtype,
+                                   float k_scale, float v_scale,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   int32_t num_splits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,9 @@ lib.paged_decode_attention.argtypes = _ATTN
 lib.paged_decode_attention.restype = _I
 lib.paged_decode_attention_splits.argtypes = _ATTN + [_I]
 lib.paged_decode_attention_splits.restype = _I
+lib.paged_decode_attention_fp8.argtypes = _ATTN[:14] + [_F, _F] + _ATTN[14:] + [_I]
+lib.paged_decode_attention_fp8.restype = _I
+_FP8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
 class PagedDecodeError(RuntimeError):
@@ -171,3 +174,44 @@ def paged_decode_attention_splits(q, k_cache, v_cache, block_table, context_lens
     """``paged_decode_attention`` with the split count forced to ``num_splits``."""
     return paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out,
                                   num_splits=num_splits, **kw)
+
+
+def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, out=None, *,
+                               k_scale, v_scale, scale=None, workspace=None, num_splits=None,
+                               stream=None):
+    """Paged decode attention over an FP8 (E4M3FN) cache.
+
+    k_cache/v_cache: [num_blocks,block_size,Hkv,D] of torch.float8_e4m3fn (or
+    uint8 holding the codes), standing for code * k_scale and code * v_scale;
+    q (and out) f16 or bf16 [B,Hq,D]. Otherwise as ``paged_decode_attention``.
+    """
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("k_cache/v_cache must be float8_e4m3fn (or uint8 codes), q f16 or bf16")
+    B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = D ** -0.5
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_table, num_splits)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
+    rc = lib.paged_decode_attention_fp8(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
+        _DTYPE_CODE[q.dtype], float(k_scale), float(v_scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), handle,
+        0 if num_splits is None else int(num_splits))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return out

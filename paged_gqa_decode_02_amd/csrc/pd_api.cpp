@@ -22,17 +22,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+bool positive_finite(float x) { return x > 0.0f && isfinite(x); }
+
 int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, const int32_t* context_lens,
                        int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
                        int32_t Hkv, int32_t D, int32_t block_size, float scale, int32_t dtype,
                        void* workspace, size_t workspace_bytes, void* stream,
-                       int32_t requested_splits) {
+                       int32_t requested_splits, bool kv_fp8 = false, float k_scale = 1.0f,
+                       float v_scale = 1.0f) {
   pd::Shape s{B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype};
   pd::Plan plan;
   int32_t st = pd::make_plan(s, requested_splits, &plan);
   if (st != PD_OK) return st;
-  if (!(scale > 0.0f) || !isfinite(scale)) return PD_ERR_VALUE;
+  if (!positive_finite(scale)) return PD_ERR_VALUE;
+  if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale))) return PD_ERR_VALUE;
   if (B == 0) return PD_OK;  // empty batch: nothing to compute
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PD_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
@@ -49,8 +53,8 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
       overlap(out, qo_bytes, context_lens, (size_t)B * 4) ||
       (need > 0 && overlap(out, qo_bytes, workspace, need)))
     return PD_ERR_ALIAS;
-  pd::Launch l{q, k_cache, v_cache, block_table, context_lens, out, workspace, s, plan, scale,
-               stream};
+  pd::Launch l{q,     k_cache, v_cache, block_table, context_lens, out,     workspace,
+               s,     plan,    scale,   stream,      kv_fp8,       k_scale, v_scale};
   return pd::launch(l);
 }
 
@@ -94,7 +98,7 @@ const char* paged_decode_strerror(int32_t code) {
     case PD_ERR_UNSUPPORTED: return "shape not supported (needs D=128, Hq/Hkv=4, block_size 16|32)";
     case PD_ERR_HIP: return "HIP runtime rejected the launch";
     case PD_ERR_INTERNAL: return "internal error";
-    case PD_ERR_VALUE: return "scale must be finite and positive";
+    case PD_ERR_VALUE: return "scale (and k_scale, v_scale) must be finite and positive";
     default: return "unknown status code";
   }
 }
@@ -183,6 +187,22 @@ int32_t paged_decode_attention_splits(const void* q, const void* k_cache, const 
     return attention_impl(q, k_cache, v_cache, block_table, context_lens, max_blocks_per_seq,
                           out, B, Hq, Hkv, D, block_size, scale, dtype, workspace,
                           workspace_bytes, stream, num_splits);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* context_lens,
+                                   int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t block_size, float scale,
+                                   int32_t dtype, float k_scale, float v_scale, void* workspace,
+                                   size_t workspace_bytes, void* stream, int32_t num_splits) {
+  try {
+    if (num_splits < 0) return PD_ERR_SHAPE;
+    return attention_impl(q, k_cache, v_cache, block_table, context_lens, max_blocks_per_seq,
+                          out, B, Hq, Hkv, D, block_size, scale, dtype, workspace,
+                          workspace_bytes, stream, num_splits, true, k_scale, v_scale);
   } catch (...) {
     return PD_ERR_INTERNAL;
   }

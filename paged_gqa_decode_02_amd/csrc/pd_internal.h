@@ -30,7 +30,8 @@ struct Plan {
 // Most blocks one wave's slice may span (four block ids per lane).
 constexpr int kMaxWaveBlocks = 256;
 // Most waves in a workgroup: each wave holds two 16-token K/V tiles in LDS
-// (17 KiB), so 8 waves fill 136 KiB of a CU's 160 KiB.
+// (17.5 KiB; an FP8 cache: two staging tiles and one converted tile, 16.75
+// KiB), so 8 waves fill at most 140 KiB of a CU's 160 KiB.
 constexpr int kMaxWaves = 8;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.
@@ -63,6 +64,9 @@ struct Launch {
   Plan plan;
   float scale;
   void* stream;
+  bool kv_fp8;    // K/V hold E4M3FN codes (1 byte per element)
+  float k_scale;  // with kv_fp8: value = code * k_scale
+  float v_scale;  // with kv_fp8: value = code * v_scale
 };
 
 // Queues the decode kernel; PD_* status code.

@@ -62,7 +62,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int D = pd::kHeadDim;  // 128
 constexpr int G = pd::kGroup;    // 4
 constexpr int kIdRegs = pd::kMaxWaveBlocks / 64;  // block ids per lane
-constexpr uint32_t kRowBytes = D * 2;          // one token row of one KV head
+constexpr uint32_t kRowBytes = D * 2;          // one token row of one KV head (16-bit)
+constexpr uint32_t kRowBytes8 = D;             // the same row of an FP8 cache
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 data format
 constexpr int kStream = 2;                     // cache policy "nt": read once
@@ -85,8 +86,9 @@ struct KArgs {
   int32_t Pw;  // tokens per slice, a multiple of the block size, <= 256 blocks
   int32_t NH;  // KV heads per workgroup
   int32_t NT;  // token slices per workgroup
-  float scale_log2;    // scale * log2(e)
-  uint32_t blk_bytes;  // block_size * Hkv * D * 2
+  float scale_log2;    // scale * log2(e), times k_scale for an FP8 cache
+  float out_scale;     // v_scale for an FP8 cache, else 1
+  uint32_t blk_bytes;  // block_size * Hkv * D * element bytes
 };
 
 template <bool BF16>
@@ -181,6 +183,9 @@ constexpr uint32_t kKGroup = 4 * kRowBytes + 64;
 constexpr uint32_t kVGroup = 4 * kRowBytes + 128;
 constexpr uint32_t kKTile = 4 * kKGroup;             // 4352
 constexpr uint32_t kLdsTile = kKTile + 4 * kVGroup;  // K then V: 8960
+// An FP8 cache lands in a plain staging tile (16 rows of 128 bytes for K,
+// then for V) and is converted into the 16-bit layout above before use.
+constexpr uint32_t kStage8 = 2 * kTileTok * kRowBytes8;  // 4096
 
 // Tile buffers per wave (tiles in flight while one is computed: buffers - 1),
 // as many as fit the 160 KiB of LDS for the workgroup size, up to PD_NBUF.
@@ -188,8 +193,12 @@ constexpr uint32_t kLdsTile = kKTile + 4 * kVGroup;  // K then V: 8960
 #define PD_NBUF 2
 #endif
 constexpr uint32_t kLdsBytes = 160 * 1024;
+template <bool KV8>
+constexpr uint32_t stage_bytes() { return KV8 ? kStage8 : kLdsTile; }
+template <bool KV8>
 constexpr int tile_buffers(int nw) {
-  return PD_NBUF >= 3 && 3 * nw * kLdsTile <= kLdsBytes ? 3 : 2;
+  return PD_NBUF >= 3 && 3 * nw * stage_bytes<KV8>() + (KV8 ? nw * kLdsTile : 0) <= kLdsBytes
+             ? 3 : 2;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -199,6 +208,8 @@ typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr_t;
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8) that waits for vmcnt <= n and nothing else.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and one that waits for every LDS access of the wave (lgkmcnt 0) only
+constexpr int kWaitLds = 15 | (3 << 14) | (7 << 4);
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -316,6 +327,47 @@ __device__ __forceinline__ void tile_compute(WaveState& st, const char* kt,
   }
 }
 
+// FP8 staging tile -> 16-bit tile layout. Lane l takes 16-byte chunks
+// 64i + l (i < 2) of the K and of the V staging tile: token c/8, dims
+// 16(c%8) .. +16; their 16 codes become two 16-byte chunks of 8 values each,
+// written where the 16-bit layout keeps them. E4M3FN values are exact in
+// both bf16 and f16, so the conversion (scale 1) loses nothing.
+template <bool BF16>
+__device__ __forceinline__ void convert_fp8_tile(const char* st, char* kt, int lane) {
+#pragma unroll
+  for (int tv = 0; tv < 2; ++tv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = 64 * i + lane;
+      const int t = c >> 3, c8 = c & 7, n = t >> 2, r = t & 3;
+      const u32x4 x = *(const u32x4*)(st + tv * (kStage8 / 2) + 16 * c);
+      u32x4 y[2];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t lo, hi;
+        if constexpr (BF16) {
+          lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+          hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+        } else {
+          lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], 1.0f, false));
+          hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], 1.0f, true));
+        }
+        y[w >> 1][2 * (w & 1)] = lo;
+        y[w >> 1][2 * (w & 1) + 1] = hi;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int chunk = 2 * c8 + h;  // 16-bit chunk (8 dims) of the row
+        const uint32_t off = tv == 0
+            ? (uint32_t)n * kKGroup + (uint32_t)r * kRowBytes + 16u * (uint32_t)((chunk + r) & 15)
+            : kKTile + (uint32_t)n * kVGroup + (uint32_t)r * kRowBytes +
+                  16u * (uint32_t)((chunk + 2 * r) & 15);
+        *(u32x4*)(kt + off) = y[h];
+      }
+    }
+  }
+}
+
 // Block id number idx (< 256, wave-uniform) of the wave's range.
 __device__ __forceinline__ int pick_id(const int (&ids)[kIdRegs], int idx) {
   const int l = idx & 63;
@@ -336,16 +388,19 @@ __device__ __forceinline__ void store4(uint16_t* o, f32x4 r, float inv) {
   *(u32x2*)o = u32x2{pack2<BF16>(r[0] * inv, r[1] * inv), pack2<BF16>(r[2] * inv, r[3] * inv)};
 }
 
-template <bool BF16, int BS, bool SPLIT, int NW>
+template <bool BF16, int BS, bool SPLIT, int NW, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
-  constexpr int kNBuf = tile_buffers(NW);
-  constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * 8);
+  constexpr int kNBuf = tile_buffers<KV8>(NW);
+  constexpr int kLoads = KV8 ? 4 : 8;  // load instructions per tile
+  constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * kLoads);
+  constexpr uint32_t kStage = stage_bytes<KV8>();
   // one array per tile buffer, so the compiler can wait for exactly the
   // loads of the buffer about to be read
-  __shared__ __align__(16) char lds0[NW * kLdsTile];
-  __shared__ __align__(16) char lds1[NW * kLdsTile];
-  __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kLdsTile : 16];
+  __shared__ __align__(16) char lds0[NW * kStage];
+  __shared__ __align__(16) char lds1[NW * kStage];
+  __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kStage : 16];
+  __shared__ __align__(16) char ldsc[KV8 ? NW * kLdsTile : 16];  // converted FP8 tile
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int b = blockIdx.z;
@@ -360,7 +415,7 @@ void pd_decode_kernel(const KArgs a) {
   const int sl = lane & 15;
   auto tile_buf = [&](int d) -> char* {
     char* base = d == 0 ? lds0 : d == 1 ? lds1 : lds2;
-    return base + w * kLdsTile;
+    return base + w * kStage;
   };
 
   const int t0 = p * a.P;
@@ -414,11 +469,17 @@ void pd_decode_kernel(const KArgs a) {
   const int nst = __builtin_amdgcn_readfirstlane(
       tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
-  const uint32_t tok_bytes = a.Hkv * kRowBytes;
-  // global offsets of this lane's 16 bytes in load instruction 0 of a tile
-  const uint32_t head_off = (uint32_t)row * tok_bytes + (uint32_t)g * kRowBytes;
-  const uint32_t koff_g = head_off + (uint32_t)((sl - row) & 15) * 16u;
-  const uint32_t voff_g = head_off + (uint32_t)((sl - 2 * row) & 15) * 16u;
+  const uint32_t tok_bytes = a.Hkv * (KV8 ? kRowBytes8 : kRowBytes);
+  // global offsets of this lane's 16 bytes in load instruction 0 of a tile:
+  // 16-bit rows take 16 lanes each (4 rows per instruction), chunks rotated;
+  // FP8 rows take 8 lanes each (8 rows per instruction), in order
+  const int lrow = KV8 ? lane >> 3 : row;
+  const uint32_t head_off =
+      (uint32_t)lrow * tok_bytes + (uint32_t)g * (KV8 ? kRowBytes8 : kRowBytes);
+  const uint32_t koff_g =
+      head_off + (uint32_t)(KV8 ? (lane & 7) : ((sl - row) & 15)) * 16u;
+  const uint32_t voff_g =
+      head_off + (uint32_t)(KV8 ? (lane & 7) : ((sl - 2 * row) & 15)) * 16u;
   // LDS offsets of the two read patterns (see the tile layout above)
   uint32_t koff[4], voff[8];
   {
@@ -448,20 +509,21 @@ void pd_decode_kernel(const KArgs a) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const uint32_t tb = (uint32_t)(tok % BS) * tok_bytes;
     char* kt = tile_buf(d);
+    constexpr int kRowsPerLoad = KV8 ? 8 : 4;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const bool ok = tw0 + tok + 4 * n + row < tw1;
-      const uint32_t nb = tb + 4u * n * tok_bytes;
+    for (int n = 0; n < kLoads / 2; ++n) {
+      const bool ok = tw0 + tok + kRowsPerLoad * n + lrow < tw1;
+      const uint32_t nb = tb + (uint32_t)(kRowsPerLoad * n) * tok_bytes;
       uint32_t ko = ok ? nb + koff_g : kOutOfBlock;
       uint32_t vo = ok ? nb + voff_g : kOutOfBlock;
       // the offsets are plain register values to the optimizer, so it cannot
       // turn the selects into a divergent branch around the loads (which
       // would issue a load twice and break the exact wait counts)
       asm("" : "+v"(ko), "+v"(vo));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + n * kKGroup), 16, ko, 0, 0,
-                                               kStream);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + kKTile + n * kVGroup), 16, vo,
-                                               0, 0, kStream);
+      const uint32_t kd = KV8 ? n * 1024u : n * kKGroup;
+      const uint32_t vd = KV8 ? kStage8 / 2 + n * 1024u : kKTile + n * kVGroup;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + kd), 16, ko, 0, 0, kStream);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + vd), 16, vo, 0, 0, kStream);
     }
   };
 
@@ -481,12 +543,34 @@ void pd_decode_kernel(const KArgs a) {
       // compiler does not always see that these LDS reads depend on them.
       __builtin_amdgcn_s_waitcnt(kWaitTile);
       __builtin_amdgcn_sched_barrier(0);
-      if (j < nst) {
-        const int tile0 = tw0 + kTileTok * j;
-        tile_compute<BF16>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
-                           tile0 + kTileTok > tw1, c);
+      // Before a buffer is refilled every LDS read of it has completed: the
+      // refill's LDS writes are not ordered after reads still in flight, and
+      // a refill past the slice reads no memory, so it lands at once.
+      if constexpr (KV8) {
+        // convert, then refill the staging buffer before computing
+        char* ct = ldsc + w * kLdsTile;
+        if (j < nst) convert_fp8_tile<BF16>(tile_buf(d), ct, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + kNBuf, d);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j < nst) {
+          const int tile0 = tw0 + kTileTok * j;
+          tile_compute<BF16>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
+                             tile0 + kTileTok > tw1, c);
+        }
+      } else {
+        if (j < nst) {
+          const int tile0 = tw0 + kTileTok * j;
+          tile_compute<BF16>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
+                             tile0 + kTileTok > tw1, c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + kNBuf, d);
       }
-      issue(j + kNBuf, d);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -546,7 +630,7 @@ void pd_decode_kernel(const KArgs a) {
   if constexpr (!SPLIT) {
     if (owner) {
       uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
-      const float inv = 1.0f / l_r;
+      const float inv = a.out_scale / l_r;
       store4<BF16>(o, o0, inv);
       store4<BF16>(o + 16, o1, inv);
     }
@@ -630,7 +714,7 @@ void pd_decode_kernel(const KArgs a) {
       }
     }
     uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
-    const float inv = 1.0f / den;
+    const float inv = a.out_scale / den;
     store4<BF16>(o, acc0, inv);
     store4<BF16>(o + 16, acc1, inv);
   }
@@ -643,19 +727,29 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-template <bool BF16, int BS, bool SPLIT>
+template <bool BF16, int BS, bool SPLIT, bool KV8>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   void* args[] = {(void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
-  const void* f = nw <= 4 ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4>
-                          : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8>;
+  const void* f = nw <= 4 ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8>
+                          : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8, KV8>;
   return hipLaunchKernel(f, grid, dim3(nw * 64), args, 0, st);
 }
 
-template <bool BF16, bool SPLIT>
+template <bool BF16, bool SPLIT, bool KV8>
 hipError_t pick_block(const KArgs& ka, dim3 grid, int bs, int nw, hipStream_t st) {
-  return bs == 32 ? launch_decode<BF16, 32, SPLIT>(ka, grid, nw, st)
-                  : launch_decode<BF16, 16, SPLIT>(ka, grid, nw, st);
+  return bs == 32 ? launch_decode<BF16, 32, SPLIT, KV8>(ka, grid, nw, st)
+                  : launch_decode<BF16, 16, SPLIT, KV8>(ka, grid, nw, st);
+}
+
+template <bool KV8>
+hipError_t pick_dtype(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
+                      hipStream_t st) {
+  if (bf16)
+    return split ? pick_block<true, true, KV8>(ka, grid, bs, nw, st)
+                 : pick_block<true, false, KV8>(ka, grid, bs, nw, st);
+  return split ? pick_block<false, true, KV8>(ka, grid, bs, nw, st)
+               : pick_block<false, false, KV8>(ka, grid, bs, nw, st);
 }
 
 }  // namespace
@@ -686,8 +780,10 @@ int32_t launch(const Launch& l) {
   ka.Pw = l.plan.wave_tokens;
   ka.NH = l.plan.heads_per_group;
   ka.NT = l.plan.slices;
-  ka.scale_log2 = l.scale * 1.4426950408889634f;
-  ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv * kRowBytes;
+  ka.scale_log2 = l.scale * 1.4426950408889634f * (l.kv_fp8 ? l.k_scale : 1.0f);
+  ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
+  ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
+                 (l.kv_fp8 ? kRowBytes8 : kRowBytes);
   const dim3 grid(l.plan.splits, l.shape.Hkv / l.plan.heads_per_group, l.shape.B);
   const int nw = l.plan.heads_per_group * l.plan.slices;
   // each wave owns kLdsTile bytes of every tile buffer of its workgroup
@@ -695,13 +791,10 @@ int32_t launch(const Launch& l) {
     return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;
-  hipError_t e;
-  if (l.shape.dtype == PD_DTYPE_BF16)
-    e = split ? pick_block<true, true>(ka, grid, l.shape.block_size, nw, st)
-              : pick_block<true, false>(ka, grid, l.shape.block_size, nw, st);
-  else
-    e = split ? pick_block<false, true>(ka, grid, l.shape.block_size, nw, st)
-              : pick_block<false, false>(ka, grid, l.shape.block_size, nw, st);
+  const bool bf16 = l.shape.dtype == PD_DTYPE_BF16;
+  const hipError_t e = l.kv_fp8
+      ? pick_dtype<true>(ka, grid, l.shape.block_size, nw, bf16, split, st)
+      : pick_dtype<false>(ka, grid, l.shape.block_size, nw, bf16, split, st);
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

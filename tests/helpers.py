@@ -80,7 +80,12 @@ def run_library(case, num_splits=None, dev=None):
     import paged_gqa_decode_02_amd as pd
     dev = dev if dev is not None else device_case(case)
     q, k, v, bt, cl = dev
-    out = pd.paged_decode_attention(q, k, v, bt, cl, scale=case.scale, num_splits=num_splits)
+    if getattr(case, "fp8", False):
+        out = pd.paged_decode_attention_fp8(q, k, v, bt, cl, k_scale=case.k_scale,
+                                            v_scale=case.v_scale, scale=case.scale,
+                                            num_splits=num_splits)
+    else:
+        out = pd.paged_decode_attention(q, k, v, bt, cl, scale=case.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return out
 

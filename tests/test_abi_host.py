@@ -189,3 +189,24 @@ def test_workspace_holds_partials_lse_and_counters(B, L, bs):
         a256 = lambda x: (x + 255) // 256 * 256
         need = 256 * 1024 + a256(B * 32 * S * 128 * 4) + a256(B * 32 * S * 4)
         assert pd.paged_decode_workspace_bytes(B, 32, 8, 128, MB, bs, BF16) >= need
+
+
+@pytest.mark.parametrize("k_scale,v_scale,splits,code", [
+    (1.0, 1.0, -1, "PD_ERR_SHAPE"),
+    (0.0, 1.0, 0, "PD_ERR_VALUE"),
+    (1.0, 0.0, 0, "PD_ERR_VALUE"),
+    (-1.0, 1.0, 0, "PD_ERR_VALUE"),
+    (float("nan"), 1.0, 0, "PD_ERR_VALUE"),
+    (1.0, float("inf"), 0, "PD_ERR_VALUE"),
+])
+def test_fp8_entry_point_argument_errors(k_scale, v_scale, splits, code):
+    f = pd.lib.paged_decode_attention_fp8
+    args = [BASE, BASE + (1 << 24), BASE + (2 << 24), BASE + (3 << 24), BASE + (3 << 24) + 4096,
+            1, BASE + (4 << 24), 2, 32, 8, 128, 16, 0.0883883, BF16]
+    assert f(*args, k_scale, v_scale, 0, 0, 0, splits) == CODES[code]
+
+
+def test_fp8_entry_point_empty_batch_is_a_no_op():
+    f = pd.lib.paged_decode_attention_fp8
+    assert f(0, 0, 0, 0, 0, 1, 0, 0, 32, 8, 128, 16, 0.0883883, BF16, 1.0, 1.0, 0, 0, 0, 0) == \
+        CODES["PD_OK"]
