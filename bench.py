@@ -51,21 +51,35 @@ def kernel_sha() -> str:
 
 
 def make_workload(name: str, seed: int = 0):
+    """Workload by name; a trailing "_fp8" stores the K/V cache as E4M3FN codes."""
     import workloads
+    kv = ""
+    if name.endswith("_fp8"):
+        name, kv = name[:-4], "fp8"
     if name == "large":
-        return workloads.large(seed)
+        return workloads.large(seed, kv_dtype=kv)
     if name == "ragged":
-        return workloads.ragged(seed)
+        return workloads.ragged(seed, kv_dtype=kv)
     if name == "tiny":
-        return workloads.tiny(seed)
+        return workloads.tiny(seed, kv_dtype=kv)
     if name.startswith("splitk_"):
         _, b, l = name.split("_")
-        return workloads.splitk(int(b[1:]), int(l[1:]), seed)
+        return workloads.splitk(int(b[1:]), int(l[1:]), seed, kv_dtype=kv)
     if name.startswith("short_"):
         # short_B32_L64_bf16_bs16
         _, b, l, dt, bs = name.split("_")
-        return workloads.short(int(b[1:]), int(l[1:]), dt, int(bs[2:]), seed)
+        return workloads.short(int(b[1:]), int(l[1:]), dt, int(bs[2:]), seed, kv_dtype=kv)
     raise SystemExit(f"unknown workload {name!r}")
+
+
+def attend(pd, case, q, k, v, bt, cl, out, ws, num_splits=None):
+    """One library call on the workload's inputs (the FP8 entry point for an FP8 cache)."""
+    if case.fp8:
+        return pd.paged_decode_attention_fp8(q, k, v, bt, cl, out, k_scale=case.k_scale,
+                                             v_scale=case.v_scale, scale=case.scale,
+                                             workspace=ws, num_splits=num_splits)
+    return pd.paged_decode_attention(q, k, v, bt, cl, out, scale=case.scale, workspace=ws,
+                                     num_splits=num_splits)
 
 
 def upload(case, torch):
@@ -145,8 +159,7 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
 
     def call(i):
         q, k, v, bt, cl = reps[i % R]
-        pd.paged_decode_attention(q, k, v, bt, cl, outs[i % R], scale=case.scale,
-                                  workspace=wss[i % R])
+        attend(pd, case, q, k, v, bt, cl, outs[i % R], wss[i % R])
 
     call(0)
     torch.cuda.synchronize()
@@ -166,6 +179,8 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
            "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
            "algorithmic_bytes": nbytes, "splits": S, "partition_tokens": P,
            "replicas": R, "rotated_bytes": R * foot, "max_abs_err": round(err["max_abs"], 6)}
+    if case.fp8:
+        res["kv_dtype"] = "fp8_e4m3fn"
     del reps, outs, wss
     torch.cuda.empty_cache()
     return res
@@ -181,12 +196,20 @@ def cpu_baseline(case, nseq: int, min_seconds: float = 10.0, max_calls: int = 25
     calls, used = 0, 0
     t0 = time.perf_counter()
     while calls < max_calls and (calls == 0 or time.perf_counter() - t0 < min_seconds):
-        _, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
-                                      case.block_table[:nseq], sub_cl, scale=case.scale,
-                                      dtype=case.dtype, nthreads=nthreads, return_threads=True)
+        if case.fp8:
+            _, _, used = oracle.attention_fp8(case.q[:nseq], case.k_cache, case.v_cache,
+                                              case.block_table[:nseq], sub_cl, scale=case.scale,
+                                              dtype=case.dtype, k_scale=case.k_scale,
+                                              v_scale=case.v_scale, nthreads=nthreads,
+                                              return_threads=True)
+        else:
+            _, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
+                                          case.block_table[:nseq], sub_cl, scale=case.scale,
+                                          dtype=case.dtype, nthreads=nthreads,
+                                          return_threads=True)
         calls += 1
     dt = (time.perf_counter() - t0) / calls
-    nbytes = 4096 * int(sub_cl.astype("int64").sum()) + 16384 * nseq
+    nbytes = (2048 if case.fp8 else 4096) * int(sub_cl.astype("int64").sum()) + 16384 * nseq
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": calls,
             "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
@@ -316,8 +339,7 @@ def main():
                                 case.block_size, dt, args.splits)
 
     def call(i):
-        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=case.scale, workspace=ws,
-                                  num_splits=args.splits)
+        attend(pd, case, q, k, v, bt, cl, out, ws, args.splits)
 
     call(0)
     torch.cuda.synchronize()
@@ -347,6 +369,7 @@ def main():
            "config": {"workload": case.name, "batch": case.B, "context": int(case.context_lens.max()),
                       "Hq": case.Hq, "Hkv": case.Hkv, "head_dim": case.D,
                       "block_size": case.block_size, "splits": S, "partition_tokens": P,
+                      "kv_dtype": "fp8_e4m3fn" if case.fp8 else case.dtype,
                       "algorithmic_bytes": nbytes},
            "parity": {"ok": ok, "bitwise_stable_over_timed_calls": stable,
                       **{k2: round(v2, 6) for k2, v2 in err.items()}},
@@ -356,7 +379,8 @@ def main():
         others = {}
         for name in ("splitk_B8_L1024", "splitk_B8_L4096", "splitk_B32_L1024", "splitk_B64_L1024",
                      "splitk_B1_L1024", "ragged", "short_B32_L64_bf16_bs16",
-                     "short_B32_L64_f16_bs32", "tiny"):
+                     "short_B32_L64_f16_bs32", "tiny", "large_fp8", "splitk_B32_L1024_fp8",
+                     "splitk_B8_L1024_fp8", "ragged_fp8"):
             others[name] = bench_other(name, torch, pd)
         res["others"] = others
     if not args.no_cpu_baseline:
