@@ -1,0 +1,205 @@
+"""Pins of the RoPE + paged-KV-write oracle (oracle/rope.py) against what the
+rotary embedding's definition fixes (RoFormer, section 3.2; rotate-half
+pairing), independent of the oracle's own formulas: closed forms at D = 2 and
+D = 4, the complex-multiplication form, the relative-position property, a
+pure-Python brute force and cache round trips through block tables."""
+import cmath
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rope
+import workloads
+from workloads import rope as wrope
+
+
+def test_table_row_zero_is_identity():
+    t = rope.cos_sin_table(4, 128, 1e6)
+    assert np.all(t[0, :64] == 1.0) and np.all(t[0, 64:] == 0.0)
+
+
+def test_d2_closed_form():
+    # D = 2: one pair, theta_0 = 1 whatever the base; (1, 0) at position m
+    # turns to (cos m, sin m): counter-clockwise, as R(m theta) of RoFormer
+    for m in (1, 2, 7):
+        tab = rope.cos_sin_table(m + 1, 2, 10000.0)
+        out = rope.rotate(np.array([1.0, 0.0]), tab[m, :1], tab[m, 1:])
+        assert out[0] == pytest.approx(math.cos(m), abs=1e-15)
+        assert out[1] == pytest.approx(math.sin(m), abs=1e-15)
+        # and (0, 1) turns to (-sin m, cos m)
+        out = rope.rotate(np.array([0.0, 1.0]), tab[m, :1], tab[m, 1:])
+        assert out[0] == pytest.approx(-math.sin(m), abs=1e-15)
+        assert out[1] == pytest.approx(math.cos(m), abs=1e-15)
+
+
+def test_d4_frequency_and_pairing():
+    # D = 4, base 100: theta = (1, 100^-1/2 = 0.1). Dimension 1 pairs with
+    # dimension 3 (rotate-half), and turns by 10 * 0.1 = 1 rad at position 10.
+    tab = rope.cos_sin_table(11, 4, 100.0)
+    x = np.array([0.0, 1.0, 0.0, 0.0])
+    out = rope.rotate(x, tab[10, :2], tab[10, 2:])
+    assert out == pytest.approx([0.0, math.cos(1.0), 0.0, math.sin(1.0)], abs=1e-14)
+    # dimension 0 turns by 10 rad, into dimension 2
+    out = rope.rotate(np.array([1.0, 0.0, 0.0, 0.0]), tab[10, :2], tab[10, 2:])
+    assert out == pytest.approx([math.cos(10.0), 0.0, math.sin(10.0), 0.0], abs=1e-14)
+
+
+def test_inv_frequencies_closed_form():
+    th = rope.inv_frequencies(128, 1e6)
+    assert th[0] == 1.0
+    assert th[32] == pytest.approx(1e6 ** -0.5, rel=1e-15)
+    assert th[63] == pytest.approx(1e6 ** (-126 / 128), rel=1e-14)
+    assert np.all(np.diff(th) < 0)
+
+
+def test_complex_form():
+    # pair i as the complex number x[i] + j x[i + D/2], times exp(j m theta_i)
+    rng = np.random.default_rng(5)
+    D, base = 128, 1e6
+    x = rng.standard_normal(D)
+    th = [base ** (-2 * i / D) for i in range(D // 2)]
+    for m in (0, 1, 37, 4095, 31999):
+        tab = rope.cos_sin_table(m + 1, D, base)
+        out = rope.rotate(x, tab[m, : D // 2], tab[m, D // 2:])
+        for i in range(D // 2):
+            z = complex(x[i], x[i + D // 2]) * cmath.exp(1j * m * th[i])
+            assert out[i] == pytest.approx(z.real, abs=1e-11)
+            assert out[i + D // 2] == pytest.approx(z.imag, abs=1e-11)
+
+
+def test_relative_position_and_norm():
+    # <R(m) q, R(n) k> depends on m - n only; each pair keeps its length
+    rng = np.random.default_rng(6)
+    D, base = 64, 10000.0
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    tab = rope.cos_sin_table(200, D, base)
+    h = D // 2
+
+    def R(x, m):
+        return rope.rotate(x, tab[m, :h], tab[m, h:])
+
+    for m, n, s in ((5, 3, 40), (100, 17, 60), (9, 9, 150)):
+        assert np.dot(R(q, m), R(k, n)) == pytest.approx(np.dot(R(q, m + s), R(k, n + s)), abs=1e-10)
+        assert np.dot(R(q, m), R(k, n)) == pytest.approx(np.dot(R(q, m - n), k), abs=1e-10)
+        r = R(q, m)
+        assert np.hypot(r[:h], r[h:]) == pytest.approx(np.hypot(q[:h], q[h:]), abs=1e-12)
+
+
+def test_table_f32_is_rounded_exact_table():
+    t64 = rope.cos_sin_table(300, 128, 1e6)
+    t32 = rope.cos_sin_table_f32(300, 128, 1e6)
+    assert t32.dtype == np.float32
+    # every float32 entry is the nearest float32 to the exact value
+    up = np.nextafter(t32, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(t32, np.float32(-np.inf)).astype(np.float64)
+    e = np.abs(t32.astype(np.float64) - t64)
+    assert np.all(e <= np.abs(up - t64)) and np.all(e <= np.abs(dn - t64))
+    assert np.allclose(t64[:, :64] ** 2 + t64[:, 64:] ** 2, 1.0, atol=1e-15)
+
+
+def _brute(case, table):
+    """Pure-Python loops, scalar math, for a tiny case."""
+    T, Hq, Hkv, D = case.T, case.Hq, case.Hkv, case.D
+    h2 = D // 2
+    qv = oracle.widen(case.q, case.dtype)
+    kv = oracle.widen(case.k, case.dtype)
+    qo = np.zeros((T, Hq, D))
+    ko = np.zeros((T, Hkv, D))
+    for t in range(T):
+        p = int(case.positions[t])
+        for src, dst, H in ((qv, qo, Hq), (kv, ko, Hkv)):
+            for h in range(H):
+                for i in range(h2):
+                    c, s = float(table[p, i]), float(table[p, h2 + i])
+                    a, b = float(src[t, h, i]), float(src[t, h, i + h2])
+                    dst[t, h, i] = a * c - b * s
+                    dst[t, h, i + h2] = b * c + a * s
+    return qo, ko
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_brute_force_tiny(dtype):
+    case = wrope.scatter(5, Hq=8, Hkv=2, D=64, dtype=dtype, max_position=1000, pad_every=3, seed=2)
+    table = rope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    q_rot, k_rot, kc, vc = rope.rope_kv_write(case.q, case.k, case.v, case.positions,
+                                              case.slot_mapping, table, case.k_cache,
+                                              case.v_cache, dtype=dtype)
+    qb, kb = _brute(case, table)
+    assert np.allclose(q_rot, qb, rtol=0, atol=1e-12)
+    assert np.allclose(k_rot, kb, rtol=0, atol=1e-12)
+    # slot s sits at block s // bs, row s % bs; padding tokens write nothing
+    bs = case.block_size
+    touched = np.zeros(case.k_cache.shape[:2], bool)
+    for t in range(case.T):
+        s = int(case.slot_mapping[t])
+        if s < 0:
+            continue
+        touched[s // bs, s % bs] = True
+        assert np.array_equal(kc[s // bs, s % bs], oracle.round_to_dtype(kb[t], dtype))
+        assert np.array_equal(vc[s // bs, s % bs], case.v[t])
+    assert np.array_equal(kc[~touched], case.k_cache[~touched])
+    assert np.array_equal(vc[~touched], case.v_cache[~touched])
+    assert int((case.slot_mapping < 0).sum()) == 1
+
+
+def test_position_zero_writes_keys_unchanged():
+    case = wrope.scatter(4, Hq=4, Hkv=1, D=128, max_position=1, seed=3)
+    assert np.all(case.positions == 0)
+    table = rope.cos_sin_table_f32(1, 128, case.base)
+    q_rot, k_rot, kc, _ = rope.rope_kv_write(case.q, case.k, case.v, case.positions,
+                                             case.slot_mapping, table, case.k_cache,
+                                             case.v_cache, dtype="bf16")
+    assert np.array_equal(q_rot, oracle.widen(case.q, "bf16"))
+    flat = kc.reshape(-1, 1, 128)
+    for t in range(4):
+        assert np.array_equal(flat[case.slot_mapping[t]], case.k[t])
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_decode_step_round_trip(bs):
+    # the new token of each sequence lands where the decode reads position L-1
+    dec = workloads.make_case("rt", 6, [1, 17, 33, 64, 5, 40], dtype="bf16", block_size=bs,
+                              Hq=8, Hkv=2, D=128, seed=4)
+    case = wrope.decode_step(dec, seed=9)
+    table = rope.cos_sin_table_f32(case.max_position, 128, case.base)
+    _, k_rot, kc, vc = rope.rope_kv_write(case.q, case.k, case.v, case.positions,
+                                          case.slot_mapping, table, case.k_cache,
+                                          case.v_cache, dtype="bf16")
+    for b in range(dec.B):
+        L = int(dec.context_lens[b])
+        blk = dec.block_table[b, (L - 1) // bs]
+        assert np.array_equal(kc[blk, (L - 1) % bs], oracle.round_to_dtype(k_rot[b], "bf16"))
+        assert np.array_equal(vc[blk, (L - 1) % bs], case.v[b])
+        assert case.positions[b] == L - 1
+
+
+def test_prefill_slots_follow_block_tables():
+    case = wrope.prefill(3, 40, Hq=4, Hkv=1, D=64, block_size=16, max_position=500, seed=1)
+    assert case.T == 120
+    s = case.slot_mapping.astype(np.int64)
+    assert len(np.unique(s)) == 120 and np.all(s >= 0)
+    for q in range(3):
+        p = case.positions[q * 40:(q + 1) * 40].astype(np.int64)
+        assert np.all(np.diff(p) == 1)
+        sl = s[q * 40:(q + 1) * 40]
+        # consecutive positions in one block occupy consecutive rows
+        same = (p[1:] // 16) == (p[:-1] // 16)
+        assert np.all((sl[1:] - sl[:-1])[same] == 1)
+        assert np.all(sl % 16 == p % 16)
+
+
+def test_oracle_rejects_bad_inputs():
+    case = wrope.scatter(3, Hq=4, Hkv=1, D=64, max_position=10, seed=0)
+    table = rope.cos_sin_table_f32(10, 64, case.base)
+    args = (case.q, case.k, case.v)
+    with pytest.raises(ValueError):
+        rope.rope_kv_write(*args, np.array([0, 1, 10]), case.slot_mapping, table,
+                           case.k_cache, case.v_cache, dtype="bf16")
+    with pytest.raises(ValueError):
+        rope.rope_kv_write(*args, case.positions, np.array([0, 0, 1]), table,
+                           case.k_cache, case.v_cache, dtype="bf16")
+    with pytest.raises(ValueError):
+        rope.rope_kv_write(*args, case.positions, np.array([0, 1, case.num_blocks * 16]), table,
+                           case.k_cache, case.v_cache, dtype="bf16")
