@@ -215,3 +215,84 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, o
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return out
+
+
+# --- KV-cache operations (include/paged_kv.h) --------------------------------
+
+_L, _D = ctypes.c_int64, ctypes.c_double
+lib.rope_cos_sin_table.argtypes = [_P, _I, _I, _D, _P]
+lib.rope_cos_sin_table.restype = _I
+lib.rope_paged_kv_write.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _P, _I, _P, _P, _P, _I,
+                                    _I, _I, _I, _I, _I, _I, _P]
+lib.rope_paged_kv_write.restype = _I
+
+
+def _handle(stream, device):
+    st = stream if stream is not None else torch.cuda.current_stream(device)
+    return st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
+
+
+def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=None, stream=None):
+    """float32 [max_position, rotary_dim] cos/sin table of the rotary
+    embedding (``rope_cos_sin_table``), built on the GPU."""
+    if out is None:
+        out = torch.empty((max_position, rotary_dim), dtype=torch.float32, device=device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or \
+            tuple(out.shape) != (max_position, rotary_dim):
+        raise ValueError("out must be a contiguous float32 [max_position, rotary_dim] tensor")
+    rc = lib.rope_cos_sin_table(out.data_ptr(), int(max_position), int(rotary_dim), float(base),
+                                _handle(stream, out.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return out
+
+
+def _rows(name, t, H, D):
+    """Row stride (elements) of a [T, H, D] view whose heads are contiguous."""
+    if t.dim() != 3 or t.shape[1] != H or t.shape[2] != D:
+        raise ValueError(f"{name} must be [T, {H}, {D}]")
+    if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != D):
+        raise ValueError(f"{name}: heads of a token must be contiguous (strides [*, D, 1])")
+    return int(t.stride(0)) if t.shape[0] > 1 else H * D
+
+
+def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out=None,
+                        *, stream=None):
+    """RoPE + paged KV-cache write (``rope_paged_kv_write``) on the current
+    (or given) stream.
+
+    q [T,Hq,D], k/v [T,Hkv,D] (f16 or bf16; views into one packed QKV array
+    are fine as long as each head is contiguous); positions, slot_mapping
+    int32 [T]; cos_sin float32 [max_position, D] (``rope_cos_sin_table``);
+    k_cache/v_cache [num_blocks,block_size,Hkv,D] (written in place). Returns
+    q_out [T,Hq,D] (allocated when not given; may be q itself).
+    """
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype or \
+            k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k, v and the caches must share one dtype, float16 or bfloat16")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or not k_cache.is_contiguous() or \
+            not v_cache.is_contiguous():
+        raise ValueError("k_cache/v_cache must be contiguous [num_blocks,block_size,Hkv,D]")
+    NB, bs, Hkv, D = (int(x) for x in k_cache.shape)
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    qs, ks, vs = _rows("q", q, Hq, D), _rows("k", k, Hkv, D), _rows("v", v, Hkv, D)
+    if k.shape[0] != T or v.shape[0] != T:
+        raise ValueError("q, k and v must have the same number of tokens")
+    for name, t in (("positions", positions), ("slot_mapping", slot_mapping)):
+        if t.dtype != torch.int32 or t.shape != (T,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 [T] tensor")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != D or \
+            not cos_sin.is_contiguous():
+        raise ValueError("cos_sin must be a contiguous float32 [max_position, D] tensor")
+    if q_out is None:
+        q_out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
+    if tuple(q_out.shape) != (T, Hq, D) or q_out.dtype != q.dtype or not q_out.is_contiguous():
+        raise ValueError("q_out must be a contiguous [T, Hq, D] tensor of q's dtype")
+    rc = lib.rope_paged_kv_write(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), qs, ks, vs, positions.data_ptr(),
+        slot_mapping.data_ptr(), cos_sin.data_ptr(), int(cos_sin.shape[0]), q_out.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[q.dtype],
+        _handle(stream, q.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return q_out

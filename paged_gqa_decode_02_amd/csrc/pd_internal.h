@@ -75,4 +75,26 @@ int32_t launch(const Launch& l);
 // Queues a kernel that zeroes `bytes` (a multiple of 4) at `ws`.
 int32_t zero_workspace(void* ws, size_t bytes, void* stream);
 
+// RoPE + paged KV-cache write (pd_rope.hip); everything validated by the
+// caller. Row strides are in elements; heads of a row are D apart.
+struct RopeLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_row_stride, k_row_stride, v_row_stride;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  const float* cos_sin;
+  int32_t max_position;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_blocks;
+  int32_t T, Hq, Hkv, D, block_size, dtype;
+  void* stream;
+};
+int32_t launch_rope_kv_write(const RopeLaunch& l);
+int32_t launch_rope_table(float* table, int32_t max_position, int32_t D, double base,
+                          void* stream);
+
 }  // namespace pd

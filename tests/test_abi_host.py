@@ -12,19 +12,24 @@ import paged_gqa_decode_02_amd as pd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_decode.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 F16, BF16 = pd.PD_DTYPE_F16, pd.PD_DTYPE_BF16
 CODES = {name: code for code, name in pd.STATUS_NAMES.items()}
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_decode_\w+)\s*\(", src)))
+    """Every function any public header declares."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) >= 8
+    assert len(names) >= 11 and "rope_paged_kv_write" in names
     lib = ctypes.CDLL(pd.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -1,0 +1,213 @@
+"""GPU parity of RoPE + paged KV-cache write (rope_paged_kv_write) and of the
+cos/sin table (rope_cos_sin_table) against the fp64 oracle (oracle/rope.py).
+
+Gates: the table within one float32 ulp of the oracle's rounded table; the
+rotated q_out and cached keys within the decode path's gates (allclose
+1e-2 + 1e-2|r| and one ulp of RNE(r)) of the unrounded fp64 rotation; the
+cached values bit-exact; every cache slot the call does not name unchanged,
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import rope as orope
+import paged_gqa_decode_02_amd as pd
+import workloads
+from workloads import rope as wrope
+
+from helpers import compare, out_bits, run_library
+
+pytestmark = pytest.mark.gpu
+
+_TABLES = {}
+
+
+def gpu_table(max_position, D, base):
+    key = (max_position, D, base)
+    if key not in _TABLES:
+        _TABLES[key] = pd.rope_cos_sin_table(max_position, D, base)
+        torch.cuda.synchronize()
+    return _TABLES[key]
+
+
+def to_dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(workloads.DTYPES[dtype]).cuda()
+
+
+def run_write(case, *, packed=True, in_place=False, table=None):
+    """Upload, call, return (q_out bits, k_cache bits, v_cache bits)."""
+    qkv = to_dev(case.qkv, case.dtype)
+    if packed:
+        q, k, v = qkv[:, :case.Hq], qkv[:, case.Hq:case.Hq + case.Hkv], qkv[:, case.Hq + case.Hkv:]
+    else:
+        q, k, v = (to_dev(a, case.dtype) for a in (case.q, case.k, case.v))
+    kc, vc = (to_dev(a, case.dtype) for a in (case.k_cache, case.v_cache))
+    pos = torch.from_numpy(case.positions).cuda()
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    tab = table if table is not None else gpu_table(case.max_position, case.D, case.base)
+    qo = pd.rope_paged_kv_write(q, k, v, pos, slots, tab, kc, vc, q_out=q if in_place else None)
+    torch.cuda.synchronize()
+    return out_bits(qo), out_bits(kc), out_bits(vc)
+
+
+def check_write(case, got, table=None):
+    qo, kc, vc = got
+    tab = table if table is not None else orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    q_rot, k_rot, kc_ref, vc_ref = orope.rope_kv_write(
+        case.q, case.k, case.v, case.positions, case.slot_mapping, tab, case.k_cache,
+        case.v_cache, dtype=case.dtype)
+    rep = compare(qo, q_rot, case.dtype, what=f"{case.name} q_out")
+    live = case.slot_mapping >= 0
+    slots = case.slot_mapping[live].astype(np.int64)
+    flat = kc.reshape(-1, case.Hkv, case.D)
+    if live.any():
+        compare(flat[slots], k_rot[live], case.dtype, what=f"{case.name} k_cache")
+    assert np.array_equal(vc, vc_ref), f"{case.name}: v_cache differs"
+    # the rotated keys at the named slots aside, the K cache is what it was
+    untouched = np.ones(flat.shape[0], bool)
+    untouched[slots] = False
+    assert np.array_equal(flat[untouched], case.k_cache.reshape(-1, case.Hkv, case.D)[untouched])
+    return rep
+
+
+def test_table_matches_oracle():
+    for max_pos, D, base in ((32768, 128, 1e6), (4096, 64, 10000.0), (2048, 256, 1e6)):
+        g = gpu_table(max_pos, D, base).cpu().numpy()
+        r = orope.cos_sin_table_f32(max_pos, D, base)
+        gi, ri = g.view(np.int32).astype(np.int64), r.view(np.int32).astype(np.int64)
+        # same sign everywhere that matters; distance in float32 ulps
+        ulp = np.abs(gi - ri)
+        zero = (g == 0) & (r == 0)
+        ulp[zero] = 0
+        assert int(ulp.max()) <= 1, (max_pos, D, base, int(ulp.max()))
+        assert (ulp == 0).mean() > 0.999, (max_pos, D, base, float((ulp == 0).mean()))
+        assert np.all(g[0, : D // 2] == 1.0) and np.all(g[0, D // 2:] == 0.0)
+
+
+CASES = [
+    # T, Hq, Hkv, D, dtype, bs, pad_every
+    (1, 32, 8, 128, "bf16", 16, 0),
+    (7, 32, 8, 128, "bf16", 32, 3),
+    (64, 32, 8, 128, "f16", 16, 0),
+    (300, 32, 8, 128, "bf16", 16, 5),
+    (33, 14, 2, 64, "bf16", 16, 4),
+    (40, 8, 1, 256, "f16", 32, 0),
+    (17, 4, 4, 128, "f16", 16, 2),
+]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,dtype,bs,pad", CASES)
+@pytest.mark.parametrize("packed", [True, False])
+def test_scatter_write_matches_oracle(T, Hq, Hkv, D, dtype, bs, pad, packed):
+    case = wrope.scatter(T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, block_size=bs, pad_every=pad,
+                         max_position=32768, seed=T + D)
+    print(case.describe(), "packed" if packed else "separate", flush=True)
+    check_write(case, run_write(case, packed=packed))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_write_matches_oracle(dtype):
+    case = wrope.prefill(2, 512, dtype=dtype, block_size=16, max_position=32768, seed=11)
+    print(case.describe(), flush=True)
+    check_write(case, run_write(case))
+
+
+def test_in_place_q():
+    case = wrope.scatter(50, dtype="bf16", seed=21)
+    print(case.describe(), "in place", flush=True)
+    check_write(case, run_write(case, packed=False, in_place=True))
+
+
+def test_position_zero_leaves_q_and_k_unchanged():
+    case = wrope.scatter(16, max_position=1, seed=4)
+    assert np.all(case.positions == 0)
+    qo, kc, _ = run_write(case)
+    assert np.array_equal(qo, case.q)
+    flat = kc.reshape(-1, case.Hkv, case.D)
+    assert np.array_equal(flat[case.slot_mapping.astype(np.int64)], case.k)
+
+
+def test_large_prefill_sampled():
+    # 16,384 tokens at the decode geometry (the HBM-bound end of the range);
+    # the oracle checks every 64th token and the caches' untouched slots
+    case = wrope.prefill(4, 4096, dtype="bf16", block_size=16, max_position=32768, seed=5)
+    print(case.describe(), flush=True)
+    qo, kc, vc = run_write(case)
+    sel = np.arange(0, case.T, 64)
+    tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    sub = wrope.RopeCase(case.name + "_sample", len(sel), case.Hq, case.Hkv, case.D, case.dtype,
+                         case.block_size, case.max_position, case.base, case.qkv[sel],
+                         case.positions[sel], case.slot_mapping[sel], case.k_cache,
+                         case.v_cache, case.seed)
+    q_rot, k_rot, _, _ = orope.rope_kv_write(sub.q, sub.k, sub.v, sub.positions,
+                                             sub.slot_mapping, tab, case.k_cache, case.v_cache,
+                                             dtype="bf16")
+    compare(qo[sel], q_rot, "bf16", what="q_out sample")
+    slots = case.slot_mapping.astype(np.int64)
+    flat_k = kc.reshape(-1, case.Hkv, case.D)
+    flat_v = vc.reshape(-1, case.Hkv, case.D)
+    compare(flat_k[slots[sel]], k_rot, "bf16", what="k_cache sample")
+    assert np.array_equal(flat_v[slots], case.v)
+    untouched = np.ones(flat_k.shape[0], bool)
+    untouched[slots] = False
+    assert np.array_equal(flat_k[untouched], case.k_cache.reshape(-1, case.Hkv, case.D)[untouched])
+    assert np.array_equal(flat_v[untouched], case.v_cache.reshape(-1, case.Hkv, case.D)[untouched])
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_write_then_decode(bs):
+    """The write feeds the decode: each sequence's new token goes to position
+    L-1 through its block table, then paged decode attention reads it."""
+    dec = workloads.make_case("feed", 8, [1, 16, 17, 100, 255, 256, 513, 1000], dtype="bf16",
+                              block_size=bs, seed=7)
+    case = wrope.decode_step(dec, seed=8)
+    print(case.describe(), flush=True)
+    qo, kc, vc = run_write(case, packed=True)
+    tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    q_rot, _, kc_ref, vc_ref = orope.rope_kv_write(case.q, case.k, case.v, case.positions,
+                                                   case.slot_mapping, tab, case.k_cache,
+                                                   case.v_cache, dtype="bf16")
+    # decode over the GPU-written cache with the GPU-rotated q, against the
+    # oracle's decode over the oracle-written cache with its rotated q rounded
+    # the same way the kernel rounds it
+    q_bits = oracle.round_to_dtype(q_rot, "bf16")
+    fed = workloads.Case(dec.name, dec.B, dec.Hq, dec.Hkv, dec.D, bs, "bf16", dec.scale, qo, kc,
+                         vc, dec.block_table, dec.context_lens, dec.seed)
+    out = run_library(fed)
+    ref, _ = oracle.attention(q_bits, kc_ref, vc_ref, dec.block_table, dec.context_lens,
+                              scale=dec.scale, dtype="bf16")
+    # q_out and the cache may differ from the oracle's rounding by one ulp in
+    # a few places, so the decode output is held to the allclose gate only
+    g = oracle.widen(out_bits(out), "bf16")
+    assert np.all(np.abs(g - ref) <= 1e-2 + 1e-2 * np.abs(ref))
+
+
+def test_graph_replay_reads_positions_at_replay():
+    case = wrope.scatter(32, seed=13)
+    qkv = to_dev(case.qkv, "bf16")
+    q, k, v = qkv[:, :32], qkv[:, 32:40], qkv[:, 40:]
+    kc, vc = (to_dev(a, "bf16") for a in (case.k_cache, case.v_cache))
+    pos = torch.from_numpy(case.positions).cuda()
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    tab = gpu_table(case.max_position, case.D, case.base)
+    qo = torch.empty((32, 32, 128), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        pd.rope_paged_kv_write(q, k, v, pos, slots, tab, kc, vc, q_out=qo)  # warm up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pd.rope_paged_kv_write(q, k, v, pos, slots, tab, kc, vc, q_out=qo)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for rep in range(3):
+        new_pos = rng.integers(0, case.max_position, 32).astype(np.int32)
+        pos.copy_(torch.from_numpy(new_pos))
+        kc.copy_(to_dev(case.k_cache, "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        c2 = wrope.RopeCase(case.name, 32, 32, 8, 128, "bf16", 16, case.max_position, case.base,
+                            case.qkv, new_pos, case.slot_mapping, case.k_cache, case.v_cache, 0)
+        check_write(c2, (out_bits(qo), out_bits(kc), out_bits(vc)))
