@@ -37,6 +37,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -265,6 +267,86 @@ def bench_rope(name, torch, pd, table, iters=200, warmup=20):
     return res
 
 
+BLOCK_CASES = ("copy_4096", "gather_4096", "scatter_4096", "compact_16384")
+
+
+def bench_blocks(name, torch, pd, iters=100, warmup=10):
+    """KV-cache block movement at the decode geometry (32 KiB blocks: block
+    size 16, Hkv 8, D 128, bf16; K and V): 4,096 blocks copied, gathered or
+    scattered in a 16,384-block pool, or the compaction of such a pool with
+    half its blocks live, dealt to 64 sequences (device part: the moves and
+    the remap of their block table; the host plan is timed on its own). Two pools
+    alternate so the moved bytes do not stay in the 256 MB Infinity Cache."""
+    from workloads import blocks as wb
+    nb, n = 16384, 4096
+    pools = []
+    for r in range(2):
+        case = wb.pool(nb, seed=r) if r == 0 else None
+        kc = torch.empty((nb, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+        vc = torch.empty_like(kc)
+        if case is not None:
+            k0, v0 = case.torch_caches()
+            kc.copy_(k0)
+            vc.copy_(v0)
+        else:
+            kc.copy_(pools[0][0])
+            vc.copy_(pools[0][1])
+        pools.append((kc, vc))
+    bb = 16 * 8 * 128 * 2
+    res = {"block_bytes": bb, "pool_blocks": nb}
+    kind = name.split("_")[0]
+    if kind == "copy":
+        pairs = torch.from_numpy(wb.copy_pairs(nb, n, seed=1)).cuda()
+
+        def call(i):
+            kc, vc = pools[i % 2]
+            pd.paged_kv_copy_blocks(kc, vc, pairs)
+        nbytes = 2 * 2 * n * bb + 8 * n
+    elif kind in ("gather", "scatter"):
+        ids = torch.from_numpy(wb.block_ids(nb, n, seed=1)).cuda()
+        bufs = [(torch.empty((n, 16, 8, 128), dtype=torch.bfloat16, device="cuda"),
+                 torch.empty((n, 16, 8, 128), dtype=torch.bfloat16, device="cuda"))
+                for _ in range(2)]
+
+        def call(i):
+            kc, vc = pools[i % 2]
+            ko, vo = bufs[i % 2]
+            if kind == "gather":
+                pd.paged_kv_gather_blocks(kc, vc, ids, ko, vo)
+            else:
+                pd.paged_kv_scatter_blocks(ko, vo, ids, kc, vc)
+        nbytes = 2 * 2 * n * bb + 4 * n
+    else:
+        live, bt, _ = wb.live_pool(nb, 64, live_frac=0.5, seed=1)
+        t0 = time.perf_counter()
+        for _ in range(10):
+            pairs_h, remap_h, n_live = pd.paged_kv_compact_plan(live)
+        res["host_plan_us"] = round((time.perf_counter() - t0) / 10 * 1e6, 1)
+        pairs = pairs_h.cuda()
+        remap = remap_h.cuda()
+        table = torch.from_numpy(bt).cuda()
+        n = int(pairs.shape[0])
+        res.update({"live_blocks": n_live, "moved_blocks": n, "table_entries": table.numel()})
+
+        def call(i):
+            kc, vc = pools[i % 2]
+            pd.paged_kv_copy_blocks(kc, vc, pairs)
+            pd.paged_kv_remap_block_table(table, remap)
+        nbytes = 2 * 2 * n * bb + 8 * n + 8 * table.numel() + 4 * nb
+    call(0)
+    torch.cuda.synchronize()
+    ms = time_calls(call, iters, warmup, torch)
+    ms_g = time_graph(call, iters, torch)
+    res.update({"blocks": n, "us_per_call": round(ms * 1e3, 3),
+                "us_per_call_graph": round(ms_g * 1e3, 3),
+                "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
+                "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
+                "algorithmic_bytes": nbytes})
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls: int = 25):
     """The oracle leg: time the fp64 oracle on the first `nseq` sequences of
     the workload, repeating the call until at least `min_seconds` have
@@ -478,6 +560,7 @@ def main():
         from workloads import rope as wrope
         table = pd.rope_cos_sin_table(32768, 128, wrope.QWEN_BASE)
         res["rope_kv_write"] = {n: bench_rope(n, torch, pd, table) for n in ROPE_CASES}
+        res["kv_block_moves"] = {n: bench_blocks(n, torch, pd) for n in BLOCK_CASES}
     if baseline is not None:
         res["cpu_baseline"] = baseline
     print(json.dumps(res), flush=True)

@@ -1,15 +1,17 @@
 /*
  * paged_kv.h - C ABI of the operations around the paged KV cache that the
  * decode attention of paged_decode.h reads: the fused RoPE + cache write
- * that fills it.
+ * that fills it, and the block movement (copy, gather, scatter, compaction)
+ * a scheduler applies to it.
  *
  * Same library, status codes and dtype codes as paged_decode.h; the same
  * rules for every entry point: pointers are borrowed device memory the
- * caller keeps alive until the queued work has finished; nothing is
- * allocated, synchronised or read on the host, so calls can be captured in a
- * HIP graph (positions and slot mappings are read on the device when the
- * kernel runs); a call that fails its checks returns the code and queues
- * nothing; no C++ exception crosses the ABI.
+ * caller keeps alive until the queued work has finished (host pointers
+ * only where a function says so); nothing is allocated or synchronised and
+ * no device memory is read on the host, so calls can be captured in a HIP
+ * graph (positions, slot mappings, block ids and tables are read on the
+ * device when the kernel runs); a call that fails its checks returns the
+ * code and queues nothing; no C++ exception crosses the ABI.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H
@@ -93,6 +95,86 @@ int32_t rope_paged_kv_write(const void* q, const void* k, const void* v,
                             void* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
                             int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
                             int32_t dtype, void* stream);
+
+/*
+ * KV-cache block movement (Loom Kernels home page, "Next boundaries":
+ * KV-cache movement, block copy, gather, scatter and compact work for prefix
+ * reuse and preemption). A block is one [block_size, Hkv, D] slab of a cache,
+ * block_bytes bytes (block_size * Hkv * D * element size, any element type:
+ * blocks move as raw bytes, unchanged). Each call moves blocks of k_cache
+ * and, when v_cache is not NULL, the same blocks of v_cache; both caches
+ * are [num_blocks, ...] arrays of block_bytes-sized blocks.
+ *
+ * Common rules: caches, buffers 16-byte aligned, block_bytes a positive
+ * multiple of 16; id arrays int32 on the device, 4-byte aligned; k_cache and
+ * v_cache overlap neither each other nor the ids; n = 0 queues nothing. Device-side contract: ids in [0, num_blocks) (an item
+ * naming an id outside the pool is skipped, so nothing outside the arrays
+ * is touched). Errors: PD_ERR_SHAPE (negative counts, num_blocks < 1,
+ * block_bytes not a positive multiple of 16, too many items for one
+ * launch), PD_ERR_NULL, PD_ERR_ALIGN, PD_ERR_ALIAS, PD_ERR_HIP.
+ */
+
+/*
+ * Copy: for each i < num_pairs, block pairs[2i+1] (dst) of each cache
+ * becomes a copy of block pairs[2i] (src) (copy-on-write of a shared
+ * prefix). Sources may repeat; destinations must be distinct and no block
+ * may be both a source and a destination (else the result is unspecified).
+ * pairs must not overlap the caches.
+ */
+int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, int32_t num_blocks,
+                             int64_t block_bytes, const int32_t* pairs, int32_t num_pairs,
+                             void* stream);
+
+/*
+ * Gather: k_out[i] = k_cache[ids[i]] (and v_out[i] = v_cache[ids[i]]) for
+ * i < n, into contiguous [n, ...] buffers (blocks leaving the pool on
+ * preemption). v_out is needed exactly when v_cache is given. Outputs must
+ * not overlap the caches, the ids or each other.
+ */
+int32_t paged_kv_gather_blocks(const void* k_cache, const void* v_cache, int32_t num_blocks,
+                               int64_t block_bytes, const int32_t* ids, int32_t n, void* k_out,
+                               void* v_out, void* stream);
+
+/*
+ * Scatter: k_cache[ids[i]] = k_in[i] (and v_cache[ids[i]] = v_in[i]) for
+ * i < n (blocks coming back). ids must be distinct (else which lands is
+ * unspecified). Inputs must not overlap the caches; the caches must not
+ * overlap the ids or each other.
+ */
+int32_t paged_kv_scatter_blocks(const void* k_in, const void* v_in, const int32_t* ids,
+                                int32_t n, void* k_cache, void* v_cache, int32_t num_blocks,
+                                int64_t block_bytes, void* stream);
+
+/*
+ * Compaction plan, on the host (no device is touched): with live[b] != 0
+ * for the n_live blocks in use, every live block whose id is >= n_live is
+ * moved to a free id < n_live, the k-th such block (increasing ids) to the
+ * k-th free id (increasing), so the live blocks fill [0, n_live) with the
+ * fewest moves. Writes the moves as (src, dst) pairs, *num_pairs of them
+ * (at most min(n_live, num_blocks - n_live)); remap[b] = the new id of
+ * block b (b itself for a block that does not move); and *n_live. Sources
+ * and destinations never meet, so the pairs are a valid
+ * paged_kv_copy_blocks argument; paged_kv_remap_block_table with remap then
+ * rewrites the block tables.
+ *
+ * live: host uint8 [num_blocks]; pairs: host int32 [pairs_capacity, 2];
+ * remap: host int32 [num_blocks]. Errors: PD_ERR_SHAPE (num_blocks < 1, or
+ * more moves than pairs_capacity: nothing is written then), PD_ERR_NULL.
+ */
+int32_t paged_kv_compact_plan(const uint8_t* live, int32_t num_blocks, int32_t* pairs,
+                              int32_t pairs_capacity, int32_t* num_pairs, int32_t* remap,
+                              int32_t* n_live);
+
+/*
+ * Rewrites a block table in place on the device: each of the `entries`
+ * int32 values e with 0 <= e < num_blocks becomes remap[e] (remap: device
+ * int32 [num_blocks]); any other value (padding such as -1) stays. The
+ * table must not overlap remap. Errors: PD_ERR_SHAPE (entries < 0 or
+ * >= 2^31, num_blocks < 1), PD_ERR_NULL, PD_ERR_ALIGN, PD_ERR_ALIAS,
+ * PD_ERR_HIP.
+ */
+int32_t paged_kv_remap_block_table(int32_t* block_table, int64_t entries, const int32_t* remap,
+                                   int32_t num_blocks, void* stream);
 
 #ifdef __cplusplus
 }

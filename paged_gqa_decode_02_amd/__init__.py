@@ -296,3 +296,131 @@ def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_ca
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return q_out
+
+
+lib.paged_kv_copy_blocks.argtypes = [_P, _P, _I, _L, _P, _I, _P]
+lib.paged_kv_copy_blocks.restype = _I
+lib.paged_kv_gather_blocks.argtypes = [_P, _P, _I, _L, _P, _I, _P, _P, _P]
+lib.paged_kv_gather_blocks.restype = _I
+lib.paged_kv_scatter_blocks.argtypes = [_P, _P, _P, _I, _P, _P, _I, _L, _P]
+lib.paged_kv_scatter_blocks.restype = _I
+lib.paged_kv_compact_plan.argtypes = [_P, _I, _P, _I, _PI, _P, _PI]
+lib.paged_kv_compact_plan.restype = _I
+lib.paged_kv_remap_block_table.argtypes = [_P, _L, _P, _I, _P]
+lib.paged_kv_remap_block_table.restype = _I
+
+
+def _pool(k_cache, v_cache):
+    """(num_blocks, block_bytes, v pointer) of a cache pair; v_cache may be None."""
+    if not k_cache.is_contiguous() or k_cache.dim() < 1:
+        raise ValueError("k_cache must be a contiguous [num_blocks, ...] tensor")
+    if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype
+                                or not v_cache.is_contiguous()):
+        raise ValueError("v_cache must match k_cache (shape, dtype, contiguous)")
+    nb = int(k_cache.shape[0])
+    bb = (k_cache.numel() // max(nb, 1)) * k_cache.element_size()
+    return nb, bb, (v_cache.data_ptr() if v_cache is not None else None)
+
+
+def _ids(t, name, n=None):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, pairs, *, stream=None):
+    """Block pairs[i, 1] of each cache becomes a copy of block pairs[i, 0]
+    (``paged_kv_copy_blocks``); pairs: device int32 [n, 2]. In place."""
+    nb, bb, vp = _pool(k_cache, v_cache)
+    _ids(pairs, "pairs")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    rc = lib.paged_kv_copy_blocks(k_cache.data_ptr(), vp, nb, bb, pairs.data_ptr(),
+                                  int(pairs.shape[0]), _handle(stream, k_cache.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+
+
+def paged_kv_gather_blocks(k_cache, v_cache, ids, k_out=None, v_out=None, *, stream=None):
+    """k_out[i] = k_cache[ids[i]] (and the same for V) into [n, ...] buffers
+    (``paged_kv_gather_blocks``); returns (k_out, v_out)."""
+    nb, bb, vp = _pool(k_cache, v_cache)
+    _ids(ids, "ids")
+    n = int(ids.numel())
+    shape = (n,) + tuple(k_cache.shape[1:])
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    if v_cache is not None and v_out is None:
+        v_out = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    for t in (k_out, v_out):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != k_cache.dtype
+                              or not t.is_contiguous()):
+            raise ValueError("outputs must be contiguous [n, ...] tensors of the cache dtype")
+    rc = lib.paged_kv_gather_blocks(k_cache.data_ptr(), vp, nb, bb, ids.data_ptr(), n,
+                                    k_out.data_ptr(),
+                                    v_out.data_ptr() if v_out is not None else None,
+                                    _handle(stream, k_cache.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return k_out, v_out
+
+
+def paged_kv_scatter_blocks(k_in, v_in, ids, k_cache, v_cache, *, stream=None):
+    """k_cache[ids[i]] = k_in[i] (and the same for V)
+    (``paged_kv_scatter_blocks``). In place on the caches."""
+    nb, bb, vp = _pool(k_cache, v_cache)
+    _ids(ids, "ids")
+    n = int(ids.numel())
+    shape = (n,) + tuple(k_cache.shape[1:])
+    for t in (k_in, v_in):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != k_cache.dtype
+                              or not t.is_contiguous()):
+            raise ValueError("inputs must be contiguous [n, ...] tensors of the cache dtype")
+    rc = lib.paged_kv_scatter_blocks(k_in.data_ptr(), v_in.data_ptr() if v_in is not None else None,
+                                     ids.data_ptr(), n, k_cache.data_ptr(), vp, nb, bb,
+                                     _handle(stream, k_cache.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+
+
+def paged_kv_compact_plan(live):
+    """Host compaction plan (``paged_kv_compact_plan``) of a live mask (any
+    CPU array-like of num_blocks truthy values): returns (pairs int32 [m, 2],
+    remap int32 [num_blocks], n_live) as CPU tensors / int."""
+    live_t = torch.as_tensor(live).to(torch.uint8).contiguous().cpu()
+    nb = int(live_t.numel())
+    cap = nb // 2 + 1
+    pairs = torch.empty((cap, 2), dtype=torch.int32)
+    remap = torch.empty(nb, dtype=torch.int32)
+    m, n = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib.paged_kv_compact_plan(live_t.data_ptr(), nb, pairs.data_ptr(), cap, ctypes.byref(m),
+                                   remap.data_ptr(), ctypes.byref(n))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return pairs[: m.value].clone(), remap, n.value
+
+
+def paged_kv_remap_block_table(block_table, remap, *, stream=None):
+    """In place: every entry e of the device int32 block table with
+    0 <= e < len(remap) becomes remap[e] (``paged_kv_remap_block_table``)."""
+    _ids(block_table, "block_table")
+    _ids(remap, "remap")
+    rc = lib.paged_kv_remap_block_table(block_table.data_ptr(), int(block_table.numel()),
+                                        remap.data_ptr(), int(remap.numel()),
+                                        _handle(stream, block_table.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+
+
+def paged_kv_compact(k_cache, v_cache, live, block_tables, *, stream=None):
+    """Compaction in one call: plan on the host from the live mask, copy the
+    moved blocks and remap every given device block table in place. Returns
+    (n_live, number of moved blocks, remap on the device)."""
+    pairs, remap, n = paged_kv_compact_plan(live)
+    dev = k_cache.device
+    remap_d = remap.to(dev)
+    if pairs.shape[0] > 0:
+        paged_kv_copy_blocks(k_cache, v_cache, pairs.to(dev), stream=stream)
+    for bt in block_tables:
+        paged_kv_remap_block_table(bt, remap_d, stream=stream)
+    return n, int(pairs.shape[0]), remap_d

@@ -4,10 +4,11 @@
 
 (run as a file: importing the package would load the library it rebuilds)
 
-Compiles the kernels (``csrc/pd_kernels.hip``, ``csrc/pd_rope.hip``) and the
-host side (``csrc/pd_api.cpp``, ``csrc/pd_kv_api.cpp``, ``csrc/pd_plan.cpp``)
-with hipcc into one shared library exporting the C ABI of
-``include/paged_decode.h`` and ``include/paged_kv.h``. Packed fp32 VALU
+Compiles the kernels (``csrc/pd_kernels.hip``, ``csrc/pd_rope.hip``,
+``csrc/pd_blocks.hip``) and the host side (``csrc/pd_api.cpp``,
+``csrc/pd_kv_api.cpp``, ``csrc/pd_plan.cpp``) with hipcc into one shared
+library exporting the C ABI of ``include/paged_decode.h`` and
+``include/paged_kv.h``. Packed fp32 VALU
 instructions are disabled for the device code.
 """
 from __future__ import annotations
@@ -24,7 +25,7 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libpaged_decode.so")
 ARCH = "gfx950"
 
-SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_api.cpp", "pd_kv_api.cpp", "pd_plan.cpp"]
+SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_blocks.hip", "pd_api.cpp", "pd_kv_api.cpp", "pd_plan.cpp"]
 HEADERS = ["pd_internal.h"]
 
 

@@ -97,4 +97,23 @@ int32_t launch_rope_kv_write(const RopeLaunch& l);
 int32_t launch_rope_table(float* table, int32_t max_position, int32_t D, double base,
                           void* stream);
 
+// Block movement (pd_blocks.hip); validated by the caller. mode: 0 copy
+// (ids = pairs [n, 2]), 1 gather (ids [n], pool -> buffer), 2 scatter
+// (ids [n], buffer -> pool); caches: 1 (K only) or 2 (K and V).
+struct MoveLaunch {
+  int32_t mode;
+  const void* src[2];
+  void* dst[2];
+  int32_t caches;
+  const int32_t* ids;
+  int64_t block_bytes;
+  int32_t n;
+  int32_t num_blocks;
+  void* stream;
+};
+int32_t launch_move_blocks(const MoveLaunch& l);
+int64_t move_chunk_bytes();  // bytes one workgroup moves
+int32_t launch_remap_table(int32_t* table, int64_t entries, const int32_t* remap,
+                           int32_t num_blocks, void* stream);
+
 }  // namespace pd

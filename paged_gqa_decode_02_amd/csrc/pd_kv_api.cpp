@@ -1,5 +1,5 @@
-// C ABI of the KV-cache operations (include/paged_kv.h): argument checks and
-// launch. As in pd_api.cpp, every check uses host-visible values only and
+// C ABI of the KV-cache operations (include/paged_kv.h): argument checks,
+// the host compaction planner, and launch. As in pd_api.cpp, every check uses host-visible values only and
 // every export contains all failures.
 #include <math.h>
 #include <stdint.h>
@@ -78,6 +78,37 @@ int32_t rope_write_impl(const pd::RopeLaunch& l) {
   return pd::launch_rope_kv_write(l);
 }
 
+// Checks shared by the three block moves; on success fills the launch.
+int32_t move_impl(pd::MoveLaunch& l, const void* k_cache, const void* v_cache, const void* k_buf,
+                  const void* v_buf, bool buf_is_output) {
+  if (l.n < 0 || l.num_blocks < 1 || l.block_bytes < 16 || l.block_bytes % 16) return PD_ERR_SHAPE;
+  const int64_t chunks = (l.block_bytes + pd::move_chunk_bytes() - 1) / pd::move_chunk_bytes();
+  if ((int64_t)l.n * chunks >= ((int64_t)1 << 24)) return PD_ERR_SHAPE;
+  if (l.n == 0) return PD_OK;
+  const bool copy = l.mode == 0;
+  if (!k_cache || !l.ids || (!copy && !k_buf) || (!copy && (v_cache != nullptr) != (v_buf != nullptr)))
+    return PD_ERR_NULL;
+  if (!aligned(k_cache, 16) || (v_cache && !aligned(v_cache, 16)) ||
+      (k_buf && !aligned(k_buf, 16)) || (v_buf && !aligned(v_buf, 16)) || !aligned(l.ids, 4))
+    return PD_ERR_ALIGN;
+  const size_t pool = (size_t)l.num_blocks * (size_t)l.block_bytes;
+  const size_t buf = (size_t)l.n * (size_t)l.block_bytes;
+  const size_t ids = (size_t)l.n * (copy ? 8 : 4);
+  if (overlap(k_cache, pool, v_cache, pool) || overlap(k_cache, pool, l.ids, ids) ||
+      overlap(v_cache, pool, l.ids, ids))
+    return PD_ERR_ALIAS;
+  if (!copy) {
+    const void* bufs[2] = {k_buf, v_buf};
+    for (const void* b : bufs) {
+      if (overlap(b, buf, k_cache, pool) || overlap(b, buf, v_cache, pool)) return PD_ERR_ALIAS;
+      if (buf_is_output && overlap(b, buf, l.ids, ids)) return PD_ERR_ALIAS;
+    }
+    if (overlap(k_buf, buf, v_buf, buf)) return PD_ERR_ALIAS;
+  }
+  l.caches = v_cache ? 2 : 1;
+  return pd::launch_move_blocks(l);
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +140,89 @@ int32_t rope_paged_kv_write(const void* q, const void* k, const void* v, int64_t
                      v_cache,  num_blocks, T,        Hq,           Hkv,          D,
                      block_size, dtype,   stream};
     return rope_write_impl(l);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_kv_copy_blocks(void* k_cache, void* v_cache, int32_t num_blocks,
+                             int64_t block_bytes, const int32_t* pairs, int32_t num_pairs,
+                             void* stream) {
+  try {
+    pd::MoveLaunch l{0, {k_cache, v_cache}, {k_cache, v_cache}, 0, pairs, block_bytes,
+                     num_pairs, num_blocks, stream};
+    return move_impl(l, k_cache, v_cache, nullptr, nullptr, false);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_kv_gather_blocks(const void* k_cache, const void* v_cache, int32_t num_blocks,
+                               int64_t block_bytes, const int32_t* ids, int32_t n, void* k_out,
+                               void* v_out, void* stream) {
+  try {
+    pd::MoveLaunch l{1, {k_cache, v_cache}, {k_out, v_out}, 0, ids, block_bytes, n, num_blocks,
+                     stream};
+    return move_impl(l, k_cache, v_cache, k_out, v_out, true);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_kv_scatter_blocks(const void* k_in, const void* v_in, const int32_t* ids,
+                                int32_t n, void* k_cache, void* v_cache, int32_t num_blocks,
+                                int64_t block_bytes, void* stream) {
+  try {
+    pd::MoveLaunch l{2, {k_in, v_in}, {k_cache, v_cache}, 0, ids, block_bytes, n, num_blocks,
+                     stream};
+    return move_impl(l, k_cache, v_cache, k_in, v_in, false);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_kv_compact_plan(const uint8_t* live, int32_t num_blocks, int32_t* pairs,
+                              int32_t pairs_capacity, int32_t* num_pairs, int32_t* remap,
+                              int32_t* n_live) {
+  try {
+    if (num_blocks < 1 || pairs_capacity < 0) return PD_ERR_SHAPE;
+    if (!live || !num_pairs || !remap || !n_live || (pairs_capacity > 0 && !pairs))
+      return PD_ERR_NULL;
+    int32_t n = 0;
+    for (int32_t b = 0; b < num_blocks; ++b) n += live[b] != 0;
+    int32_t moves = 0;
+    for (int32_t b = n; b < num_blocks; ++b) moves += live[b] != 0;
+    if (moves > pairs_capacity) return PD_ERR_SHAPE;
+    // two cursors: the next free id below n, the next live id at or above n
+    int32_t hole = 0, k = 0;
+    for (int32_t b = 0; b < num_blocks; ++b) remap[b] = b;
+    for (int32_t src = n; src < num_blocks; ++src) {
+      if (!live[src]) continue;
+      while (live[hole]) ++hole;  // a free id below n exists for every mover
+      pairs[2 * k] = src;
+      pairs[2 * k + 1] = hole;
+      remap[src] = hole;
+      ++k;
+      ++hole;
+    }
+    *num_pairs = moves;
+    *n_live = n;
+    return PD_OK;
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t paged_kv_remap_block_table(int32_t* block_table, int64_t entries, const int32_t* remap,
+                                   int32_t num_blocks, void* stream) {
+  try {
+    if (entries < 0 || entries >= ((int64_t)1 << 31) || num_blocks < 1) return PD_ERR_SHAPE;
+    if (entries == 0) return PD_OK;
+    if (!block_table || !remap) return PD_ERR_NULL;
+    if (!aligned(block_table, 4) || !aligned(remap, 4)) return PD_ERR_ALIGN;
+    if (overlap(block_table, (size_t)entries * 4, remap, (size_t)num_blocks * 4))
+      return PD_ERR_ALIAS;
+    return pd::launch_remap_table(block_table, entries, remap, num_blocks, stream);
   } catch (...) {
     return PD_ERR_INTERNAL;
   }

@@ -102,3 +102,106 @@ def test_rope_table_argument_errors(over, code):
     a = dict(table=GB, maxpos=4096, dim=128, base=1e6)
     a.update(over)
     assert pd.lib.rope_cos_sin_table(a["table"], a["maxpos"], a["dim"], a["base"], 0) == CODES[code]
+
+
+# ---------------------------------------------------------------------------
+# block movement
+
+import numpy as np
+from oracle import blocks as ob
+
+
+def move_call(fn, **over):
+    a = dict(kc=1 * GB, vc=2 * GB, nb=1024, bb=32768, ids=3 * GB, n=16, ko=4 * GB, vo=5 * GB)
+    a.update(over)
+    if fn == "copy":
+        return pd.lib.paged_kv_copy_blocks(a["kc"], a["vc"], a["nb"], a["bb"], a["ids"], a["n"], 0)
+    if fn == "gather":
+        return pd.lib.paged_kv_gather_blocks(a["kc"], a["vc"], a["nb"], a["bb"], a["ids"], a["n"],
+                                             a["ko"], a["vo"], 0)
+    return pd.lib.paged_kv_scatter_blocks(a["ko"], a["vo"], a["ids"], a["n"], a["kc"], a["vc"],
+                                          a["nb"], a["bb"], 0)
+
+
+MOVE_ERRORS = [
+    (dict(n=-1), "PD_ERR_SHAPE"),
+    (dict(nb=0), "PD_ERR_SHAPE"),
+    (dict(bb=0), "PD_ERR_SHAPE"),
+    (dict(bb=40), "PD_ERR_SHAPE"),
+    (dict(n=1 << 23, bb=1 << 20), "PD_ERR_SHAPE"),
+    (dict(kc=0), "PD_ERR_NULL"),
+    (dict(ids=0), "PD_ERR_NULL"),
+    (dict(kc=GB + 8), "PD_ERR_ALIGN"),
+    (dict(vc=2 * GB + 4), "PD_ERR_ALIGN"),
+    (dict(ids=3 * GB + 2), "PD_ERR_ALIGN"),
+    (dict(vc=GB + 32768 * 10), "PD_ERR_ALIAS"),     # v_cache inside k_cache
+    (dict(ids=GB + 64), "PD_ERR_ALIAS"),            # ids inside k_cache
+]
+
+
+@pytest.mark.parametrize("fn", ["copy", "gather", "scatter"])
+@pytest.mark.parametrize("over,code", MOVE_ERRORS)
+def test_block_move_argument_errors(fn, over, code):
+    assert move_call(fn, **over) == CODES[code]
+
+
+@pytest.mark.parametrize("fn", ["gather", "scatter"])
+def test_block_move_buffer_errors(fn):
+    assert move_call(fn, ko=0) == CODES["PD_ERR_NULL"]
+    assert move_call(fn, vo=0) == CODES["PD_ERR_NULL"]          # v cache without a v buffer
+    assert move_call(fn, vc=0, vo=5 * GB) == CODES["PD_ERR_NULL"]  # v buffer without a v cache
+    assert move_call(fn, ko=4 * GB + 8) == CODES["PD_ERR_ALIGN"]
+    assert move_call(fn, ko=GB + 32768) == CODES["PD_ERR_ALIAS"]   # buffer inside the pool
+    assert move_call(fn, vo=4 * GB + 16384) == CODES["PD_ERR_ALIAS"]  # buffers overlap
+
+
+def test_gather_output_must_not_overlap_ids():
+    assert move_call("gather", ids=4 * GB + 64) == CODES["PD_ERR_ALIAS"]
+
+
+def test_block_moves_of_nothing_are_no_ops():
+    for fn in ("copy", "gather", "scatter"):
+        assert move_call(fn, n=0, kc=0, vc=0, ids=0, ko=0, vo=0) == 0
+
+
+def test_remap_argument_errors():
+    f = pd.lib.paged_kv_remap_block_table
+    assert f(GB, -1, 2 * GB, 16, 0) == CODES["PD_ERR_SHAPE"]
+    assert f(GB, 1 << 31, 2 * GB, 16, 0) == CODES["PD_ERR_SHAPE"]
+    assert f(GB, 10, 2 * GB, 0, 0) == CODES["PD_ERR_SHAPE"]
+    assert f(0, 10, 2 * GB, 16, 0) == CODES["PD_ERR_NULL"]
+    assert f(GB, 10, 0, 16, 0) == CODES["PD_ERR_NULL"]
+    assert f(GB + 2, 10, 2 * GB, 16, 0) == CODES["PD_ERR_ALIGN"]
+    assert f(GB, 10, GB + 8, 16, 0) == CODES["PD_ERR_ALIAS"]
+    assert f(0, 0, 0, 16, 0) == 0
+
+
+@pytest.mark.parametrize("nb,frac,seed", [(1, 1.0, 0), (1, 0.0, 0), (2, 0.5, 1), (7, 0.5, 2),
+                                          (100, 0.3, 3), (100, 0.9, 4), (4096, 0.5, 5),
+                                          (5000, 0.02, 6), (64, 1.0, 7), (64, 0.0, 8)])
+def test_compact_plan_matches_oracle(nb, frac, seed):
+    rng = np.random.default_rng(seed)
+    live = (rng.random(nb) < frac).astype(np.uint8)
+    pairs, remap, n = pd.paged_kv_compact_plan(live)
+    p2, r2, n2 = ob.compact_plan(live.astype(bool))
+    assert n == n2
+    assert np.array_equal(pairs.numpy(), p2.astype(np.int32).reshape(-1, 2))
+    assert np.array_equal(remap.numpy(), r2.astype(np.int32))
+
+
+def test_compact_plan_errors():
+    import ctypes
+    live = (ctypes.c_uint8 * 8)(0, 0, 0, 0, 1, 1, 1, 1)
+    pairs = (ctypes.c_int32 * 16)()
+    remap = (ctypes.c_int32 * 8)()
+    m, n = ctypes.c_int32(-5), ctypes.c_int32(-5)
+    f = pd.lib.paged_kv_compact_plan
+    # 4 moves needed: capacity 3 is refused and nothing is written
+    assert f(live, 8, pairs, 3, ctypes.byref(m), remap, ctypes.byref(n)) == CODES["PD_ERR_SHAPE"]
+    assert m.value == -5 and n.value == -5
+    assert f(live, 8, pairs, 4, ctypes.byref(m), remap, ctypes.byref(n)) == 0
+    assert (m.value, n.value) == (4, 4)
+    assert f(live, 0, pairs, 4, ctypes.byref(m), remap, ctypes.byref(n)) == CODES["PD_ERR_SHAPE"]
+    assert f(None, 8, pairs, 4, ctypes.byref(m), remap, ctypes.byref(n)) == CODES["PD_ERR_NULL"]
+    assert f(live, 8, pairs, 4, None, remap, ctypes.byref(n)) == CODES["PD_ERR_NULL"]
+    assert f(live, 8, pairs, 4, ctypes.byref(m), None, ctypes.byref(n)) == CODES["PD_ERR_NULL"]
