@@ -359,6 +359,26 @@ def test_matches_a_dense_numpy_formulation(dtype):
             assert abs(lse[b, h] - (s.max() + np.log(w.sum()))) <= 1e-12
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 64), (32, 1, 64), (8, 8, 16), (20, 1, 32),
+                                     (6, 2, 128), (32, 1, 128)])
+def test_matches_the_dense_formulation_at_other_geometries(Hq, Hkv, D):
+    # odd group sizes (G = 7, 20, 3), MQA (G = 32), MHA (G = 1), D = 16..128:
+    # query head h reads KV head h // G
+    G = Hq // Hkv
+    c, dt = small_case(B=3, Hq=Hq, Hkv=Hkv, D=D, bs=8, ctx=(1, 9, 23), dtype="bf16", seed=G + D)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, lse = run(c, dt, scale=scale)
+    q = vals(c["q"], dt)
+    for b in range(3):
+        for h in range(Hq):
+            K, V = gather(c, dt, b, h // G)
+            s_ = scale * (K @ q[b, h])
+            w = np.exp(s_ - s_.max())
+            ref = (w[:, None] * V).sum(0) / w.sum()
+            assert np.max(np.abs(out[b, h] - ref)) <= 1e-12
+            assert abs(lse[b, h] - (s_.max() + np.log(w.sum()))) <= 1e-12
+
+
 # --------------------------------------------------------------------------
 # regression fixture for the tiny workload (written by tests/golden/make_golden.py,
 # which calls only oracle/ and workloads/)
