@@ -7,9 +7,9 @@
 
 namespace pd {
 
-// Head dimension and query heads per KV head the kernels are built for.
-constexpr int kHeadDim = 128;
-constexpr int kGroup = 4;
+// Geometries the decode kernels are built for: head dim 64 or 128 (FP8
+// caches: 128), and up to kMaxGroup query heads per KV head.
+constexpr int kMaxGroup = 32;
 
 struct Shape {
   int32_t B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype;
@@ -30,8 +30,8 @@ struct Plan {
 // Most blocks one wave's slice may span (four block ids per lane).
 constexpr int kMaxWaveBlocks = 256;
 // Most waves in a workgroup: each wave holds two 16-token K/V tiles in LDS
-// (17.5 KiB; an FP8 cache: two staging tiles and one converted tile, 16.75
-// KiB), so 8 waves fill at most 140 KiB of a CU's 160 KiB.
+// (17.5 KiB at D = 128; an FP8 cache: two staging tiles and one converted
+// tile, 16.75 KiB), so 8 waves fill at most 140 KiB of a CU's 160 KiB.
 constexpr int kMaxWaves = 8;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.

@@ -2,40 +2,44 @@
 //
 // Method (Loom Kernels home page, "Supported now": paged MQA/GQA decode with
 // GQA packing and local split-K/LSE): one query token per head attends over
-// a paged K/V cache; the 4 query heads that share a KV head are served by one
-// pass over that head's K/V bytes, and a long context is cut into
-// partitions whose normalised partial outputs and log-sum-exps are merged.
+// a paged K/V cache; the G = Hq / Hkv query heads that share a KV head are
+// served by one pass over that head's K/V bytes, and a long context is cut
+// into partitions whose normalised partial outputs and log-sum-exps are
+// merged. Built for head dims D = 64 and 128 and any G up to 32 (MQA at
+// 32/1 included): G <= 16 query heads fill one 16-column MFMA block, G <= 32
+// two (NC), the extra columns repeating heads.
 //
 // One kernel. Workgroup (partition p, KV-head group hg, sequence b) has
 // NH x NT wave64s: wave w serves KV head hg*NH + w%NH over token slice w/NH
 // of the partition (a block-aligned range of at most 256 blocks). Waves of
 // the same slice read the same physical blocks, so a workgroup sweeps whole
-// blocks (all heads of a token are one contiguous 2 KiB row group) rather
-// than 256-byte slivers of them.
+// blocks (all heads of a token are one contiguous row group) rather than
+// slivers of them.
 //   * K/V move in tiles of 16 tokens from HBM straight into LDS with
 //     bounds-checked buffer loads whose resource is the current physical
 //     block (base = pool + id * block bytes, size = block bytes), so an
 //     access cannot leave the block; lanes past the context get an offset
 //     beyond the block and read nothing. Each 128-bit load instruction of a
-//     wave reads four whole 256-byte rows. One or two tiles stay in flight
-//     while the oldest is computed; the loads use the streaming (nt) cache
-//     policy since every K/V byte is read once.
+//     wave reads 1 KiB: four whole 256-byte rows (D = 128) or eight 128-byte
+//     rows (D = 64). One or two tiles stay in flight while the oldest is
+//     computed; the loads use the streaming (nt) cache policy since every
+//     K/V byte is read once.
 //   * block ids: each lane loads up to four block-table entries of the
 //     wave's range before the context length is known; a tile takes its
 //     (wave-uniform) id with v_readlane, so addresses are scalar.
-//   * scores: q . k for the 16 tokens of a tile and the 4 query heads of the
-//     KV head are one 16x16 output of four v_mfma_f32_16x16x32 (bf16 or
-//     f16 inputs, exact products, fp32 sums), read from LDS in the operand
-//     order; one multiply by scale*log2(e) puts the softmax in base 2
+//   * scores: q . k for the 16 tokens of a tile and 16 query-head columns
+//     are one 16x16 output of D/32 v_mfma_f32_16x16x32 (bf16 or f16 inputs,
+//     exact products, fp32 sums) per column block, read from LDS in the
+//     operand order; one multiply by scale*log2(e) puts the softmax in base 2
 //     (v_exp_f32).
-//   * softmax: per head, a running maximum that only moves when a ballot
-//     finds a tile maximum above it (then the accumulators are rescaled);
-//     each lane keeps its own partial sum of weights.
-//   * PV: fp32 FMA of each weight with the 16-bit V values widened exactly,
-//     acc[4 heads][8 dims] per lane.
-//   * end of slice: a reduce-scatter over the 4 rows (permlane32_swap, then
-//     permlane16_swap) leaves query head r's 128 sums in row r; the NT slices
-//     of a head are merged through LDS.
+//   * softmax: per head column, a running maximum that only moves when a
+//     ballot finds a tile maximum above it (then the accumulators are
+//     rescaled); each lane keeps its own partial sum of weights.
+//   * PV: per 16-dim block, a 16x16x32 MFMA of V^T (read from LDS with the
+//     transposing ds_read_b64_tr_b16) and the weights split into 16-bit
+//     terms, accumulating in fp32.
+//   * end of slice: each head's D sums sit in the 4 lanes of its column;
+//     the NT slices of a head are merged through LDS.
 //   * S == 1: the workgroup writes `out`, rounded to the dtype.
 //   * S > 1: the workgroup writes its fp32 partial output and log2-sum-exp
 //     with write-through (device-coherent) stores, then bumps a per
@@ -59,11 +63,9 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int D = pd::kHeadDim;  // 128
-constexpr int G = pd::kGroup;    // 4
 constexpr int kIdRegs = pd::kMaxWaveBlocks / 64;  // block ids per lane
-constexpr uint32_t kRowBytes = D * 2;          // one token row of one KV head (16-bit)
-constexpr uint32_t kRowBytes8 = D;             // the same row of an FP8 cache
+constexpr int kD8 = 128;                       // the head dim of the FP8 cache path
+constexpr uint32_t kRowBytes8 = kD8;           // one token row of one KV head, FP8
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 data format
 constexpr int kStream = 2;                     // cache policy "nt": read once
@@ -80,6 +82,7 @@ struct KArgs {
   float* lse_part;    // [B, Hq, S], log2 domain
   int32_t* counters;  // [B, Hkv / NH], at the start of the workspace
   int32_t Hkv;
+  int32_t G;   // query heads per KV head
   int32_t MB;
   int32_t S;
   int32_t P;
@@ -164,27 +167,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Tiles of 16 tokens of one KV head go from HBM straight into LDS (buffer
-// loads with the LDS destination, no VGPRs held while in flight). Within a
-// tile, load instruction n moves tokens 4n..4n+3: lane (row, sl) reads 16
-// bytes of token 4n + row, so every 16 lanes read one whole 256-byte row.
-// Which 16-byte chunk a lane takes is rotated per row, and the four 1 KiB
-// groups of a tile are padded apart, so that the LDS reads below touch
-// distinct bank groups:
-//   K: lane sl takes chunk (sl - row) mod 16, groups 1088 bytes apart; read
+// loads with the LDS destination, no VGPRs held while in flight). A token row
+// of one KV head is C = D/8 16-byte chunks; one load instruction moves R =
+// 64 / C rows (4 at D = 128, 8 at D = 64), lane (r, sl) = (lane / C, lane %
+// C) reading 16 bytes of row r, so every C lanes read one whole row, and
+// lands them as one 1 KiB group in LDS. Which chunk a lane takes is rotated
+// per row, and the 16/R groups of a tile are padded apart, so that the LDS
+// reads below spread over the banks:
+//   K: lane sl takes chunk (sl - r) mod C, groups 1088 bytes apart; read
 //      back 16 bytes per lane in MFMA operand order (token lane%16, chunk
-//      4s + lane/16): any 16 (and any 8 consecutive) lanes hit distinct
-//      16-byte bank groups;
-//   V: lane sl takes chunk (sl - 2 row) mod 16, groups 1152 bytes apart;
-//      read back with the transposing ds_read_b64_tr_b16, 8 bytes per lane
-//      (token 4(lane/16) + (lane%16)/4, dims 4(lane%4) of a 16-dim block):
-//      each 32 lanes hit distinct 8-byte bank slots.
+//      4s + lane/16);
+//   V: lane sl takes chunk (sl - 2r) mod C, groups 1152 bytes apart; read
+//      back with the transposing ds_read_b64_tr_b16, 8 bytes per lane
+//      (token 4(lane/16) + (lane%16)/4, dims 4(lane%4) of a 16-dim block).
+// At D = 128 any 16 lanes of the K read, and each 32 lanes of the V read,
+// hit distinct 16-byte (8-byte) bank slots.
 constexpr int kTileTok = 16;
-constexpr uint32_t kKGroup = 4 * kRowBytes + 64;
-constexpr uint32_t kVGroup = 4 * kRowBytes + 128;
-constexpr uint32_t kKTile = 4 * kKGroup;             // 4352
-constexpr uint32_t kLdsTile = kKTile + 4 * kVGroup;  // K then V: 8960
-// An FP8 cache lands in a plain staging tile (16 rows of 128 bytes for K,
-// then for V) and is converted into the 16-bit layout above before use.
+template <int D>
+struct Geo {
+  static constexpr int kChunks = D / 8;                     // C
+  static constexpr uint32_t kRowBytes = 2 * D;              // one 16-bit row of one KV head
+  static constexpr int kRowsPerLoad = 64 / kChunks;         // R
+  static constexpr int kGroups = kTileTok / kRowsPerLoad;   // load instructions per tile and tensor
+  static constexpr uint32_t kKGroup = 1024 + 64;
+  static constexpr uint32_t kVGroup = 1024 + 128;
+  static constexpr uint32_t kKTile = kGroups * kKGroup;
+  static constexpr uint32_t kLdsTile = kKTile + kGroups * kVGroup;  // K then V
+  static constexpr int kSteps = D / 32;   // score MFMAs per column block
+  static constexpr int kBlocks = D / 16;  // 16-dim output blocks (PV MFMAs)
+};
+static_assert(Geo<128>::kLdsTile == 8960 && Geo<64>::kLdsTile == 4480, "tile layout");
+// An FP8 cache (D = 128) lands in a plain staging tile (16 rows of 128 bytes
+// for K, then for V) and is converted into the 16-bit layout above before
+// use.
 constexpr uint32_t kStage8 = 2 * kTileTok * kRowBytes8;  // 4096
 
 // Tile buffers per wave (tiles in flight while one is computed: buffers - 1),
@@ -193,11 +208,12 @@ constexpr uint32_t kStage8 = 2 * kTileTok * kRowBytes8;  // 4096
 #define PD_NBUF 2
 #endif
 constexpr uint32_t kLdsBytes = 160 * 1024;
-template <bool KV8>
-constexpr uint32_t stage_bytes() { return KV8 ? kStage8 : kLdsTile; }
-template <bool KV8>
+template <int D, bool KV8>
+constexpr uint32_t stage_bytes() { return KV8 ? kStage8 : Geo<D>::kLdsTile; }
+template <int D, bool KV8>
 constexpr int tile_buffers(int nw) {
-  return PD_NBUF >= 3 && 3 * nw * stage_bytes<KV8>() + (KV8 ? nw * kLdsTile : 0) <= kLdsBytes
+  return PD_NBUF >= 3 &&
+                 3 * nw * stage_bytes<D, KV8>() + (KV8 ? nw * Geo<kD8>::kLdsTile : 0) <= kLdsBytes
              ? 3 : 2;
 }
 
@@ -253,81 +269,91 @@ struct WeightBias {
   static constexpr float log2 = BF16 ? 0.f : 8.f;
 };
 
-// Per-lane state of one wave's online softmax over its token slice. Lane l
-// follows query head l%4 of the KV head; acc[m][i] is its unnormalised PV
-// sum for dim 16m + 4(l/16) + i (the four lane quads of a row hold copies).
+// Per-lane state of one wave's online softmax over its token slice, per
+// column block j < NC. Lane l follows head column 16j + l%16 (query head
+// (16j + l%16) % G of the KV head); acc[j][m][i] is its unnormalised PV sum
+// for dim 16m + 4(l/16) + i.
+template <int D, int NC>
 struct WaveState {
-  f32x4 acc[8];
-  float lsum;  // sum of weights over the tokens of this lane's row
-  float m;     // running maximum (log2 domain)
+  f32x4 acc[NC][Geo<D>::kBlocks];
+  float lsum[NC];  // sum of weights over the tokens of this lane's row
+  float m[NC];     // running maximum (log2 domain)
 };
 
 // One 16-token tile, already in LDS at kt (K) and kt + kKTile (V).
-//   scores: the K tile is the A operand of four 16x16x32 MFMAs (row = token
-//     lane%16, k = dims 32s + 8(lane/16) .. +8), q the B operand (column =
-//     lane%16 -> query head (lane%16)%4, the 4 heads repeated 4 times): lane
-//     l gets the scores of tokens 4(l/16) + i, i < 4, for head l%4;
-//   softmax: the tile maximum per head (4 registers, then the 4 rows); the
+//   scores: the K tile is the A operand of D/32 16x16x32 MFMAs per column
+//     block (row = token lane%16, k = dims 32s + 8(lane/16) .. +8), q the B
+//     operand (column = lane%16 -> its head column): lane l gets the scores
+//     of tokens 4(l/16) + i, i < 4, for its column;
+//   softmax: the tile maximum per column (4 registers, then the 4 rows); the
 //     running maximum only moves when a ballot finds a tile maximum above it;
-//   PV: per 16-dim block, one 16x16x32 MFMA with A = V^T (row = dim, k = the
-//     lane's 4 tokens, twice) and B = those tokens' weights (hi in k 0..3,
-//     lo in k 4..7), which is the layout the scores came out in; for bf16 a
-//     second one adds the third weight term.
-template <bool BF16>
-__device__ __forceinline__ void tile_compute(WaveState& st, const char* kt,
-                                             const u32x4 (&qb)[4], const uint32_t (&koff)[4],
-                                             const uint32_t (&voff)[8], int tok_row0, int tw1,
-                                             bool partial, float c) {
-  u32x4 ka[4];
+//   PV: per 16-dim block, one 16x16x32 MFMA per column block with A = V^T
+//     (row = dim, k = the lane's 4 tokens, twice; read once for all column
+//     blocks) and B = those tokens' weights (hi in k 0..3, lo in k 4..7),
+//     which is the layout the scores came out in; for bf16 a second one adds
+//     the third weight term.
+template <bool BF16, int D, int NC>
+__device__ __forceinline__ void tile_compute(WaveState<D, NC>& st, const char* kt,
+                                             const u32x4 (&qb)[NC][Geo<D>::kSteps],
+                                             const uint32_t (&koff)[Geo<D>::kSteps],
+                                             const uint32_t (&voff)[Geo<D>::kBlocks],
+                                             int tok_row0, int tw1, bool partial, float c) {
+  constexpr int kS = Geo<D>::kSteps, kM = Geo<D>::kBlocks;
+  u32x4 ka[kS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
-  v4i16_t vt[8];
+  for (int s = 0; s < kS; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
+  v4i16_t vt[kM];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+  for (int m = 0; m < kM; ++m)
     vt[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr_t)(kt + voff[m]));
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[s], sc);
-  float s_[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
   if (partial) {
-    // tokens past the slice get no weight, and their V rows (whatever the
-    // LDS holds there) are replaced by zeros
+    // V rows of tokens past the slice (whatever the LDS holds there) are
+    // replaced by zeros; V^T element i of every block is token 4(lane/16) + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
-    // V^T element i of every block is token 4(lane/16) + i as well
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < kM; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) vt[m][i] = tok_row0 + i < tw1 ? vt[m][i] : (short)0;
   }
-  const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
-  if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
-    const float mn = fmaxf(st.m, tm);
-    const float alpha = exp2_fast(st.m - mn);  // 1 where the maximum stays, 0 from -inf
-    st.m = mn;
-    st.lsum *= alpha;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) st.acc[m] *= alpha;
-  }
-  float pr[4];
+  for (int j = 0; j < NC; ++j) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m + WeightBias<BF16>::log2);
-  st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const Weights<BF16> wb = split_weights<BF16>(pr);
+    for (int s = 0; s < kS; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[j][s], sc);
+    float s_[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
-    const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
-    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[m]);
-    if constexpr (BF16)  // k 4..7 of this one are zero on both sides
-      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
-                                      u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[m]);
+    for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
+    if (partial) {
+      // tokens past the slice get no weight
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
+    }
+    const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
+    if (__builtin_amdgcn_ballot_w64(tm > st.m[j]) != 0) {
+      const float mn = fmaxf(st.m[j], tm);
+      const float alpha = exp2_fast(st.m[j] - mn);  // 1 where the maximum stays, 0 from -inf
+      st.m[j] = mn;
+      st.lsum[j] *= alpha;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) st.acc[j][m] *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m[j] + WeightBias<BF16>::log2);
+    st.lsum[j] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const Weights<BF16> wb = split_weights<BF16>(pr);
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
+      const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
+      st.acc[j][m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[j][m]);
+      if constexpr (BF16)  // k 4..7 of this one are zero on both sides
+        st.acc[j][m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
+                                           u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[j][m]);
+    }
   }
 }
 
-// FP8 staging tile -> 16-bit tile layout. Lane l takes 16-byte chunks
+// FP8 staging tile -> 16-bit tile layout (D = 128). Lane l takes 16-byte chunks
 // 64i + l (i < 2) of the K and of the V staging tile: token c/8, dims
 // 16(c%8) .. +16; their 16 codes become two 16-byte chunks of 8 values each,
 // written where the 16-bit layout keeps them. E4M3FN values are exact in
@@ -357,10 +383,12 @@ __device__ __forceinline__ void convert_fp8_tile(const char* st, char* kt, int l
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        using Gm = Geo<kD8>;
         const int chunk = 2 * c8 + h;  // 16-bit chunk (8 dims) of the row
         const uint32_t off = tv == 0
-            ? (uint32_t)n * kKGroup + (uint32_t)r * kRowBytes + 16u * (uint32_t)((chunk + r) & 15)
-            : kKTile + (uint32_t)n * kVGroup + (uint32_t)r * kRowBytes +
+            ? (uint32_t)n * Gm::kKGroup + (uint32_t)r * Gm::kRowBytes +
+                  16u * (uint32_t)((chunk + r) & 15)
+            : Gm::kKTile + (uint32_t)n * Gm::kVGroup + (uint32_t)r * Gm::kRowBytes +
                   16u * (uint32_t)((chunk + 2 * r) & 15);
         *(u32x4*)(kt + off) = y[h];
       }
@@ -388,22 +416,60 @@ __device__ __forceinline__ void store4(uint16_t* o, f32x4 r, float inv) {
   *(u32x2*)o = u32x2{pack2<BF16>(r[0] * inv, r[1] * inv), pack2<BF16>(r[2] * inv, r[3] * inv)};
 }
 
-template <bool BF16, int BS, bool SPLIT, int NW, bool KV8>
+// Lane ownership of the results: lane l (column u = 16j + l%16 of block j,
+// rows 4(l/16)..+4 of each 16-dim block) speaks for query head u % G. Every
+// head has 16 NC / G column copies; the first `copies` of them (a power of
+// two, at most D/16) split the head's D/16 dim blocks into runs of nown =
+// (D/16) / copies, copy q taking blocks [q nown, (q+1) nown), so each (head,
+// dim) is written by exactly one lane. Kernels built FAST (G <= 4) use four
+// copies, so nown = D/64 is known when compiling and the epilogue is
+// straight-line code.
+struct Owner {
+  int head;  // query head of the KV head, < G
+  int copy;  // u / G
+  int nown;  // dim blocks per owning lane
+  bool active;
+  __device__ int block(int k) const { return copy * nown + k; }
+};
+
+template <bool FAST>
+__device__ __forceinline__ Owner make_owner(int u, int G, int NC, int kM) {
+  int p2 = 4;
+  if constexpr (!FAST) {
+    const int copies = 16 * NC / G;
+    p2 = 1;
+    while (2 * p2 <= copies && 2 * p2 <= kM) p2 *= 2;
+  }
+  Owner o;
+  o.head = u % G;
+  o.copy = u / G;
+  o.nown = kM / p2;
+  o.active = o.copy < p2;
+  return o;
+}
+
+template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, int NC, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
-  constexpr int kNBuf = tile_buffers<KV8>(NW);
-  constexpr int kLoads = KV8 ? 4 : 8;  // load instructions per tile
+  static_assert(!KV8 || D == kD8, "the FP8 path is built for D = 128");
+  static_assert(!FAST || NC == 1, "FAST kernels serve G <= 4");
+  using Gm = Geo<D>;
+  constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
+  constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
+  constexpr int kNBuf = tile_buffers<D, KV8>(NW);
+  constexpr int kLoads = KV8 ? 4 : 2 * Gm::kGroups;  // load instructions per tile
   constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * kLoads);
-  constexpr uint32_t kStage = stage_bytes<KV8>();
+  constexpr uint32_t kStage = stage_bytes<D, KV8>();
   // one array per tile buffer, so the compiler can wait for exactly the
   // loads of the buffer about to be read
   __shared__ __align__(16) char lds0[NW * kStage];
   __shared__ __align__(16) char lds1[NW * kStage];
   __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kStage : 16];
-  __shared__ __align__(16) char ldsc[KV8 ? NW * kLdsTile : 16];  // converted FP8 tile
+  __shared__ __align__(16) char ldsc[KV8 ? NW * Gm::kLdsTile : 16];  // converted FP8 tile
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int b = blockIdx.z;
+  const int G = a.G;
   const int Hq = a.Hkv * G;
   const int nw = a.NH * a.NT;
   const int lane = threadIdx.x & 63;
@@ -412,7 +478,6 @@ void pd_decode_kernel(const KArgs a) {
   const int ts = w / a.NH;  // token slice
   const int g = hg * a.NH + hl;
   const int row = lane >> 4;
-  const int sl = lane & 15;
   auto tile_buf = [&](int d) -> char* {
     char* base = d == 0 ? lds0 : d == 1 ? lds1 : lds2;
     return base + w * kStage;
@@ -421,14 +486,18 @@ void pd_decode_kernel(const KArgs a) {
   const int t0 = p * a.P;
   const int tw0 = t0 + ts * a.Pw;
   const int bi0 = tw0 / BS;
-  // q as the MFMA B operand: head lane%4, dims 32s + 8(lane/16) .. +8.
-  // Loaded before the block ids, so that waiting for the ids (which the
-  // first K/V addresses need) also covers q, and no later wait has to drain
-  // the tile loads.
-  u32x4 qb[4];
-  const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G + (lane & 3)) * D + 8 * row;
+  // q as the MFMA B operand: column u = 16j + lane%16 -> head u % G, dims
+  // 32s + 8(lane/16) .. +8. Loaded before the block ids, so that waiting for
+  // the ids (which the first K/V addresses need) also covers q, and no later
+  // wait has to drain the tile loads.
+  u32x4 qb[NC][kS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qb[s] = *(const u32x4*)(qp + 32 * s);
+  for (int j = 0; j < NC; ++j) {
+    const int hc = (16 * j + (lane & 15)) % G;
+    const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G + hc) * D + 8 * row;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) qb[j][s] = *(const u32x4*)(qp + 32 * s);
+  }
   // block ids of the wave's whole slice, fetched before the context length
   // is known (entries past the live ones are loaded but never used)
   const int nb_max = min(a.Pw / BS, a.MB - bi0);
@@ -437,11 +506,14 @@ void pd_decode_kernel(const KArgs a) {
 #pragma unroll
   for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
 
-  WaveState st;
-  st.lsum = 0.f;
-  st.m = -INFINITY;
+  WaveState<D, NC> st;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NC; ++j) {
+    st.lsum[j] = 0.f;
+    st.m[j] = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) st.acc[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // loop bounds and block addresses in scalar registers
@@ -469,35 +541,37 @@ void pd_decode_kernel(const KArgs a) {
   const int nst = __builtin_amdgcn_readfirstlane(
       tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
-  const uint32_t tok_bytes = a.Hkv * (KV8 ? kRowBytes8 : kRowBytes);
+  constexpr uint32_t kRow = KV8 ? kRowBytes8 : Gm::kRowBytes;
+  constexpr int kChunks = KV8 ? 8 : Gm::kChunks;  // 16-byte chunks per row as loaded
+  const uint32_t tok_bytes = a.Hkv * kRow;
   // global offsets of this lane's 16 bytes in load instruction 0 of a tile:
-  // 16-bit rows take 16 lanes each (4 rows per instruction), chunks rotated;
-  // FP8 rows take 8 lanes each (8 rows per instruction), in order
-  const int lrow = KV8 ? lane >> 3 : row;
-  const uint32_t head_off =
-      (uint32_t)lrow * tok_bytes + (uint32_t)g * (KV8 ? kRowBytes8 : kRowBytes);
-  const uint32_t koff_g =
-      head_off + (uint32_t)(KV8 ? (lane & 7) : ((sl - row) & 15)) * 16u;
+  // a 16-bit row takes C lanes (64 / C rows per instruction), chunks
+  // rotated; an FP8 row takes 8 lanes (8 rows per instruction), in order
+  const int lrow = lane / kChunks;
+  const int lsl = lane % kChunks;
+  const uint32_t head_off = (uint32_t)lrow * tok_bytes + (uint32_t)g * kRow;
+  const uint32_t koff_g = head_off + (uint32_t)(KV8 ? lsl : (lsl - lrow + kChunks) % kChunks) * 16u;
   const uint32_t voff_g =
-      head_off + (uint32_t)(KV8 ? (lane & 7) : ((sl - 2 * row) & 15)) * 16u;
+      head_off + (uint32_t)(KV8 ? lsl : (lsl - 2 * lrow + 2 * kChunks) % kChunks) * 16u;
   // LDS offsets of the two read patterns (see the tile layout above)
-  uint32_t koff[4], voff[8];
+  uint32_t koff[kS], voff[kM];
   {
-    const int t = lane & 15, r = t & 3;
+    constexpr int C = Gm::kChunks, R = Gm::kRowsPerLoad;
+    const int t = lane & 15, r = t % R;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      koff[s] = (uint32_t)(t >> 2) * kKGroup + (uint32_t)r * kRowBytes +
-                16u * (uint32_t)((4 * s + row + r) & 15);
+    for (int s = 0; s < kS; ++s)
+      koff[s] = (uint32_t)(t / R) * Gm::kKGroup + (uint32_t)r * Gm::kRowBytes +
+                16u * (uint32_t)((4 * s + row + r) % C);
     // source lane of the transposing read: token 4(lane/16) + (lane%16)/4,
     // dims 16m + 4(lane%4) .. +4, i.e. chunk 2m + (lane%4)/2, half lane%2
-    const int k = (lane & 15) >> 2, a4 = lane & 3;
+    const int tt = 4 * row + ((lane & 15) >> 2), a4 = lane & 3, rr = tt % R;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      voff[m] = kKTile + (uint32_t)row * kVGroup + (uint32_t)k * kRowBytes +
-                16u * (uint32_t)((2 * m + (a4 >> 1) + 2 * k) & 15) + 8u * (uint32_t)(a4 & 1);
+    for (int m = 0; m < kM; ++m)
+      voff[m] = Gm::kKTile + (uint32_t)(tt / R) * Gm::kVGroup + (uint32_t)rr * Gm::kRowBytes +
+                16u * (uint32_t)((2 * m + (a4 >> 1) + 2 * rr) % C) + 8u * (uint32_t)(a4 & 1);
   }
 
-  // Queue the 8 loads of tile j into buffer d. Straight-line, always eight
+  // Queue the loads of tile j into buffer d. Straight-line, always kLoads
   // loads, so the wait counts stay exact: past the slice (j >= nst) every
   // lane's token is >= tw1 and its offset is out of the block, and the block
   // id is forced to 0, so those loads read nothing.
@@ -509,7 +583,7 @@ void pd_decode_kernel(const KArgs a) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (int64_t)id * a.blk_bytes, a.blk_bytes);
     const uint32_t tb = (uint32_t)(tok % BS) * tok_bytes;
     char* kt = tile_buf(d);
-    constexpr int kRowsPerLoad = KV8 ? 8 : 4;
+    constexpr int kRowsPerLoad = 64 / kChunks;
 #pragma unroll
     for (int n = 0; n < kLoads / 2; ++n) {
       const bool ok = tw0 + tok + kRowsPerLoad * n + lrow < tw1;
@@ -520,8 +594,8 @@ void pd_decode_kernel(const KArgs a) {
       // turn the selects into a divergent branch around the loads (which
       // would issue a load twice and break the exact wait counts)
       asm("" : "+v"(ko), "+v"(vo));
-      const uint32_t kd = KV8 ? n * 1024u : n * kKGroup;
-      const uint32_t vd = KV8 ? kStage8 / 2 + n * 1024u : kKTile + n * kVGroup;
+      const uint32_t kd = KV8 ? n * 1024u : n * Gm::kKGroup;
+      const uint32_t vd = KV8 ? kStage8 / 2 + n * 1024u : Gm::kKTile + n * Gm::kVGroup;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + kd), 16, ko, 0, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + vd), 16, vo, 0, 0, kStream);
     }
@@ -539,8 +613,8 @@ void pd_decode_kernel(const KArgs a) {
     for (int d = 0; d < kNBuf; ++d) {
       const int j = j0 + d;
       // tile j's loads are the oldest in flight: wait until only the later
-      // tiles' (kNBuf - 1) * 8 loads are outstanding. Explicit, because the
-      // compiler does not always see that these LDS reads depend on them.
+      // tiles' (kNBuf - 1) * kLoads loads are outstanding. Explicit, because
+      // the compiler does not always see that these LDS reads depend on them.
       __builtin_amdgcn_s_waitcnt(kWaitTile);
       __builtin_amdgcn_sched_barrier(0);
       // Before a buffer is refilled every LDS read of it has completed: the
@@ -548,7 +622,7 @@ void pd_decode_kernel(const KArgs a) {
       // a refill past the slice reads no memory, so it lands at once.
       if constexpr (KV8) {
         // convert, then refill the staging buffer before computing
-        char* ct = ldsc + w * kLdsTile;
+        char* ct = ldsc + w * Gm::kLdsTile;
         if (j < nst) convert_fp8_tile<BF16>(tile_buf(d), ct, lane);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kWaitLds);
@@ -557,14 +631,14 @@ void pd_decode_kernel(const KArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (j < nst) {
           const int tile0 = tw0 + kTileTok * j;
-          tile_compute<BF16>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
-                             tile0 + kTileTok > tw1, c);
+          tile_compute<BF16, D, NC>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
+                                    tile0 + kTileTok > tw1, c);
         }
       } else {
         if (j < nst) {
           const int tile0 = tw0 + kTileTok * j;
-          tile_compute<BF16>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
-                             tile0 + kTileTok > tw1, c);
+          tile_compute<BF16, D, NC>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
+                                    tile0 + kTileTok > tw1, c);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kWaitLds);
@@ -578,61 +652,97 @@ void pd_decode_kernel(const KArgs a) {
   // tile buffers are reused below
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- this lane's share of the result: query head h of the KV head, the
-  // 8 dims [d0, d0+4) and [d0+16, d0+20) (one of the 4 copies of each)
-  const int h = lane & 3;
-  const int qd = (lane >> 2) & 3;
-  const int d0 = 32 * qd + 4 * row;
-  f32x4 o0 = qd == 0 ? st.acc[0] : qd == 1 ? st.acc[2] : qd == 2 ? st.acc[4] : st.acc[6];
-  f32x4 o1 = qd == 0 ? st.acc[1] : qd == 1 ? st.acc[3] : qd == 2 ? st.acc[5] : st.acc[7];
-  float m_r = st.m;
-  float l_r = sum_rows(st.lsum);
+  // ---- per column block: the lane's head, its owned dim blocks gathered
+  // into o[j][0..nown), running maximum and weight sum
+  Owner own[NC];
+  f32x4 o[NC][kOwn];
+  float m_r[NC], l_r[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    own[j] = make_owner<FAST>(16 * j + (lane & 15), G, NC, kM);
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      o[j][k] = st.acc[j][k];
+      if constexpr (FAST) {
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+          if (own[j].copy == q) o[j][k] = st.acc[j][q * kOwn + k];
+      } else {
+#pragma unroll
+        for (int m = k + 1; m < kM; ++m)
+          if (m == own[j].block(k)) o[j][k] = st.acc[j][m];
+      }
+    }
+    m_r[j] = st.m[j];
+    l_r[j] = sum_rows(st.lsum[j]);
+  }
+  const int d_row = 4 * row;  // the lane's 4 dims within each 16-dim block
 
-  // ---- merge the NT slices of each head through LDS (the first tile
-  // buffer); slice 0 keeps the result
+  // ---- merge the NT slices of each head through LDS (a full 16-bit tile
+  // per wave: the first tile buffer, or the converted-tile buffer of an FP8
+  // kernel; it holds G * (D + 2) floats per wave for G <= 16, and the
+  // planner keeps NT = 1 above that); slice 0 keeps the result
   if (a.NT > 1) {
     __syncthreads();  // every wave is done with its tile buffers
-    float* s_acc = (float*)lds0;            // [(w*G + h)*D + dim]
-    float* s_m = (float*)lds0 + nw * G * D;  // [w*G + h]
+    float* s_acc = (float*)(KV8 ? ldsc : lds0);  // [(w*G + h)*D + dim]
+    float* s_m = s_acc + nw * G * D;             // [w*G + h]
     float* s_l = s_m + nw * G;
-    *(f32x4*)(s_acc + (w * G + h) * D + d0) = o0;
-    *(f32x4*)(s_acc + (w * G + h) * D + d0 + 16) = o1;
-    if ((lane >> 2) == 0) {
-      s_m[w * G + h] = m_r;
-      s_l[w * G + h] = l_r;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (!own[j].active) continue;
+      const int h = own[j].head;
+      float* dst = s_acc + (w * G + h) * D + 16 * own[j].block(0) + d_row;
+#pragma unroll
+      for (int k = 0; k < kOwn; ++k)
+        if (FAST || k < own[j].nown) *(f32x4*)(dst + 16 * k) = o[j][k];
+      if (row == 0 && own[j].copy == 0) {
+        s_m[w * G + h] = m_r[j];
+        s_l[w * G + h] = l_r[j];
+      }
     }
     __syncthreads();
     if (ts == 0) {
-      float M = m_r;
-      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
-      float den = 0.f;
-      o0 = f32x4{0.f, 0.f, 0.f, 0.f};
-      o1 = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i < a.NT; ++i) {
-        const int wi = (i * a.NH + hl) * G + h;
-        const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
-        den = fmaf(wt, s_l[wi], den);
-        const f32x4 x0 = *(const f32x4*)(s_acc + wi * D + d0);
-        const f32x4 x1 = *(const f32x4*)(s_acc + wi * D + d0 + 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o0[e] = fmaf(wt, x0[e], o0[e]);
-          o1[e] = fmaf(wt, x1[e], o1[e]);
+      for (int j = 0; j < NC; ++j) {
+        if (!own[j].active) continue;
+        const int h = own[j].head;
+        float M = m_r[j];
+        for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
+        float den = 0.f;
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k) o[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < a.NT; ++i) {
+          const int wi = (i * a.NH + hl) * G + h;
+          const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
+          den = fmaf(wt, s_l[wi], den);
+          const float* src = s_acc + wi * D + 16 * own[j].block(0) + d_row;
+#pragma unroll
+          for (int k = 0; k < kOwn; ++k) {
+            if (!FAST && k >= own[j].nown) continue;
+            const f32x4 x = *(const f32x4*)(src + 16 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[j][k][e] = fmaf(wt, x[e], o[j][k][e]);
+          }
         }
+        m_r[j] = M;
+        l_r[j] = den;
       }
-      m_r = M;
-      l_r = den;
     }
   }
   const bool owner = ts == 0;
-  const int hq = g * G + h;  // query head of this lane
 
   if constexpr (!SPLIT) {
     if (owner) {
-      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
-      const float inv = a.out_scale / l_r;
-      store4<BF16>(o, o0, inv);
-      store4<BF16>(o + 16, o1, inv);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if (!own[j].active) continue;
+        uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + own[j].head) * D +
+                       16 * own[j].block(0) + d_row;
+        const float inv = a.out_scale / l_r[j];
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k)
+          if (FAST || k < own[j].nown) store4<BF16>(op + 16 * k, o[j][k], inv);
+      }
     }
     return;
   } else {
@@ -642,18 +752,24 @@ void pd_decode_kernel(const KArgs a) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o_part + slot0 * D, rows_bytes);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse_part + slot0, (uint32_t)G * a.S * 4);
     if (owner) {
-      // the raw buffer builtins move 32-bit words: floats go through bit casts
-      const float inv = 1.0f / l_r;
-      const uint32_t off = ((uint32_t)(h * a.S + p) * D + d0) * 4;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0 * inv), ro, off, 0,
-                                             kCoherent);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1 * inv), ro, off + 64,
-                                             0, kCoherent);
-      if ((lane >> 2) == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r) -
-                                             WeightBias<BF16>::log2),
-            rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if (!own[j].active) continue;
+        const int h = own[j].head;
+        // the raw buffer builtins move 32-bit words: floats go through bit casts
+        const float inv = 1.0f / l_r[j];
+        const uint32_t off = ((uint32_t)(h * a.S + p) * D + 16 * own[j].block(0) + d_row) * 4;
+#pragma unroll
+        for (int k = 0; k < kOwn; ++k)
+          if (FAST || k < own[j].nown)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[j][k] * inv), ro,
+                                                   off + 64 * k, 0, kCoherent);
+        if (row == 0 && own[j].copy == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, m_r[j] + __builtin_amdgcn_logf(l_r[j]) -
+                                               WeightBias<BF16>::log2),
+              rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
+      }
     }
     // the stores are complete (and past every non-coherent cache) before the
     // counter moves
@@ -671,52 +787,67 @@ void pd_decode_kernel(const KArgs a) {
     __syncthreads();
     if (!s_last || !owner) return;
 
-    // ---- last workgroup: LSE merge over the n_live partitions, in order
+    // ---- last workgroup: LSE merge over the n_live partitions, in order,
+    // two owned dim blocks per pass (one pass at G <= 4, D = 128)
     constexpr int kBatch = 8;
-    float M = -INFINITY, den = 0.f;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < n_live; i0 += kBatch) {
-      float lse[kBatch];
-      f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        // partitions past n_live read zeros and are skipped below
-        const bool ok = i0 + u < n_live;
-        const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
-        const uint32_t off = ok ? (slot * D + d0) * 4 : kOutOfBlock;
-        x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
-                                                                                kCoherent));
-        x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              ro, ok ? off + 64 : kOutOfBlock, 0, kCoherent));
-        lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
-      }
-      float bm = M;
+    for (int j = 0; j < NC; ++j) {
+      if (!own[j].active) continue;
+      const int h = own[j].head;
+      uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D +
+                     16 * own[j].block(0) + d_row;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
-      const float alpha = exp2_fast(M - bm);  // 0 on the first batch
-      den *= alpha;
-      acc0 *= alpha;
-      acc1 *= alpha;
-      M = bm;
+      for (int k0 = 0; k0 < kOwn; k0 += 2) {
+        const int nown = FAST ? kOwn : own[j].nown;
+        if (k0 >= nown) break;
+        const bool two = k0 + 1 < nown;
+        const uint32_t dim0 = (uint32_t)(16 * own[j].block(k0) + d_row);
+        float M = -INFINITY, den = 0.f;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        for (int i0 = 0; i0 < n_live; i0 += kBatch) {
+          float lse[kBatch];
+          f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (i0 + u < n_live) {
-          const float wt = exp2_fast(lse[u] - M);
-          den += wt;
+          for (int u = 0; u < kBatch; ++u) {
+            // partitions past n_live read zeros and are skipped below
+            const bool ok = i0 + u < n_live;
+            const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
+            const uint32_t off = ok ? (slot * D + dim0) * 4 : kOutOfBlock;
+            x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
+                                                                                    kCoherent));
+            x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  ro, ok && two ? off + 64 : kOutOfBlock, 0,
+                                                  kCoherent));
+            lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
+          }
+          float bm = M;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
-            acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
+          for (int u = 0; u < kBatch; ++u)
+            if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
+          const float alpha = exp2_fast(M - bm);  // 0 on the first batch
+          den *= alpha;
+          acc0 *= alpha;
+          acc1 *= alpha;
+          M = bm;
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if (i0 + u < n_live) {
+              const float wt = exp2_fast(lse[u] - M);
+              den += wt;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
+                acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
+              }
+            }
           }
         }
+        const float inv = a.out_scale / den;
+        store4<BF16>(op + 16 * k0, acc0, inv);
+        if (two) store4<BF16>(op + 16 * (k0 + 1), acc1, inv);
       }
     }
-    uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + hq) * D + d0;
-    const float inv = a.out_scale / den;
-    store4<BF16>(o, acc0, inv);
-    store4<BF16>(o + 16, acc1, inv);
   }
 }
 
@@ -727,29 +858,48 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-template <bool BF16, int BS, bool SPLIT, bool KV8>
+template <bool BF16, int BS, bool SPLIT, bool KV8, int D, int NC, bool FAST>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   void* args[] = {(void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
-  const void* f = nw <= 4 ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8>
-                          : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8, KV8>;
+  const void* f = nw <= 4
+      ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, NC, FAST>
+      : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8, KV8, D, NC, FAST>;
   return hipLaunchKernel(f, grid, dim3(nw * 64), args, 0, st);
 }
 
-template <bool BF16, bool SPLIT, bool KV8>
+template <bool BF16, bool SPLIT, bool KV8, int D, int NC, bool FAST>
 hipError_t pick_block(const KArgs& ka, dim3 grid, int bs, int nw, hipStream_t st) {
-  return bs == 32 ? launch_decode<BF16, 32, SPLIT, KV8>(ka, grid, nw, st)
-                  : launch_decode<BF16, 16, SPLIT, KV8>(ka, grid, nw, st);
+  return bs == 32 ? launch_decode<BF16, 32, SPLIT, KV8, D, NC, FAST>(ka, grid, nw, st)
+                  : launch_decode<BF16, 16, SPLIT, KV8, D, NC, FAST>(ka, grid, nw, st);
 }
 
-template <bool KV8>
+template <bool KV8, int D, int NC, bool FAST>
 hipError_t pick_dtype(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
                       hipStream_t st) {
   if (bf16)
-    return split ? pick_block<true, true, KV8>(ka, grid, bs, nw, st)
-                 : pick_block<true, false, KV8>(ka, grid, bs, nw, st);
-  return split ? pick_block<false, true, KV8>(ka, grid, bs, nw, st)
-               : pick_block<false, false, KV8>(ka, grid, bs, nw, st);
+    return split ? pick_block<true, true, KV8, D, NC, FAST>(ka, grid, bs, nw, st)
+                 : pick_block<true, false, KV8, D, NC, FAST>(ka, grid, bs, nw, st);
+  return split ? pick_block<false, true, KV8, D, NC, FAST>(ka, grid, bs, nw, st)
+               : pick_block<false, false, KV8, D, NC, FAST>(ka, grid, bs, nw, st);
+}
+
+// Instances: 16-bit caches at D = 64 and 128 with one column block (G <= 4
+// FAST, or any G <= 16) or two (G <= 32); FP8 caches at D = 128, G <= 16.
+hipError_t pick_geometry(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
+                         bool kv8, int D, int G, hipStream_t st) {
+  const bool fast = G <= 4;
+  if (kv8)
+    return fast ? pick_dtype<true, 128, 1, true>(ka, grid, bs, nw, bf16, split, st)
+                : pick_dtype<true, 128, 1, false>(ka, grid, bs, nw, bf16, split, st);
+  if (D == 64) {
+    if (G > 16) return pick_dtype<false, 64, 2, false>(ka, grid, bs, nw, bf16, split, st);
+    return fast ? pick_dtype<false, 64, 1, true>(ka, grid, bs, nw, bf16, split, st)
+                : pick_dtype<false, 64, 1, false>(ka, grid, bs, nw, bf16, split, st);
+  }
+  if (G > 16) return pick_dtype<false, 128, 2, false>(ka, grid, bs, nw, bf16, split, st);
+  return fast ? pick_dtype<false, 128, 1, true>(ka, grid, bs, nw, bf16, split, st)
+              : pick_dtype<false, 128, 1, false>(ka, grid, bs, nw, bf16, split, st);
 }
 
 }  // namespace
@@ -774,6 +924,7 @@ int32_t launch(const Launch& l) {
     ka.lse_part = (float*)(ws + kCounterBytes + partials_bytes(l.shape, l.plan));
   }
   ka.Hkv = l.shape.Hkv;
+  ka.G = l.shape.Hq / l.shape.Hkv;
   ka.MB = l.shape.max_blocks_per_seq;
   ka.S = l.plan.splits;
   ka.P = l.plan.partition_tokens;
@@ -783,18 +934,21 @@ int32_t launch(const Launch& l) {
   ka.scale_log2 = l.scale * 1.4426950408889634f * (l.kv_fp8 ? l.k_scale : 1.0f);
   ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
-                 (l.kv_fp8 ? kRowBytes8 : kRowBytes);
+                 (l.kv_fp8 ? kRowBytes8 : 2u * (uint32_t)l.shape.D);
   const dim3 grid(l.plan.splits, l.shape.Hkv / l.plan.heads_per_group, l.shape.B);
   const int nw = l.plan.heads_per_group * l.plan.slices;
-  // each wave owns kLdsTile bytes of every tile buffer of its workgroup
-  if (nw < 1 || nw > kMaxWaves || l.shape.Hkv % l.plan.heads_per_group != 0)
+  const int nc = ka.G > 16 ? 2 : 1;
+  // each wave owns a tile's bytes of every tile buffer of its workgroup; the
+  // slice merge needs G * (D + 2) floats of them per wave
+  if (nw < 1 || nw > kMaxWaves || l.shape.Hkv % l.plan.heads_per_group != 0 ||
+      ka.G > kMaxGroup || (l.shape.D != 64 && l.shape.D != 128) ||
+      (l.kv_fp8 && (l.shape.D != kD8 || nc != 1)) || (nc > 1 && l.plan.slices > 1))
     return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;
   const bool bf16 = l.shape.dtype == PD_DTYPE_BF16;
-  const hipError_t e = l.kv_fp8
-      ? pick_dtype<true>(ka, grid, l.shape.block_size, nw, bf16, split, st)
-      : pick_dtype<false>(ka, grid, l.shape.block_size, nw, bf16, split, st);
+  const hipError_t e = pick_geometry(ka, grid, l.shape.block_size, nw, bf16, split, l.kv_fp8,
+                                     l.shape.D, ka.G, st);
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

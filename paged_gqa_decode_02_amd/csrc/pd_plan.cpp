@@ -36,7 +36,7 @@ int32_t check_shape(const Shape& s) {
     return PD_ERR_SHAPE;
   if (s.Hq % s.Hkv != 0) return PD_ERR_SHAPE;
   if ((int64_t)s.max_blocks_per_seq * s.block_size > INT_MAX / 2) return PD_ERR_SHAPE;
-  if (s.D != kHeadDim || s.Hq / s.Hkv != kGroup) return PD_ERR_UNSUPPORTED;
+  if ((s.D != 64 && s.D != 128) || s.Hq / s.Hkv > kMaxGroup) return PD_ERR_UNSUPPORTED;
   if (s.block_size != 16 && s.block_size != 32) return PD_ERR_UNSUPPORTED;
   // grid limits: (S, Hkv, B) with y and z below 65536
   if (s.B > 65535 || s.Hkv > 65535) return PD_ERR_SHAPE;
@@ -47,7 +47,9 @@ int32_t check_shape(const Shape& s) {
 // block_size tokens) into S partitions of P tokens, each served by one
 // workgroup of 4 waves per group of NH KV heads; a wave covers one slice of
 // Pw tokens (block aligned, at most 256 blocks) of one head, in tiles of 16.
-// Slices of a head merge in LDS, partitions merge across workgroups.
+// Slices of a head merge in LDS, partitions merge across workgroups. With
+// more than 16 query heads per KV head (MQA) a workgroup has one slice per
+// head and the split rule fills the GPU with partitions instead.
 //
 // The rule was fitted to sweeps of every (NH, NT, S) on an MI355X over the
 // decode workloads (batch 1..64, contexts 16..4,096, block sizes 16/32):
@@ -71,8 +73,11 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
   const int64_t pw_max = kMaxWaveBlocks * bs;
   const bool pairs = s.Hkv % 2 == 0;
+  // more than 16 query heads per KV head: the slice merge would not fit a
+  // wave's LDS share, so one slice per workgroup (partitions take the rest)
+  const bool one_slice = s.Hq / s.Hkv > 16;
   int64_t nh = pairs && units >= 2 * kFillWaves / kWaves ? 2 : 1;
-  int64_t nt = kWaves / nh;
+  int64_t nt = one_slice ? 1 : kWaves / nh;
   int64_t P;
   if (requested_splits > 0) {
     const int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
@@ -86,7 +91,7 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
       if (S < 1) S = 1;
       if (S > 1 && pairs && nh == 1 && cap / (S * nt) >= kPairTiles * kTileTok) {
         nh = 2;
-        nt = kWaves / nh;
+        nt = one_slice ? 1 : kWaves / nh;
         S *= 2;
       }
     }
@@ -99,6 +104,7 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
 #endif
   if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
+  if (one_slice) nt = 1;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
   int64_t pw = round_up(ceil_div(P, nt), bs);
   if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more

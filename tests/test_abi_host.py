@@ -91,8 +91,12 @@ def test_forced_splits(req):
 
 
 def test_plan_rejects_what_the_attention_call_rejects():
+    for D in (96, 256, 32):
+        with pytest.raises(pd.PagedDecodeError) as e:
+            pd.paged_decode_plan(1, 32, 8, D, 4, 16, BF16)
+        assert e.value.code == CODES["PD_ERR_UNSUPPORTED"]
     with pytest.raises(pd.PagedDecodeError) as e:
-        pd.paged_decode_plan(1, 32, 8, 64, 4, 16, BF16)
+        pd.paged_decode_plan(1, 33, 1, 128, 4, 16, BF16)   # 33 query heads per KV head
     assert e.value.code == CODES["PD_ERR_UNSUPPORTED"]
     with pytest.raises(pd.PagedDecodeError) as e:
         pd.paged_decode_plan(1, 30, 8, 128, 4, 16, BF16)
@@ -103,7 +107,7 @@ def test_plan_rejects_what_the_attention_call_rejects():
     with pytest.raises(pd.PagedDecodeError) as e:
         pd.paged_decode_plan(1, 32, 8, 128, 4, 16, BF16, num_splits=0)
     assert e.value.code == CODES["PD_ERR_SHAPE"]
-    assert pd.paged_decode_workspace_bytes(1, 32, 8, 64, 4, 16, BF16) == 0
+    assert pd.paged_decode_workspace_bytes(1, 32, 8, 96, 4, 16, BF16) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -128,8 +132,9 @@ def call(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=5), "PD_ERR_DTYPE"),
-    (dict(D=64), "PD_ERR_UNSUPPORTED"),
-    (dict(Hq=16), "PD_ERR_UNSUPPORTED"),
+    (dict(D=96), "PD_ERR_UNSUPPORTED"),
+    (dict(D=256), "PD_ERR_UNSUPPORTED"),
+    (dict(Hq=8 * 33), "PD_ERR_UNSUPPORTED"),
     (dict(Hq=30), "PD_ERR_SHAPE"),
     (dict(bs=8), "PD_ERR_UNSUPPORTED"),
     (dict(bs=0), "PD_ERR_SHAPE"),
@@ -215,3 +220,27 @@ def test_fp8_entry_point_empty_batch_is_a_no_op():
     f = pd.lib.paged_decode_attention_fp8
     assert f(0, 0, 0, 0, 0, 1, 0, 0, 32, 8, 128, 16, 0.0883883, BF16, 1.0, 1.0, 0, 0, 0, 0) == \
         CODES["PD_OK"]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 64), (32, 1, 128), (28, 4, 128)])
+def test_fp8_entry_point_rejects_geometries_it_is_not_built_for(Hq, Hkv, D):
+    # the FP8 kernels are built for D = 128 and at most 16 query heads per KV head
+    f = pd.lib.paged_decode_attention_fp8
+    args = [BASE, BASE + (1 << 24), BASE + (2 << 24), BASE + (3 << 24), BASE + (3 << 24) + 4096,
+            1, BASE + (4 << 24), 2, Hq, Hkv, D, 16, 0.125, BF16]
+    want = "PD_ERR_UNSUPPORTED" if (D != 128 or Hq // Hkv > 16) else "PD_ERR_NULL"
+    if want == "PD_ERR_NULL":   # supported: make it fail on a null output instead of launching
+        args[6] = 0
+    assert f(*args, 1.0, 1.0, 0, 0, 0, 0) == CODES[want]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 64), (32, 1, 128), (32, 1, 64), (8, 8, 128),
+                                      (20, 1, 128), (64, 4, 64)])
+@pytest.mark.parametrize("B,L", [(1, 16), (1, 4096), (8, 1024), (64, 4096)])
+def test_plan_at_other_geometries(Hq, Hkv, D, B, L):
+    MB = -(-L // 16)
+    S, P = pd.paged_decode_plan(B, Hq, Hkv, D, MB, 16, BF16)
+    assert S >= 1 and P % 16 == 0 and S * P >= MB * 16
+    ws = pd.paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, 16, BF16)
+    if S > 1:
+        assert ws >= 256 * 1024 + B * Hq * S * D * 4 + B * Hq * S * 4

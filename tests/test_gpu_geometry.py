@@ -45,3 +45,51 @@ def test_f16_block32_long_contexts():
                             block_size=32, seed=80)
     print(c.describe(), flush=True)
     check_case(c)
+
+
+# ---------------------------------------------------------------------------
+# other geometries: head dim 64, odd group sizes (14/2 -> 7), MQA (32/1), MHA
+
+import numpy as np
+
+OTHER = [
+    # Hq, Hkv, D, dtype, bs
+    (14, 2, 64, "bf16", 16),    # the pages' 14/2 D64 route
+    (14, 2, 128, "f16", 32),
+    (32, 1, 128, "bf16", 16),   # MQA
+    (32, 1, 64, "f16", 16),
+    (8, 8, 128, "bf16", 32),    # MHA, G = 1
+    (16, 8, 64, "bf16", 16),    # G = 2
+    (24, 8, 128, "f16", 16),    # G = 3
+    (40, 8, 128, "bf16", 16),   # G = 5
+    (64, 8, 128, "bf16", 32),   # G = 8
+    (32, 2, 64, "f16", 32),     # G = 16
+    (20, 1, 128, "bf16", 16),   # G = 20, two column blocks with repeats
+    (32, 8, 64, "bf16", 16),    # D = 64 at the 32/8 grouping
+]
+
+
+def other_case(Hq, Hkv, D, dtype, bs, lens, seed, name="geom"):
+    return workloads.make_case(f"{name}_{Hq}x{Hkv}_D{D}_{dtype}_bs{bs}", len(lens), lens,
+                               dtype=dtype, block_size=bs, Hq=Hq, Hkv=Hkv, D=D, seed=seed,
+                               scale=float(np.float32(1.0 / np.sqrt(D))))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,bs", OTHER)
+@pytest.mark.parametrize("splits", [None, 1, 3])
+def test_other_geometries(Hq, Hkv, D, dtype, bs, splits):
+    lens = [1, 37, 700, 1024, 513, 0, 16]
+    c = other_case(Hq, Hkv, D, dtype, bs, lens, seed=Hq + 3 * Hkv + D)
+    print(f"{c.describe()} S={splits}", flush=True)
+    check_case(c, num_splits=splits, what=f"{c.name} S={splits}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,B,L", [(14, 2, 64, 32, 1024), (32, 1, 128, 8, 4096),
+                                          (32, 1, 64, 64, 512), (14, 2, 64, 1, 4096),
+                                          (64, 8, 128, 16, 2048)])
+def test_other_geometries_planned_long(Hq, Hkv, D, B, L):
+    c = other_case(Hq, Hkv, D, "bf16", 16, [L] * B, seed=B + L, name="long")
+    import paged_gqa_decode_02_amd as pd
+    S, P = pd.paged_decode_plan(B, Hq, Hkv, D, c.max_blocks_per_seq, 16, torch.bfloat16)
+    print(f"{c.describe()} plan S={S} P={P}", flush=True)
+    check_case(c)
