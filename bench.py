@@ -21,6 +21,7 @@ the GPU tests cover.
 Other modes:
   --calibrate-copy   only run device-to-device copies of a known size
                      (reference kernel for the HBM traffic counters)
+  --extras-only      only the RoPE + KV write and block-movement tables
   --ingest-pmc F W CF CW
                      turn four rocprofv3 --pmc counter CSVs (FETCH_SIZE and
                      WRITE_SIZE of the bench run, then of the copy run) into
@@ -70,6 +71,11 @@ def make_workload(name: str, seed: int = 0):
     if name.startswith("splitk_"):
         _, b, l = name.split("_")
         return workloads.splitk(int(b[1:]), int(l[1:]), seed, kv_dtype=kv)
+    if name.startswith("geom_"):
+        # geom_14x2_D64_B32_L1024
+        _, hh, d, b, l = name.split("_")
+        hq, hkv = hh.split("x")
+        return workloads.geometry(int(hq), int(hkv), int(d[1:]), int(b[1:]), int(l[1:]), seed)
     if name.startswith("short_"):
         # short_B32_L64_bf16_bs16
         _, b, l, dt, bs = name.split("_")
@@ -482,6 +488,8 @@ def main():
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="only the RoPE + KV write and block-movement tables (for profiling)")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"))
     args = ap.parse_args()
 
@@ -498,6 +506,13 @@ def main():
     import paged_gqa_decode_02_amd as pd
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.extras_only:
+        from workloads import rope as wrope
+        table = pd.rope_cos_sin_table(32768, 128, wrope.QWEN_BASE)
+        print(json.dumps({"rope_kv_write": {n: bench_rope(n, torch, pd, table) for n in ROPE_CASES},
+                          "kv_block_moves": {n: bench_blocks(n, torch, pd) for n in BLOCK_CASES}}),
+              flush=True)
         return
 
     case = make_workload(args.workload, args.seed)
@@ -554,7 +569,10 @@ def main():
         for name in ("splitk_B8_L1024", "splitk_B8_L4096", "splitk_B32_L1024", "splitk_B64_L1024",
                      "splitk_B1_L1024", "ragged", "short_B32_L64_bf16_bs16",
                      "short_B32_L64_f16_bs32", "tiny", "large_fp8", "splitk_B32_L1024_fp8",
-                     "splitk_B8_L1024_fp8", "ragged_fp8"):
+                     "splitk_B8_L1024_fp8", "ragged_fp8", "geom_14x2_D64_B32_L1024",
+                     "geom_14x2_D64_B64_L4096", "geom_32x1_D128_B8_L4096",
+                     "geom_32x1_D128_B64_L4096", "geom_32x1_D64_B64_L4096",
+                     "geom_64x8_D128_B16_L4096"):
             others[name] = bench_other(name, torch, pd)
         res["others"] = others
         from workloads import rope as wrope

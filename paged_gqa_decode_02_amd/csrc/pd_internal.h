@@ -15,9 +15,11 @@ struct Shape {
   int32_t B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype;
 };
 
-// How one call is laid out on the GPU: a grid of (S, Hkv/NH, B) workgroups
-// of NH x NT waves; wave w serves KV head w % NH of its group over token
-// slice w / NH (Pw tokens) of its partition (P tokens).
+// How one call is laid out on the GPU: a grid of (S, HS*Hkv/NH, B)
+// workgroups of NH x NT waves; wave w serves virtual KV head w % NH of its
+// group over token slice w / NH (Pw tokens) of its partition (P tokens). A
+// KV head with more than 16 query heads is HS virtual KV heads of G/HS query
+// heads each (consecutive virtual heads read the same physical KV head).
 struct Plan {
   int32_t splits;            // S: context partitions per (sequence, KV head)
   int32_t partition_tokens;  // P: tokens per partition, a multiple of block_size
@@ -25,6 +27,7 @@ struct Plan {
   int32_t slices;            // NT: token slices per workgroup, NH * NT <= 8
   int32_t wave_tokens;       // Pw: tokens per slice, a multiple of block_size,
                              //     at most 256 blocks; NT * Pw >= P
+  int32_t head_split;        // HS: virtual KV heads per KV head, G / HS <= 16
 };
 
 // Most blocks one wave's slice may span (four block ids per lane).

@@ -6,8 +6,11 @@
 // served by one pass over that head's K/V bytes, and a long context is cut
 // into partitions whose normalised partial outputs and log-sum-exps are
 // merged. Built for head dims D = 64 and 128 and any G up to 32 (MQA at
-// 32/1 included): G <= 16 query heads fill one 16-column MFMA block, G <= 32
-// two (NC), the extra columns repeating heads.
+// 32/1 included). The query heads of a wave fill the 16 columns of an MFMA
+// block (spare columns repeat heads); a KV head with more than 16 query
+// heads is served by HS "virtual" KV heads of G / HS <= 16 query heads each,
+// whose waves sit in one workgroup and read the same K/V blocks together
+// (the second read is an L2 hit).
 //
 // One kernel. Workgroup (partition p, KV-head group hg, sequence b) has
 // NH x NT wave64s: wave w serves KV head hg*NH + w%NH over token slice w/NH
@@ -29,8 +32,7 @@
 //     (wave-uniform) id with v_readlane, so addresses are scalar.
 //   * scores: q . k for the 16 tokens of a tile and 16 query-head columns
 //     are one 16x16 output of D/32 v_mfma_f32_16x16x32 (bf16 or f16 inputs,
-//     exact products, fp32 sums) per column block, read from LDS in the
-//     operand order; one multiply by scale*log2(e) puts the softmax in base 2
+//     exact products, fp32 sums), read from LDS in the operand order; one multiply by scale*log2(e) puts the softmax in base 2
 //     (v_exp_f32).
 //   * softmax: per head column, a running maximum that only moves when a
 //     ballot finds a tile maximum above it (then the accumulators are
@@ -81,8 +83,9 @@ struct KArgs {
   float* o_part;      // [B, Hq, S, D]
   float* lse_part;    // [B, Hq, S], log2 domain
   int32_t* counters;  // [B, Hkv / NH], at the start of the workspace
-  int32_t Hkv;
-  int32_t G;   // query heads per KV head
+  int32_t Hkv;  // virtual KV heads: physical KV heads x HS
+  int32_t HS;   // virtual KV heads per physical KV head
+  int32_t G;    // query heads per virtual KV head, <= 16
   int32_t MB;
   int32_t S;
   int32_t P;
@@ -269,32 +272,30 @@ struct WeightBias {
   static constexpr float log2 = BF16 ? 0.f : 8.f;
 };
 
-// Per-lane state of one wave's online softmax over its token slice, per
-// column block j < NC. Lane l follows head column 16j + l%16 (query head
-// (16j + l%16) % G of the KV head); acc[j][m][i] is its unnormalised PV sum
-// for dim 16m + 4(l/16) + i.
-template <int D, int NC>
+// Per-lane state of one wave's online softmax over its token slice. Lane l
+// follows head column l%16 (query head (l%16) % G of the virtual KV head);
+// acc[m][i] is its unnormalised PV sum for dim 16m + 4(l/16) + i.
+template <int D>
 struct WaveState {
-  f32x4 acc[NC][Geo<D>::kBlocks];
-  float lsum[NC];  // sum of weights over the tokens of this lane's row
-  float m[NC];     // running maximum (log2 domain)
+  f32x4 acc[Geo<D>::kBlocks];
+  float lsum;  // sum of weights over the tokens of this lane's row
+  float m;     // running maximum (log2 domain)
 };
 
 // One 16-token tile, already in LDS at kt (K) and kt + kKTile (V).
-//   scores: the K tile is the A operand of D/32 16x16x32 MFMAs per column
-//     block (row = token lane%16, k = dims 32s + 8(lane/16) .. +8), q the B
-//     operand (column = lane%16 -> its head column): lane l gets the scores
-//     of tokens 4(l/16) + i, i < 4, for its column;
+//   scores: the K tile is the A operand of D/32 16x16x32 MFMAs (row = token
+//     lane%16, k = dims 32s + 8(lane/16) .. +8), q the B operand (column =
+//     lane%16 -> its head): lane l gets the scores of tokens 4(l/16) + i,
+//     i < 4, for its column;
 //   softmax: the tile maximum per column (4 registers, then the 4 rows); the
 //     running maximum only moves when a ballot finds a tile maximum above it;
-//   PV: per 16-dim block, one 16x16x32 MFMA per column block with A = V^T
-//     (row = dim, k = the lane's 4 tokens, twice; read once for all column
-//     blocks) and B = those tokens' weights (hi in k 0..3, lo in k 4..7),
-//     which is the layout the scores came out in; for bf16 a second one adds
-//     the third weight term.
-template <bool BF16, int D, int NC>
-__device__ __forceinline__ void tile_compute(WaveState<D, NC>& st, const char* kt,
-                                             const u32x4 (&qb)[NC][Geo<D>::kSteps],
+//   PV: per 16-dim block, one 16x16x32 MFMA with A = V^T (row = dim, k = the
+//     lane's 4 tokens, twice) and B = those tokens' weights (hi in k 0..3, lo
+//     in k 4..7), which is the layout the scores came out in; for bf16 a
+//     second one adds the third weight term.
+template <bool BF16, int D>
+__device__ __forceinline__ void tile_compute(WaveState<D>& st, const char* kt,
+                                             const u32x4 (&qb)[Geo<D>::kSteps],
                                              const uint32_t (&koff)[Geo<D>::kSteps],
                                              const uint32_t (&voff)[Geo<D>::kBlocks],
                                              int tok_row0, int tw1, bool partial, float c) {
@@ -306,50 +307,45 @@ __device__ __forceinline__ void tile_compute(WaveState<D, NC>& st, const char* k
 #pragma unroll
   for (int m = 0; m < kM; ++m)
     vt[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr_t)(kt + voff[m]));
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kS; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[s], sc);
+  float s_[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
   if (partial) {
-    // V rows of tokens past the slice (whatever the LDS holds there) are
-    // replaced by zeros; V^T element i of every block is token 4(lane/16) + i
+    // tokens past the slice get no weight, and their V rows (whatever the
+    // LDS holds there) are replaced by zeros
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
+    // V^T element i of every block is token 4(lane/16) + i as well
 #pragma unroll
     for (int m = 0; m < kM; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) vt[m][i] = tok_row0 + i < tw1 ? vt[m][i] : (short)0;
   }
+  const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
+  if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
+    const float mn = fmaxf(st.m, tm);
+    const float alpha = exp2_fast(st.m - mn);  // 1 where the maximum stays, 0 from -inf
+    st.m = mn;
+    st.lsum *= alpha;
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < kM; ++m) st.acc[m] *= alpha;
+  }
+  float pr[4];
 #pragma unroll
-    for (int s = 0; s < kS; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[j][s], sc);
-    float s_[4];
+  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m + WeightBias<BF16>::log2);
+  st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  const Weights<BF16> wb = split_weights<BF16>(pr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
-    if (partial) {
-      // tokens past the slice get no weight
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
-    }
-    const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
-    if (__builtin_amdgcn_ballot_w64(tm > st.m[j]) != 0) {
-      const float mn = fmaxf(st.m[j], tm);
-      const float alpha = exp2_fast(st.m[j] - mn);  // 1 where the maximum stays, 0 from -inf
-      st.m[j] = mn;
-      st.lsum[j] *= alpha;
-#pragma unroll
-      for (int m = 0; m < kM; ++m) st.acc[j][m] *= alpha;
-    }
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m[j] + WeightBias<BF16>::log2);
-    st.lsum[j] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const Weights<BF16> wb = split_weights<BF16>(pr);
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-      const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
-      const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
-      st.acc[j][m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[j][m]);
-      if constexpr (BF16)  // k 4..7 of this one are zero on both sides
-        st.acc[j][m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
-                                           u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[j][m]);
-    }
+  for (int m = 0; m < kM; ++m) {
+    const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
+    const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
+    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[m]);
+    if constexpr (BF16)  // k 4..7 of this one are zero on both sides
+      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
+                                      u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[m]);
   }
 }
 
@@ -416,9 +412,9 @@ __device__ __forceinline__ void store4(uint16_t* o, f32x4 r, float inv) {
   *(u32x2*)o = u32x2{pack2<BF16>(r[0] * inv, r[1] * inv), pack2<BF16>(r[2] * inv, r[3] * inv)};
 }
 
-// Lane ownership of the results: lane l (column u = 16j + l%16 of block j,
-// rows 4(l/16)..+4 of each 16-dim block) speaks for query head u % G. Every
-// head has 16 NC / G column copies; the first `copies` of them (a power of
+// Lane ownership of the results: lane l (column u = l%16, rows 4(l/16)..+4
+// of each 16-dim block) speaks for query head u % G. Every head has 16 / G
+// column copies; the first `copies` of them (a power of
 // two, at most D/16) split the head's D/16 dim blocks into runs of nown =
 // (D/16) / copies, copy q taking blocks [q nown, (q+1) nown), so each (head,
 // dim) is written by exactly one lane. Kernels built FAST (G <= 4) use four
@@ -433,10 +429,10 @@ struct Owner {
 };
 
 template <bool FAST>
-__device__ __forceinline__ Owner make_owner(int u, int G, int NC, int kM) {
+__device__ __forceinline__ Owner make_owner(int u, int G, int kM) {
   int p2 = 4;
   if constexpr (!FAST) {
-    const int copies = 16 * NC / G;
+    const int copies = 16 / G;
     p2 = 1;
     while (2 * p2 <= copies && 2 * p2 <= kM) p2 *= 2;
   }
@@ -448,11 +444,10 @@ __device__ __forceinline__ Owner make_owner(int u, int G, int NC, int kM) {
   return o;
 }
 
-template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, int NC, bool FAST>
+template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
   static_assert(!KV8 || D == kD8, "the FP8 path is built for D = 128");
-  static_assert(!FAST || NC == 1, "FAST kernels serve G <= 4");
   using Gm = Geo<D>;
   constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
   constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
@@ -476,7 +471,8 @@ void pd_decode_kernel(const KArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = w % a.NH;  // KV head within the workgroup's group
   const int ts = w / a.NH;  // token slice
-  const int g = hg * a.NH + hl;
+  const int g = hg * a.NH + hl;  // virtual KV head
+  const int gk = g / a.HS;        // the physical KV head it reads
   const int row = lane >> 4;
   auto tile_buf = [&](int d) -> char* {
     char* base = d == 0 ? lds0 : d == 1 ? lds1 : lds2;
@@ -486,17 +482,16 @@ void pd_decode_kernel(const KArgs a) {
   const int t0 = p * a.P;
   const int tw0 = t0 + ts * a.Pw;
   const int bi0 = tw0 / BS;
-  // q as the MFMA B operand: column u = 16j + lane%16 -> head u % G, dims
+  // q as the MFMA B operand: column lane%16 -> head (lane%16) % G, dims
   // 32s + 8(lane/16) .. +8. Loaded before the block ids, so that waiting for
   // the ids (which the first K/V addresses need) also covers q, and no later
   // wait has to drain the tile loads.
-  u32x4 qb[NC][kS];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int hc = (16 * j + (lane & 15)) % G;
+  u32x4 qb[kS];
+  {
+    const int hc = (lane & 15) % G;
     const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G + hc) * D + 8 * row;
 #pragma unroll
-    for (int s = 0; s < kS; ++s) qb[j][s] = *(const u32x4*)(qp + 32 * s);
+    for (int s = 0; s < kS; ++s) qb[s] = *(const u32x4*)(qp + 32 * s);
   }
   // block ids of the wave's whole slice, fetched before the context length
   // is known (entries past the live ones are loaded but never used)
@@ -506,14 +501,11 @@ void pd_decode_kernel(const KArgs a) {
 #pragma unroll
   for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
 
-  WaveState<D, NC> st;
+  WaveState<D> st;
+  st.lsum = 0.f;
+  st.m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    st.lsum[j] = 0.f;
-    st.m[j] = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < kM; ++m) st.acc[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int m = 0; m < kM; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // loop bounds and block addresses in scalar registers
@@ -543,13 +535,13 @@ void pd_decode_kernel(const KArgs a) {
   const float c = a.scale_log2;
   constexpr uint32_t kRow = KV8 ? kRowBytes8 : Gm::kRowBytes;
   constexpr int kChunks = KV8 ? 8 : Gm::kChunks;  // 16-byte chunks per row as loaded
-  const uint32_t tok_bytes = a.Hkv * kRow;
+  const uint32_t tok_bytes = (a.Hkv / a.HS) * kRow;  // physical KV heads
   // global offsets of this lane's 16 bytes in load instruction 0 of a tile:
   // a 16-bit row takes C lanes (64 / C rows per instruction), chunks
   // rotated; an FP8 row takes 8 lanes (8 rows per instruction), in order
   const int lrow = lane / kChunks;
   const int lsl = lane % kChunks;
-  const uint32_t head_off = (uint32_t)lrow * tok_bytes + (uint32_t)g * kRow;
+  const uint32_t head_off = (uint32_t)lrow * tok_bytes + (uint32_t)gk * kRow;
   const uint32_t koff_g = head_off + (uint32_t)(KV8 ? lsl : (lsl - lrow + kChunks) % kChunks) * 16u;
   const uint32_t voff_g =
       head_off + (uint32_t)(KV8 ? lsl : (lsl - 2 * lrow + 2 * kChunks) % kChunks) * 16u;
@@ -631,13 +623,13 @@ void pd_decode_kernel(const KArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (j < nst) {
           const int tile0 = tw0 + kTileTok * j;
-          tile_compute<BF16, D, NC>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
+          tile_compute<BF16, D>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
                                     tile0 + kTileTok > tw1, c);
         }
       } else {
         if (j < nst) {
           const int tile0 = tw0 + kTileTok * j;
-          tile_compute<BF16, D, NC>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
+          tile_compute<BF16, D>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
                                     tile0 + kTileTok > tw1, c);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -652,97 +644,79 @@ void pd_decode_kernel(const KArgs a) {
   // tile buffers are reused below
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- per column block: the lane's head, its owned dim blocks gathered
-  // into o[j][0..nown), running maximum and weight sum
-  Owner own[NC];
-  f32x4 o[NC][kOwn];
-  float m_r[NC], l_r[NC];
+  // ---- the lane's head, its owned dim blocks gathered into o[0..nown),
+  // running maximum and weight sum
+  const Owner own = make_owner<FAST>(lane & 15, G, kM);
+  f32x4 o[kOwn];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    own[j] = make_owner<FAST>(16 * j + (lane & 15), G, NC, kM);
+  for (int k = 0; k < kOwn; ++k) {
+    o[k] = st.acc[k];
+    if constexpr (FAST) {
 #pragma unroll
-    for (int k = 0; k < kOwn; ++k) {
-      o[j][k] = st.acc[j][k];
-      if constexpr (FAST) {
+      for (int q = 1; q < 4; ++q)
+        if (own.copy == q) o[k] = st.acc[q * kOwn + k];
+    } else {
 #pragma unroll
-        for (int q = 1; q < 4; ++q)
-          if (own[j].copy == q) o[j][k] = st.acc[j][q * kOwn + k];
-      } else {
-#pragma unroll
-        for (int m = k + 1; m < kM; ++m)
-          if (m == own[j].block(k)) o[j][k] = st.acc[j][m];
-      }
+      for (int m = k + 1; m < kM; ++m)
+        if (m == own.block(k)) o[k] = st.acc[m];
     }
-    m_r[j] = st.m[j];
-    l_r[j] = sum_rows(st.lsum[j]);
   }
-  const int d_row = 4 * row;  // the lane's 4 dims within each 16-dim block
+  float m_r = st.m;
+  float l_r = sum_rows(st.lsum);
+  const int h = own.head;
+  const int nown = FAST ? kOwn : own.nown;
+  const int d0 = 16 * own.block(0) + 4 * row;  // first owned dim; runs of 4 every 16
 
   // ---- merge the NT slices of each head through LDS (a full 16-bit tile
   // per wave: the first tile buffer, or the converted-tile buffer of an FP8
-  // kernel; it holds G * (D + 2) floats per wave for G <= 16, and the
-  // planner keeps NT = 1 above that); slice 0 keeps the result
+  // kernel; it holds G * (D + 2) floats per wave as G <= 16); slice 0 keeps
+  // the result
   if (a.NT > 1) {
     __syncthreads();  // every wave is done with its tile buffers
     float* s_acc = (float*)(KV8 ? ldsc : lds0);  // [(w*G + h)*D + dim]
     float* s_m = s_acc + nw * G * D;             // [w*G + h]
     float* s_l = s_m + nw * G;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (!own[j].active) continue;
-      const int h = own[j].head;
-      float* dst = s_acc + (w * G + h) * D + 16 * own[j].block(0) + d_row;
+    if (own.active) {
 #pragma unroll
       for (int k = 0; k < kOwn; ++k)
-        if (FAST || k < own[j].nown) *(f32x4*)(dst + 16 * k) = o[j][k];
-      if (row == 0 && own[j].copy == 0) {
-        s_m[w * G + h] = m_r[j];
-        s_l[w * G + h] = l_r[j];
+        if (k < nown) *(f32x4*)(s_acc + (w * G + h) * D + d0 + 16 * k) = o[k];
+      if (row == 0 && own.copy == 0) {
+        s_m[w * G + h] = m_r;
+        s_l[w * G + h] = l_r;
       }
     }
     __syncthreads();
-    if (ts == 0) {
+    if (ts == 0 && own.active) {
+      float M = m_r;
+      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
+      float den = 0.f;
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        if (!own[j].active) continue;
-        const int h = own[j].head;
-        float M = m_r[j];
-        for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
-        float den = 0.f;
+      for (int k = 0; k < kOwn; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < a.NT; ++i) {
+        const int wi = (i * a.NH + hl) * G + h;
+        const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
+        den = fmaf(wt, s_l[wi], den);
 #pragma unroll
-        for (int k = 0; k < kOwn; ++k) o[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < a.NT; ++i) {
-          const int wi = (i * a.NH + hl) * G + h;
-          const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
-          den = fmaf(wt, s_l[wi], den);
-          const float* src = s_acc + wi * D + 16 * own[j].block(0) + d_row;
+        for (int k = 0; k < kOwn; ++k) {
+          if (k >= nown) continue;
+          const f32x4 x = *(const f32x4*)(s_acc + wi * D + d0 + 16 * k);
 #pragma unroll
-          for (int k = 0; k < kOwn; ++k) {
-            if (!FAST && k >= own[j].nown) continue;
-            const f32x4 x = *(const f32x4*)(src + 16 * k);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[j][k][e] = fmaf(wt, x[e], o[j][k][e]);
-          }
+          for (int e = 0; e < 4; ++e) o[k][e] = fmaf(wt, x[e], o[k][e]);
         }
-        m_r[j] = M;
-        l_r[j] = den;
       }
+      m_r = M;
+      l_r = den;
     }
   }
-  const bool owner = ts == 0;
+  const bool owner = ts == 0 && own.active;
 
   if constexpr (!SPLIT) {
     if (owner) {
+      uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
+      const float inv = a.out_scale / l_r;
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        if (!own[j].active) continue;
-        uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + own[j].head) * D +
-                       16 * own[j].block(0) + d_row;
-        const float inv = a.out_scale / l_r[j];
-#pragma unroll
-        for (int k = 0; k < kOwn; ++k)
-          if (FAST || k < own[j].nown) store4<BF16>(op + 16 * k, o[j][k], inv);
-      }
+      for (int k = 0; k < kOwn; ++k)
+        if (k < nown) store4<BF16>(op + 16 * k, o[k], inv);
     }
     return;
   } else {
@@ -752,24 +726,19 @@ void pd_decode_kernel(const KArgs a) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o_part + slot0 * D, rows_bytes);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse_part + slot0, (uint32_t)G * a.S * 4);
     if (owner) {
+      // the raw buffer builtins move 32-bit words: floats go through bit casts
+      const float inv = 1.0f / l_r;
+      const uint32_t off = ((uint32_t)(h * a.S + p) * D + d0) * 4;
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        if (!own[j].active) continue;
-        const int h = own[j].head;
-        // the raw buffer builtins move 32-bit words: floats go through bit casts
-        const float inv = 1.0f / l_r[j];
-        const uint32_t off = ((uint32_t)(h * a.S + p) * D + 16 * own[j].block(0) + d_row) * 4;
-#pragma unroll
-        for (int k = 0; k < kOwn; ++k)
-          if (FAST || k < own[j].nown)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[j][k] * inv), ro,
-                                                   off + 64 * k, 0, kCoherent);
-        if (row == 0 && own[j].copy == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __builtin_bit_cast(uint32_t, m_r[j] + __builtin_amdgcn_logf(l_r[j]) -
-                                               WeightBias<BF16>::log2),
-              rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
-      }
+      for (int k = 0; k < kOwn; ++k)
+        if (k < nown)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[k] * inv), ro,
+                                                 off + 64 * k, 0, kCoherent);
+      if (row == 0 && own.copy == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r) -
+                                             WeightBias<BF16>::log2),
+            rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
     }
     // the stores are complete (and past every non-coherent cache) before the
     // counter moves
@@ -785,68 +754,65 @@ void pd_decode_kernel(const KArgs a) {
       s_last = last;
     }
     __syncthreads();
-    if (!s_last || !owner) return;
+    if (!s_last || !own.active) return;
 
-    // ---- last workgroup: LSE merge over the n_live partitions, in order,
-    // two owned dim blocks per pass (one pass at G <= 4, D = 128)
+    // ---- last workgroup: LSE merge over the n_live partitions, in order.
+    // It reads only the published partials, so the NT slice waves of a head
+    // share it: wave ts merges its share of the lane's owned dim blocks, two
+    // per pass (at G <= 4, D = 128: one block per wave with NT = 2).
     constexpr int kBatch = 8;
+    uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
+    const int per = (nown + a.NT - 1) / a.NT;
+    const int kb = ts * per, ke = min(nown, kb + per);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (!own[j].active) continue;
-      const int h = own[j].head;
-      uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D +
-                     16 * own[j].block(0) + d_row;
+    for (int k0 = 0; k0 < kOwn; k0 += 2) {
+      if (kb + k0 >= ke) break;
+      const bool two = kb + k0 + 1 < ke;
+      const uint32_t dim0 = (uint32_t)(d0 + 16 * (kb + k0));
+      float M = -INFINITY, den = 0.f;
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < n_live; i0 += kBatch) {
+        float lse[kBatch];
+        f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
-      for (int k0 = 0; k0 < kOwn; k0 += 2) {
-        const int nown = FAST ? kOwn : own[j].nown;
-        if (k0 >= nown) break;
-        const bool two = k0 + 1 < nown;
-        const uint32_t dim0 = (uint32_t)(16 * own[j].block(k0) + d_row);
-        float M = -INFINITY, den = 0.f;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        for (int i0 = 0; i0 < n_live; i0 += kBatch) {
-          float lse[kBatch];
-          f32x4 x0[kBatch], x1[kBatch];
+        for (int u = 0; u < kBatch; ++u) {
+          // partitions past n_live read zeros and are skipped below
+          const bool ok = i0 + u < n_live;
+          const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
+          const uint32_t off = ok ? (slot * D + dim0) * 4 : kOutOfBlock;
+          x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
+                                                                                  kCoherent));
+          x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                ro, ok && two ? off + 64 : kOutOfBlock, 0,
+                                                kCoherent));
+          lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
+        }
+        float bm = M;
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            // partitions past n_live read zeros and are skipped below
-            const bool ok = i0 + u < n_live;
-            const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
-            const uint32_t off = ok ? (slot * D + dim0) * 4 : kOutOfBlock;
-            x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
-                                                                                    kCoherent));
-            x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  ro, ok && two ? off + 64 : kOutOfBlock, 0,
-                                                  kCoherent));
-            lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                   rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
-          }
-          float bm = M;
+        for (int u = 0; u < kBatch; ++u)
+          if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
+        const float alpha = exp2_fast(M - bm);  // 0 on the first batch
+        den *= alpha;
+        acc0 *= alpha;
+        acc1 *= alpha;
+        M = bm;
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u)
-            if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
-          const float alpha = exp2_fast(M - bm);  // 0 on the first batch
-          den *= alpha;
-          acc0 *= alpha;
-          acc1 *= alpha;
-          M = bm;
+        for (int u = 0; u < kBatch; ++u) {
+          if (i0 + u < n_live) {
+            const float wt = exp2_fast(lse[u] - M);
+            den += wt;
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            if (i0 + u < n_live) {
-              const float wt = exp2_fast(lse[u] - M);
-              den += wt;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
-                acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
-              }
+            for (int e = 0; e < 4; ++e) {
+              acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
+              acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
             }
           }
         }
-        const float inv = a.out_scale / den;
-        store4<BF16>(op + 16 * k0, acc0, inv);
-        if (two) store4<BF16>(op + 16 * (k0 + 1), acc1, inv);
       }
+      const float inv = a.out_scale / den;
+      store4<BF16>(op + 16 * (kb + k0), acc0, inv);
+      if (two) store4<BF16>(op + 16 * (kb + k0 + 1), acc1, inv);
     }
   }
 }
@@ -858,48 +824,46 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-template <bool BF16, int BS, bool SPLIT, bool KV8, int D, int NC, bool FAST>
+template <bool BF16, int BS, bool SPLIT, bool KV8, int D, bool FAST>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   void* args[] = {(void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
   const void* f = nw <= 4
-      ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, NC, FAST>
-      : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8, KV8, D, NC, FAST>;
+      ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, FAST>
+      : (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 8, KV8, D, FAST>;
   return hipLaunchKernel(f, grid, dim3(nw * 64), args, 0, st);
 }
 
-template <bool BF16, bool SPLIT, bool KV8, int D, int NC, bool FAST>
+template <bool BF16, bool SPLIT, bool KV8, int D, bool FAST>
 hipError_t pick_block(const KArgs& ka, dim3 grid, int bs, int nw, hipStream_t st) {
-  return bs == 32 ? launch_decode<BF16, 32, SPLIT, KV8, D, NC, FAST>(ka, grid, nw, st)
-                  : launch_decode<BF16, 16, SPLIT, KV8, D, NC, FAST>(ka, grid, nw, st);
+  return bs == 32 ? launch_decode<BF16, 32, SPLIT, KV8, D, FAST>(ka, grid, nw, st)
+                  : launch_decode<BF16, 16, SPLIT, KV8, D, FAST>(ka, grid, nw, st);
 }
 
-template <bool KV8, int D, int NC, bool FAST>
+template <bool KV8, int D, bool FAST>
 hipError_t pick_dtype(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
                       hipStream_t st) {
   if (bf16)
-    return split ? pick_block<true, true, KV8, D, NC, FAST>(ka, grid, bs, nw, st)
-                 : pick_block<true, false, KV8, D, NC, FAST>(ka, grid, bs, nw, st);
-  return split ? pick_block<false, true, KV8, D, NC, FAST>(ka, grid, bs, nw, st)
-               : pick_block<false, false, KV8, D, NC, FAST>(ka, grid, bs, nw, st);
+    return split ? pick_block<true, true, KV8, D, FAST>(ka, grid, bs, nw, st)
+                 : pick_block<true, false, KV8, D, FAST>(ka, grid, bs, nw, st);
+  return split ? pick_block<false, true, KV8, D, FAST>(ka, grid, bs, nw, st)
+               : pick_block<false, false, KV8, D, FAST>(ka, grid, bs, nw, st);
 }
 
-// Instances: 16-bit caches at D = 64 and 128 with one column block (G <= 4
-// FAST, or any G <= 16) or two (G <= 32); FP8 caches at D = 128, G <= 16.
+// Instances: D = 64 and 128 for 16-bit caches, D = 128 for FP8 caches; each
+// with a compile-time epilogue for G <= 4 query heads per virtual KV head
+// (FAST) and a general one.
 hipError_t pick_geometry(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
-                         bool kv8, int D, int G, hipStream_t st) {
-  const bool fast = G <= 4;
+                         bool kv8, int D, hipStream_t st) {
+  const bool fast = ka.G <= 4;
   if (kv8)
-    return fast ? pick_dtype<true, 128, 1, true>(ka, grid, bs, nw, bf16, split, st)
-                : pick_dtype<true, 128, 1, false>(ka, grid, bs, nw, bf16, split, st);
-  if (D == 64) {
-    if (G > 16) return pick_dtype<false, 64, 2, false>(ka, grid, bs, nw, bf16, split, st);
-    return fast ? pick_dtype<false, 64, 1, true>(ka, grid, bs, nw, bf16, split, st)
-                : pick_dtype<false, 64, 1, false>(ka, grid, bs, nw, bf16, split, st);
-  }
-  if (G > 16) return pick_dtype<false, 128, 2, false>(ka, grid, bs, nw, bf16, split, st);
-  return fast ? pick_dtype<false, 128, 1, true>(ka, grid, bs, nw, bf16, split, st)
-              : pick_dtype<false, 128, 1, false>(ka, grid, bs, nw, bf16, split, st);
+    return fast ? pick_dtype<true, 128, true>(ka, grid, bs, nw, bf16, split, st)
+                : pick_dtype<true, 128, false>(ka, grid, bs, nw, bf16, split, st);
+  if (D == 64)
+    return fast ? pick_dtype<false, 64, true>(ka, grid, bs, nw, bf16, split, st)
+                : pick_dtype<false, 64, false>(ka, grid, bs, nw, bf16, split, st);
+  return fast ? pick_dtype<false, 128, true>(ka, grid, bs, nw, bf16, split, st)
+              : pick_dtype<false, 128, false>(ka, grid, bs, nw, bf16, split, st);
 }
 
 }  // namespace
@@ -923,8 +887,10 @@ int32_t launch(const Launch& l) {
     ka.o_part = (float*)(ws + kCounterBytes);
     ka.lse_part = (float*)(ws + kCounterBytes + partials_bytes(l.shape, l.plan));
   }
-  ka.Hkv = l.shape.Hkv;
-  ka.G = l.shape.Hq / l.shape.Hkv;
+  const int hs = l.plan.head_split;
+  ka.Hkv = l.shape.Hkv * hs;
+  ka.HS = hs;
+  ka.G = l.shape.Hq / ka.Hkv;
   ka.MB = l.shape.max_blocks_per_seq;
   ka.S = l.plan.splits;
   ka.P = l.plan.partition_tokens;
@@ -935,20 +901,19 @@ int32_t launch(const Launch& l) {
   ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
                  (l.kv_fp8 ? kRowBytes8 : 2u * (uint32_t)l.shape.D);
-  const dim3 grid(l.plan.splits, l.shape.Hkv / l.plan.heads_per_group, l.shape.B);
+  const dim3 grid(l.plan.splits, ka.Hkv / l.plan.heads_per_group, l.shape.B);
   const int nw = l.plan.heads_per_group * l.plan.slices;
-  const int nc = ka.G > 16 ? 2 : 1;
   // each wave owns a tile's bytes of every tile buffer of its workgroup; the
-  // slice merge needs G * (D + 2) floats of them per wave
-  if (nw < 1 || nw > kMaxWaves || l.shape.Hkv % l.plan.heads_per_group != 0 ||
-      ka.G > kMaxGroup || (l.shape.D != 64 && l.shape.D != 128) ||
-      (l.kv_fp8 && (l.shape.D != kD8 || nc != 1)) || (nc > 1 && l.plan.slices > 1))
+  // slice merge needs G * (D + 2) floats of them per wave, so G <= 16
+  if (nw < 1 || nw > kMaxWaves || hs < 1 || ka.Hkv % l.plan.heads_per_group != 0 ||
+      ka.G * ka.Hkv != l.shape.Hq || ka.G > 16 || (l.shape.D != 64 && l.shape.D != 128) ||
+      (l.kv_fp8 && l.shape.D != kD8))
     return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;
   const bool bf16 = l.shape.dtype == PD_DTYPE_BF16;
   const hipError_t e = pick_geometry(ka, grid, l.shape.block_size, nw, bf16, split, l.kv_fp8,
-                                     l.shape.D, ka.G, st);
+                                     l.shape.D, st);
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

@@ -21,6 +21,7 @@ constexpr int64_t kTileTok = 16;      // tokens per K/V tile of a wave
 constexpr int64_t kMinSplitTiles = 2;  // tiles per wave a split must leave
 constexpr int64_t kNoSplitTiles = 4;   // tiles per wave below which a split never pays
 constexpr int64_t kPairTiles = 16;     // tiles per wave from which split KV heads go in pairs
+constexpr int64_t kMergeRows = 128;    // most (query head, partition) rows a head's merge reads
 constexpr int64_t kMaxSplits = 1 << 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -47,9 +48,9 @@ int32_t check_shape(const Shape& s) {
 // block_size tokens) into S partitions of P tokens, each served by one
 // workgroup of 4 waves per group of NH KV heads; a wave covers one slice of
 // Pw tokens (block aligned, at most 256 blocks) of one head, in tiles of 16.
-// Slices of a head merge in LDS, partitions merge across workgroups. With
-// more than 16 query heads per KV head (MQA) a workgroup has one slice per
-// head and the split rule fills the GPU with partitions instead.
+// Slices of a head merge in LDS, partitions merge across workgroups. A KV
+// head with more than 16 query heads (MQA) counts as HS virtual KV heads,
+// paired in a workgroup when HS is even.
 //
 // The rule was fitted to sweeps of every (NH, NT, S) on an MI355X over the
 // decode workloads (batch 1..64, contexts 16..4,096, block sizes 16/32):
@@ -63,21 +64,28 @@ int32_t check_shape(const Shape& s) {
 //     trips), so it is not used when a wave would have at most
 //     kNoSplitTiles tiles without it;
 //   * a split call whose waves still have kPairTiles or more tiles each
-//     does better with KV heads in pairs and twice the partitions.
+//     does better with KV heads in pairs and twice the partitions;
+//   * with more than 4 query heads per wave the merge of a head reads
+//     G/HS x S partial rows, so S is capped at kMergeRows / (G/HS).
 // A forced S fixes P instead and cuts it into up to NT slices.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
   const int64_t cap = (int64_t)s.max_blocks_per_seq * bs;  // longest possible context
-  const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * s.Hkv;
+  // a wave serves at most 16 query heads: split each KV head into the fewest
+  // virtual heads of equal size that respects that
+  const int64_t G = s.Hq / s.Hkv;
+  int64_t hs = 1;
+  while (G % hs != 0 || G / hs > 16) ++hs;
+  const int64_t hkv = s.Hkv * hs;  // virtual KV heads
+  const int64_t units = (int64_t)(s.B > 0 ? s.B : 1) * hkv;
   const int64_t pw_max = kMaxWaveBlocks * bs;
-  const bool pairs = s.Hkv % 2 == 0;
-  // more than 16 query heads per KV head: the slice merge would not fit a
-  // wave's LDS share, so one slice per workgroup (partitions take the rest)
-  const bool one_slice = s.Hq / s.Hkv > 16;
-  int64_t nh = pairs && units >= 2 * kFillWaves / kWaves ? 2 : 1;
-  int64_t nt = one_slice ? 1 : kWaves / nh;
+  // virtual heads of one KV head pair up, so both waves of a pair read the
+  // same blocks
+  const bool pairs = hkv % 2 == 0;
+  int64_t nh = pairs && (hs % 2 == 0 || units >= 2 * kFillWaves / kWaves) ? 2 : 1;
+  int64_t nt = kWaves / nh;
   int64_t P;
   if (requested_splits > 0) {
     const int64_t want = requested_splits > kMaxSplits ? kMaxSplits : requested_splits;
@@ -88,10 +96,14 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
       S = ceil_div(kFillWaves, units * nt);
       const int64_t s_max = cap / (nt * kMinSplitTiles * kTileTok);
       if (S > s_max) S = s_max;
+      // the merge of a virtual head reads G/HS x S partial rows; with many
+      // query heads per wave, fewer partitions
+      const int64_t g_wave = G / hs;
+      if (g_wave > 4 && S * g_wave > kMergeRows) S = kMergeRows / g_wave;
       if (S < 1) S = 1;
       if (S > 1 && pairs && nh == 1 && cap / (S * nt) >= kPairTiles * kTileTok) {
         nh = 2;
-        nt = one_slice ? 1 : kWaves / nh;
+        nt = kWaves / nh;
         S *= 2;
       }
     }
@@ -101,10 +113,9 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   if (PD_FORCE_NT > 0) nt = PD_FORCE_NT;
 #endif
 #ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
-  if (PD_FORCE_NH > 0 && s.Hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
+  if (PD_FORCE_NH > 0 && hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
 #endif
   if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
-  if (one_slice) nt = 1;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
   int64_t pw = round_up(ceil_div(P, nt), bs);
   if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more
@@ -115,12 +126,14 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
   const int64_t S = ceil_div(cap, P);
   if (S > kMaxSplits) return PD_ERR_SHAPE;
   // the split path keeps one arrival counter per (sequence, head group)
-  if (S > 1 && (int64_t)s.B * (s.Hkv / nh) > kMaxCounters) return PD_ERR_UNSUPPORTED;
+  if (S > 1 && (int64_t)s.B * (hkv / nh) > kMaxCounters) return PD_ERR_UNSUPPORTED;
+  if (hkv > 65535) return PD_ERR_SHAPE;  // grid y
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
   plan->heads_per_group = (int32_t)nh;
   plan->slices = (int32_t)nt;
   plan->wave_tokens = (int32_t)pw;
+  plan->head_split = (int32_t)hs;
   return PD_OK;
 }
 

@@ -311,3 +311,12 @@ def large(seed: int = 0, B: int = 64, L: int = 4096, kv_dtype: str = "") -> Case
     MB = L // bs
     return make_case(f"large_B{B}_L{L}{_suffix(kv_dtype)}", B, L, dtype="bf16", block_size=bs,
                      seed=seed, pool_blocks=B * MB, max_blocks_per_seq=MB, kv_dtype=kv_dtype)
+
+
+def geometry(Hq: int, Hkv: int, D: int, B: int, L: int, seed: int = 0, dtype: str = "bf16",
+             block_size: int = 16) -> Case:
+    """B sequences of L tokens at another head geometry (the pages' 14/2 D64
+    route, MQA 32/1, ...), N(0, 1) inputs, scale 1/sqrt(D) rounded to float32."""
+    return make_case(f"geom_{Hq}x{Hkv}_D{D}_B{B}_L{L}", B, L, dtype=dtype, block_size=block_size,
+                     Hq=Hq, Hkv=Hkv, D=D, seed=seed,
+                     scale=float(np.float32(1.0 / math.sqrt(D))))
