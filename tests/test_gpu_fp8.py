@@ -155,3 +155,14 @@ def test_fp8_binding_rejects_mismatched_inputs():
     with pytest.raises(pd.PagedDecodeError) as e:
         pd.paged_decode_attention_fp8(q, k, v, bt, cl, k_scale=0.0, v_scale=1.0)
     assert e.value.code == 10
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(14, 2), (32, 1), (8, 8), (64, 8), (20, 1)])
+@pytest.mark.parametrize("splits", [None, 3])
+def test_fp8_other_group_sizes(Hq, Hkv, splits):
+    # odd groups, MQA (two virtual KV heads), MHA, G = 8 and 20 at D = 128
+    lens = [1, 37, 700, 1024, 513, 0]
+    c = workloads.make_case(f"fp8_{Hq}x{Hkv}", len(lens), lens, dtype="bf16", block_size=16,
+                            Hq=Hq, Hkv=Hkv, seed=90 + Hq, kv_dtype="fp8")
+    note(f"{c.describe()} S={splits}")
+    check_case(c, num_splits=splits, what=f"{c.name} S={splits}")
