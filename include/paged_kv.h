@@ -42,7 +42,7 @@ int32_t rope_cos_sin_table(float* table, int32_t max_position, int32_t rotary_di
                            void* stream);
 
 /*
- * RoPE + paged KV-cache write (Loom Kernels home page, operator list: "RoPE +
+ * RoPE + paged KV-cache write (Loom Kernels home page, "Supported now": "RoPE +
  * paged-KV write", a packed Q/K rotation and a write into the native cache;
  * benchmark page, "What the ratios mean": 1-512 tokens). For each token
  * t < T with m = positions[t] and s = slot_mapping[t]:

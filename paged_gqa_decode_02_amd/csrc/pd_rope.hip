@@ -1,6 +1,6 @@
 // RoPE + paged KV-cache write, and the cos/sin table it reads, for gfx950.
 //
-// Operation (Loom Kernels home page, operator list: "RoPE + paged-KV write",
+// Operation (Loom Kernels home page, "Supported now": "RoPE + paged-KV write",
 // a packed Q/K rotation with a write into the native cache; it is the step
 // that fills the cache the paged decode reads): for token t at position
 // m = positions[t], every query and key head vector is rotated pair by pair,
