@@ -1,10 +1,12 @@
-"""GPU parity at other KV-head counts with four query heads per KV head.
+"""GPU parity at other head geometries.
 
-The kernel serves any Hkv with Hq = 4 * Hkv and D = 128: KV heads pair up in
-a workgroup only when Hkv is even, and the planner's choices change with
-B * Hkv. These cases cover one, two, three, four and sixteen KV heads, with
-ragged contexts that leave partial tiles, both dtypes and block sizes, the
-planned split count and forced ones.
+First, other KV-head counts with four query heads per KV head: KV heads pair
+up in a workgroup only when Hkv is even, and the planner's choices change
+with B * Hkv (one, two, three, four and sixteen KV heads). Then other group
+sizes and head dims: the Qwen2.5-style 14/2 at D 64, MQA 32/1 (two virtual
+KV heads of 16), MHA (G = 1), G = 2, 3, 5, 8, 16, 20 and D 64 at 32/8. All
+with ragged (and empty) contexts that leave partial tiles, both dtypes and
+block sizes, the planned split count and forced ones.
 """
 import pytest
 import torch
