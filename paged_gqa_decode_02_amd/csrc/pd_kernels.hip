@@ -200,10 +200,24 @@ struct Geo {
   static constexpr int kBlocks = D / 16;  // 16-dim output blocks (PV MFMAs)
 };
 static_assert(Geo<128>::kLdsTile == 8960 && Geo<64>::kLdsTile == 4480, "tile layout");
-// An FP8 cache (D = 128) lands in a plain staging tile (16 rows of 128 bytes
-// for K, then for V) and is converted into the 16-bit layout above before
-// use.
-constexpr uint32_t kStage8 = 2 * kTileTok * kRowBytes8;  // 4096
+// An FP8 cache (D = 128) stays in its codes in LDS: a tile is 16 rows of 128
+// bytes for K, then for V, as two 1 KiB groups each (8 rows per load
+// instruction, 8 lanes per row), groups 1040 bytes apart; chunk c of row r
+// sits at slot (c + (r & ~1)) mod 8. The tile path reads it in operand order
+// and widens in registers:
+//   K: ds_read_b64 of token lane%16, dims 32s + 8(lane/16) .. +8;
+//   V: ds_read_b64_tr_b8, source lane 16g + a + 2k giving token 4g + k%4,
+//      dims 16(m + k/4) + 8a .. +8, so that lane l receives dim 16m +
+//      l%16 of tokens 4(l/16)..+4 (bytes 0..3) and dim 16(m+1) + l%16 of
+//      the same tokens (bytes 4..7): two 16-dim blocks per read.
+// Within each half-wave these reads touch 32 distinct 8-byte bank slots
+// (no bank conflicts; measured with the LDS conflict counter).
+constexpr uint32_t kGroup8 = 1024 + 16;
+constexpr uint32_t kKTile8 = 2 * kGroup8;
+constexpr uint32_t kStage8 = 4 * kGroup8;  // 4160
+// the slice merge's per-wave scratch: G * (D + 2) floats for G <= 16
+template <int D>
+constexpr uint32_t merge_bytes() { return 16u * (D + 2) * 4u; }
 
 // Tile buffers per wave (tiles in flight while one is computed: buffers - 1),
 // as many as fit the 160 KiB of LDS for the workgroup size, up to PD_NBUF.
@@ -215,13 +229,13 @@ template <int D, bool KV8>
 constexpr uint32_t stage_bytes() { return KV8 ? kStage8 : Geo<D>::kLdsTile; }
 template <int D, bool KV8>
 constexpr int tile_buffers(int nw) {
-  return PD_NBUF >= 3 &&
-                 3 * nw * stage_bytes<D, KV8>() + (KV8 ? nw * Geo<kD8>::kLdsTile : 0) <= kLdsBytes
-             ? 3 : 2;
+  return PD_NBUF >= 3 && 3 * nw * stage_bytes<D, KV8>() <= kLdsBytes ? 3 : 2;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr_t;
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -293,20 +307,16 @@ struct WaveState {
 //     lane's 4 tokens, twice) and B = those tokens' weights (hi in k 0..3, lo
 //     in k 4..7), which is the layout the scores came out in; for bf16 a
 //     second one adds the third weight term.
+// The math of one tile: ka[s] the K tile as score-MFMA A operands, v01/v23
+// the V^T operand of each 16-dim block (16-bit values of tokens 4(lane/16)
+// + 0,1 and + 2,3 for dim lane%16 of the block).
 template <bool BF16, int D>
-__device__ __forceinline__ void tile_compute(WaveState<D>& st, const char* kt,
-                                             const u32x4 (&qb)[Geo<D>::kSteps],
-                                             const uint32_t (&koff)[Geo<D>::kSteps],
-                                             const uint32_t (&voff)[Geo<D>::kBlocks],
-                                             int tok_row0, int tw1, bool partial, float c) {
+__device__ __forceinline__ void tile_math(WaveState<D>& st, const u32x4 (&ka)[Geo<D>::kSteps],
+                                          uint32_t (&v01)[Geo<D>::kBlocks],
+                                          uint32_t (&v23)[Geo<D>::kBlocks],
+                                          const u32x4 (&qb)[Geo<D>::kSteps], int tok_row0,
+                                          int tw1, bool partial, float c) {
   constexpr int kS = Geo<D>::kSteps, kM = Geo<D>::kBlocks;
-  u32x4 ka[kS];
-#pragma unroll
-  for (int s = 0; s < kS; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
-  v4i16_t vt[kM];
-#pragma unroll
-  for (int m = 0; m < kM; ++m)
-    vt[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr_t)(kt + voff[m]));
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kS; ++s) sc = mfma_16x16x32<BF16>(ka[s], qb[s], sc);
@@ -314,15 +324,18 @@ __device__ __forceinline__ void tile_compute(WaveState<D>& st, const char* kt,
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_[i] = sc[i] * c;
   if (partial) {
-    // tokens past the slice get no weight, and their V rows (whatever the
+    // tokens past the slice get no weight, and their V values (whatever the
     // LDS holds there) are replaced by zeros
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_[i] = tok_row0 + i < tw1 ? s_[i] : -INFINITY;
-    // V^T element i of every block is token 4(lane/16) + i as well
+    const uint32_t keep01 = (tok_row0 < tw1 ? 0xffffu : 0u) | (tok_row0 + 1 < tw1 ? 0xffff0000u : 0u);
+    const uint32_t keep23 =
+        (tok_row0 + 2 < tw1 ? 0xffffu : 0u) | (tok_row0 + 3 < tw1 ? 0xffff0000u : 0u);
 #pragma unroll
-    for (int m = 0; m < kM; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vt[m][i] = tok_row0 + i < tw1 ? vt[m][i] : (short)0;
+    for (int m = 0; m < kM; ++m) {
+      v01[m] &= keep01;
+      v23[m] &= keep23;
+    }
   }
   const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
   if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
@@ -340,56 +353,73 @@ __device__ __forceinline__ void tile_compute(WaveState<D>& st, const char* kt,
   const Weights<BF16> wb = split_weights<BF16>(pr);
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
-    const uint32_t v01 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 0, 1));
-    const uint32_t v23 = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[m], vt[m], 2, 3));
-    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, v01, v23}, wb.hi_lo, st.acc[m]);
+    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01[m], v23[m], v01[m], v23[m]}, wb.hi_lo, st.acc[m]);
     if constexpr (BF16)  // k 4..7 of this one are zero on both sides
-      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01, v23, 0u, 0u},
+      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01[m], v23[m], 0u, 0u},
                                       u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[m]);
   }
 }
 
-// FP8 staging tile -> 16-bit tile layout (D = 128). Lane l takes 16-byte chunks
-// 64i + l (i < 2) of the K and of the V staging tile: token c/8, dims
-// 16(c%8) .. +16; their 16 codes become two 16-byte chunks of 8 values each,
-// written where the 16-bit layout keeps them. E4M3FN values are exact in
-// both bf16 and f16, so the conversion (scale 1) loses nothing.
+// One 16-bit tile, already in LDS at kt (K) and kt + kKTile (V): its LDS
+// reads go out first (K in operand order, V^T through the transposing read),
+// then the math.
+template <bool BF16, int D>
+__device__ __forceinline__ void tile_compute(WaveState<D>& st, const char* kt,
+                                             const u32x4 (&qb)[Geo<D>::kSteps],
+                                             const uint32_t (&koff)[Geo<D>::kSteps],
+                                             const uint32_t (&voff)[Geo<D>::kBlocks],
+                                             int tok_row0, int tw1, bool partial, float c) {
+  constexpr int kS = Geo<D>::kSteps, kM = Geo<D>::kBlocks;
+  u32x4 ka[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s) ka[s] = *(const u32x4*)(kt + koff[s]);
+  uint32_t v01[kM], v23[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    const v4i16_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr_t)(kt + voff[m]));
+    v01[m] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt, vt, 0, 1));
+    v23[m] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt, vt, 2, 3));
+  }
+  tile_math<BF16, D>(st, ka, v01, v23, qb, tok_row0, tw1, partial, c);
+}
+
+// Two E4M3FN codes (bytes 2 HI, 2 HI + 1 of x) -> two 16-bit values, exact.
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t widen_pair(uint32_t x) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+}
+
+typedef __attribute__((address_space(3))) v2i32_t* lds_v2i32_ptr_t;
+
+// One 16-token FP8 tile (D = 128) at kt: K codes widened into the score
+// MFMA's A operand, V^T codes (two 16-dim blocks per transposing read)
+// widened into the PV operand; then the same math as the 16-bit tile.
 template <bool BF16>
-__device__ __forceinline__ void convert_fp8_tile(const char* st, char* kt, int lane) {
+__device__ __forceinline__ void tile_compute_fp8(WaveState<kD8>& st, const char* kt,
+                                                 const u32x4 (&qb)[4], const uint32_t (&koff)[4],
+                                                 const uint32_t (&voff)[4], int tok_row0,
+                                                 int tw1, bool partial, float c) {
+  u32x4 ka[4];
 #pragma unroll
-  for (int tv = 0; tv < 2; ++tv) {
+  for (int s = 0; s < 4; ++s) {
+    const u32x2_t x = *(const u32x2_t*)(kt + koff[s]);
+    ka[s] = u32x4{widen_pair<BF16, false>(x[0]), widen_pair<BF16, true>(x[0]),
+                  widen_pair<BF16, false>(x[1]), widen_pair<BF16, true>(x[1])};
+  }
+  uint32_t v01[8], v23[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = 64 * i + lane;
-      const int t = c >> 3, c8 = c & 7, n = t >> 2, r = t & 3;
-      const u32x4 x = *(const u32x4*)(st + tv * (kStage8 / 2) + 16 * c);
-      u32x4 y[2];
+  for (int mm = 0; mm < 4; ++mm) {
+    const v2i32_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr_t)(kt + voff[mm]));
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t lo, hi;
-        if constexpr (BF16) {
-          lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
-          hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
-        } else {
-          lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], 1.0f, false));
-          hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[w], 1.0f, true));
-        }
-        y[w >> 1][2 * (w & 1)] = lo;
-        y[w >> 1][2 * (w & 1) + 1] = hi;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        using Gm = Geo<kD8>;
-        const int chunk = 2 * c8 + h;  // 16-bit chunk (8 dims) of the row
-        const uint32_t off = tv == 0
-            ? (uint32_t)n * Gm::kKGroup + (uint32_t)r * Gm::kRowBytes +
-                  16u * (uint32_t)((chunk + r) & 15)
-            : Gm::kKTile + (uint32_t)n * Gm::kVGroup + (uint32_t)r * Gm::kRowBytes +
-                  16u * (uint32_t)((chunk + 2 * r) & 15);
-        *(u32x4*)(kt + off) = y[h];
-      }
+    for (int u = 0; u < 2; ++u) {
+      v01[2 * mm + u] = widen_pair<BF16, false>((uint32_t)x[u]);
+      v23[2 * mm + u] = widen_pair<BF16, true>((uint32_t)x[u]);
     }
   }
+  tile_math<BF16, kD8>(st, ka, v01, v23, qb, tok_row0, tw1, partial, c);
 }
 
 // Block id number idx (< 256, wave-uniform) of the wave's range.
@@ -457,10 +487,10 @@ void pd_decode_kernel(const KArgs a) {
   constexpr uint32_t kStage = stage_bytes<D, KV8>();
   // one array per tile buffer, so the compiler can wait for exactly the
   // loads of the buffer about to be read
-  __shared__ __align__(16) char lds0[NW * kStage];
+  // the first also holds the slice merge's scratch after the loop
+  __shared__ __align__(16) char lds0[NW * (kStage > merge_bytes<D>() ? kStage : merge_bytes<D>())];
   __shared__ __align__(16) char lds1[NW * kStage];
   __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kStage : 16];
-  __shared__ __align__(16) char ldsc[KV8 ? NW * Gm::kLdsTile : 16];  // converted FP8 tile
   const int p = blockIdx.x;
   const int hg = blockIdx.y;
   const int b = blockIdx.z;
@@ -542,11 +572,27 @@ void pd_decode_kernel(const KArgs a) {
   const int lrow = lane / kChunks;
   const int lsl = lane % kChunks;
   const uint32_t head_off = (uint32_t)lrow * tok_bytes + (uint32_t)gk * kRow;
-  const uint32_t koff_g = head_off + (uint32_t)(KV8 ? lsl : (lsl - lrow + kChunks) % kChunks) * 16u;
+  const uint32_t koff_g =
+      head_off + (uint32_t)(KV8 ? (lsl - (lrow & ~1) + 8) % 8 : (lsl - lrow + kChunks) % kChunks) *
+                     16u;
   const uint32_t voff_g =
-      head_off + (uint32_t)(KV8 ? lsl : (lsl - 2 * lrow + 2 * kChunks) % kChunks) * 16u;
-  // LDS offsets of the two read patterns (see the tile layout above)
+      head_off +
+      (uint32_t)(KV8 ? (lsl - (lrow & ~1) + 8) % 8 : (lsl - 2 * lrow + 2 * kChunks) % kChunks) * 16u;
+  // LDS offsets of the two read patterns (see the tile layouts above)
   uint32_t koff[kS], voff[kM];
+  uint32_t koff8[4], voff8[4];  // FP8 tiles
+  if constexpr (KV8) {
+    auto at = [](int t, int chunk, int half) -> uint32_t {
+      return (uint32_t)(t / 8) * kGroup8 + (uint32_t)(t % 8) * kRowBytes8 +
+             16u * (uint32_t)((chunk + ((t % 8) & ~1)) % 8) + 8u * (uint32_t)half;
+    };
+#pragma unroll
+    for (int s = 0; s < 4; ++s) koff8[s] = at(lane & 15, 2 * s + (row >> 1), row & 1);
+    const int j = lane & 15, a8 = j & 1, k8 = j >> 1;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+      voff8[mm] = kKTile8 + at(4 * row + (k8 & 3), 2 * mm + (k8 >> 2), a8);
+  }
   {
     constexpr int C = Gm::kChunks, R = Gm::kRowsPerLoad;
     const int t = lane & 15, r = t % R;
@@ -586,8 +632,8 @@ void pd_decode_kernel(const KArgs a) {
       // turn the selects into a divergent branch around the loads (which
       // would issue a load twice and break the exact wait counts)
       asm("" : "+v"(ko), "+v"(vo));
-      const uint32_t kd = KV8 ? n * 1024u : n * Gm::kKGroup;
-      const uint32_t vd = KV8 ? kStage8 / 2 + n * 1024u : Gm::kKTile + n * Gm::kVGroup;
+      const uint32_t kd = KV8 ? n * kGroup8 : n * Gm::kKGroup;
+      const uint32_t vd = KV8 ? kKTile8 + n * kGroup8 : Gm::kKTile + n * Gm::kVGroup;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + kd), 16, ko, 0, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + vd), 16, vo, 0, 0, kStream);
     }
@@ -612,31 +658,19 @@ void pd_decode_kernel(const KArgs a) {
       // Before a buffer is refilled every LDS read of it has completed: the
       // refill's LDS writes are not ordered after reads still in flight, and
       // a refill past the slice reads no memory, so it lands at once.
-      if constexpr (KV8) {
-        // convert, then refill the staging buffer before computing
-        char* ct = ldsc + w * Gm::kLdsTile;
-        if (j < nst) convert_fp8_tile<BF16>(tile_buf(d), ct, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(j + kNBuf, d);
-        __builtin_amdgcn_sched_barrier(0);
-        if (j < nst) {
-          const int tile0 = tw0 + kTileTok * j;
-          tile_compute<BF16, D>(st, ct, qb, koff, voff, tile0 + 4 * row, tw1,
-                                    tile0 + kTileTok > tw1, c);
-        }
-      } else {
-        if (j < nst) {
-          const int tile0 = tw0 + kTileTok * j;
+      if (j < nst) {
+        const int tile0 = tw0 + kTileTok * j;
+        if constexpr (KV8)
+          tile_compute_fp8<BF16>(st, tile_buf(d), qb, koff8, voff8, tile0 + 4 * row, tw1,
+                                 tile0 + kTileTok > tw1, c);
+        else
           tile_compute<BF16, D>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
-                                    tile0 + kTileTok > tw1, c);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(j + kNBuf, d);
+                                tile0 + kTileTok > tw1, c);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLds);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + kNBuf, d);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -667,13 +701,12 @@ void pd_decode_kernel(const KArgs a) {
   const int nown = FAST ? kOwn : own.nown;
   const int d0 = 16 * own.block(0) + 4 * row;  // first owned dim; runs of 4 every 16
 
-  // ---- merge the NT slices of each head through LDS (a full 16-bit tile
-  // per wave: the first tile buffer, or the converted-tile buffer of an FP8
-  // kernel; it holds G * (D + 2) floats per wave as G <= 16); slice 0 keeps
-  // the result
+  // ---- merge the NT slices of each head through LDS (the first tile
+  // buffer, sized to hold G * (D + 2) floats per wave as G <= 16); slice 0
+  // keeps the result
   if (a.NT > 1) {
     __syncthreads();  // every wave is done with its tile buffers
-    float* s_acc = (float*)(KV8 ? ldsc : lds0);  // [(w*G + h)*D + dim]
+    float* s_acc = (float*)lds0;                 // [(w*G + h)*D + dim]
     float* s_m = s_acc + nw * G * D;             // [w*G + h]
     float* s_l = s_m + nw * G;
     if (own.active) {
