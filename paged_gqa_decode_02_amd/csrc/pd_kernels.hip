@@ -9,8 +9,8 @@
 // 32/1 included). The query heads of a wave fill the 16 columns of an MFMA
 // block (spare columns repeat heads); a KV head with more than 16 query
 // heads is served by HS "virtual" KV heads of G / HS <= 16 query heads each,
-// whose waves sit in one workgroup and read the same K/V blocks together
-// (the second read is an L2 hit).
+// whose waves sit in one workgroup and read the same K/V blocks together.
+// An FP8 (E4M3FN) cache is read as codes and widened in registers.
 //
 // One kernel. Workgroup (partition p, KV-head group hg, sequence b) has
 // NH x NT wave64s: wave w serves KV head hg*NH + w%NH over token slice w/NH
@@ -32,8 +32,8 @@
 //     (wave-uniform) id with v_readlane, so addresses are scalar.
 //   * scores: q . k for the 16 tokens of a tile and 16 query-head columns
 //     are one 16x16 output of D/32 v_mfma_f32_16x16x32 (bf16 or f16 inputs,
-//     exact products, fp32 sums), read from LDS in the operand order; one multiply by scale*log2(e) puts the softmax in base 2
-//     (v_exp_f32).
+//     exact products, fp32 sums), read from LDS in the operand order; one
+//     multiply by scale*log2(e) puts the softmax in base 2 (v_exp_f32).
 //   * softmax: per head column, a running maximum that only moves when a
 //     ballot finds a tile maximum above it (then the accumulators are
 //     rescaled); each lane keeps its own partial sum of weights.
