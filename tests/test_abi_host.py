@@ -235,7 +235,8 @@ def test_fp8_entry_point_rejects_geometries_it_is_not_built_for(Hq, Hkv, D):
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 64), (32, 1, 128), (32, 1, 64), (8, 8, 128),
-                                      (20, 1, 128), (64, 4, 64)])
+                                      (20, 1, 128), (64, 4, 64), (21, 1, 128), (17, 1, 64),
+                                      (48, 2, 128)])
 @pytest.mark.parametrize("B,L", [(1, 16), (1, 4096), (8, 1024), (64, 4096)])
 def test_plan_at_other_geometries(Hq, Hkv, D, B, L):
     MB = -(-L // 16)

@@ -66,8 +66,11 @@ OTHER = [
     (40, 8, 128, "bf16", 16),   # G = 5
     (64, 8, 128, "bf16", 32),   # G = 8
     (32, 2, 64, "f16", 32),     # G = 16
-    (20, 1, 128, "bf16", 16),   # G = 20, two column blocks with repeats
+    (20, 1, 128, "bf16", 16),   # G = 20: two virtual KV heads of 10
     (32, 8, 64, "bf16", 16),    # D = 64 at the 32/8 grouping
+    (21, 1, 128, "f16", 16),    # G = 21: three virtual KV heads of 7 (odd split)
+    (17, 1, 64, "bf16", 32),    # G = 17 (prime): 17 virtual KV heads of 1
+    (48, 2, 128, "bf16", 16),   # G = 24: two virtual KV heads of 12, two KV heads
 ]
 
 
