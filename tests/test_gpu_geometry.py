@@ -98,3 +98,12 @@ def test_other_geometries_planned_long(Hq, Hkv, D, B, L):
     S, P = pd.paged_decode_plan(B, Hq, Hkv, D, c.max_blocks_per_seq, 16, torch.bfloat16)
     print(f"{c.describe()} plan S={S} P={P}", flush=True)
     check_case(c)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 64), (32, 1, 128)])
+def test_bench_geometry_workloads_full_size(Hq, Hkv, D):
+    # the bench's B64 x 4,096-token geometry workloads, at the planned split
+    # count the bench times, every output against the oracle
+    c = workloads.geometry(Hq, Hkv, D, 64, 4096, seed=0)
+    print(c.describe(), flush=True)
+    check_case(c)
