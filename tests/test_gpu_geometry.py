@@ -107,3 +107,21 @@ def test_bench_geometry_workloads_full_size(Hq, Hkv, D):
     c = workloads.geometry(Hq, Hkv, D, 64, 4096, seed=0)
     print(c.describe(), flush=True)
     check_case(c)
+
+
+@pytest.mark.parametrize("lens,dtype,bs,kv", [([32768, 20001], "bf16", 16, ""),
+                                            ([65536], "f16", 32, ""),
+                                            ([40000, 1, 12345], "bf16", 16, ""),
+                                            ([32768, 7000], "bf16", 16, "fp8")])
+@pytest.mark.parametrize("splits", [None, 1])
+def test_long_contexts(lens, dtype, bs, kv, splits):
+    # contexts past what one workgroup's slices cover (8 waves x 256 blocks):
+    # the plan adds partitions even when one is asked for
+    c = workloads.make_case(f"long_{max(lens)}_{dtype}_bs{bs}{'_' + kv if kv else ''}", len(lens),
+                            lens, dtype=dtype, block_size=bs, seed=len(lens) + bs, kv_dtype=kv)
+    import paged_gqa_decode_02_amd as pd
+    S, P = pd.paged_decode_plan(c.B, c.Hq, c.Hkv, c.D, c.max_blocks_per_seq, bs,
+                                workloads.DTYPES[dtype], splits)
+    print(f"{c.describe()} S={S} P={P}", flush=True)
+    assert S * P >= max(lens)
+    check_case(c, num_splits=splits, what=f"{c.name} S={splits}")
