@@ -33,7 +33,7 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
                        float v_scale = 1.0f) {
   pd::Shape s{B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype};
   pd::Plan plan;
-  int32_t st = pd::make_plan(s, requested_splits, &plan);
+  int32_t st = pd::make_plan(s, requested_splits, &plan, kv_fp8);
   if (st != PD_OK) return st;
   if (!positive_finite(scale)) return PD_ERR_VALUE;
   if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale))) return PD_ERR_VALUE;

@@ -41,7 +41,9 @@ constexpr int kMaxWaves = 8;
 int32_t check_shape(const Shape& s);
 
 // Split plan: requested_splits <= 0 runs the heuristic, else S is forced.
-int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan);
+// kv_fp8 may change the slices per workgroup, never S or P (so the plan
+// and workspace queries, which do not know the cache format, stay right).
+int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_fp8 = false);
 
 // Workspace layout for S > 1: a fixed region of int32 arrival counters
 // [B, Hkv / NH] (kCounterBytes, the same at every shape, so it only ever

@@ -66,9 +66,12 @@ int32_t check_shape(const Shape& s) {
 //   * a split call whose waves still have kPairTiles or more tiles each
 //     does better with KV heads in pairs and twice the partitions;
 //   * with more than 4 query heads per wave the merge of a head reads
-//     G/HS x S partial rows, so S is capped at kMergeRows / (G/HS).
+//     G/HS x S partial rows, so S is capped at kMergeRows / (G/HS);
+//   * tiles with more work per byte (an FP8 cache; 16 query heads per wave
+//     at D 64) take four slices per KV-head pair instead of two, which puts
+//     two waves on each SIMD (S and P are unchanged).
 // A forced S fixes P instead and cuts it into up to NT slices.
-int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
+int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_fp8) {
   int32_t st = check_shape(s);
   if (st != PD_OK) return st;
   const int64_t bs = s.block_size;
@@ -115,6 +118,10 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan) {
 #ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
   if (PD_FORCE_NH > 0 && hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
 #endif
+  // tiles with more work per byte (FP8 codes widened in registers; 16 query
+  // heads per wave at D 64) run better with two waves per SIMD: paired KV
+  // heads then take four slices instead of two (same S and P)
+  if (nh == 2 && nt == 2 && (kv_fp8 || (s.D == 64 && G / hs > 8))) nt = 4;
   if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
   int64_t pw = round_up(ceil_div(P, nt), bs);
