@@ -141,10 +141,11 @@ int32_t paged_decode_attention(const void* q, const void* k_cache, const void* v
  * of the heuristic's; P becomes the smallest multiple of block_size with
  * S*P >= max_blocks_per_seq * block_size, and S is then recomputed as
  * ceil(max_blocks_per_seq * block_size / P), so it can come out smaller than
- * asked. A partition never exceeds 8 waves x 64 blocks (4,096 tokens at
- * block size 16), so a very long context can also get more splits than
- * asked. For tests and measurements of the split path; the result equals
- * the planned call's up to fp32 rounding order.
+ * asked. A partition never exceeds what one workgroup's token slices cover,
+ * 256 blocks each: 4 slices (16,384 tokens at block size 16), or 2 when KV
+ * heads are served in pairs, so a very long context can also get more splits
+ * than asked. For tests and measurements of the split path; the result
+ * equals the planned call's up to fp32 rounding order.
  */
 int32_t paged_decode_attention_splits(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_table, const int32_t* context_lens,

@@ -118,16 +118,19 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
 #ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
   if (PD_FORCE_NH > 0 && hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
 #endif
-  // tiles with more work per byte (FP8 codes widened in registers; 16 query
-  // heads per wave at D 64) run better with two waves per SIMD: paired KV
-  // heads then take four slices instead of two (same S and P)
-  if (nh == 2 && nt == 2 && (kv_fp8 || (s.D == 64 && G / hs > 8))) nt = 4;
   if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
   int64_t pw = round_up(ceil_div(P, nt), bs);
   if (pw > pw_max) {  // a slice cannot exceed 256 blocks: split more
     pw = pw_max;
     P = nt * pw;
+  }
+  // tiles with more work per byte (FP8 codes widened in registers; 16 query
+  // heads per wave at D 64) run better with two waves per SIMD: paired KV
+  // heads then cut the partition, now fixed, into four slices instead of two
+  if (nh == 2 && nt == 2 && (kv_fp8 || (s.D == 64 && G / hs > 8)) && P / bs > 2) {
+    nt = P / bs < 4 ? P / bs : 4;
+    pw = round_up(ceil_div(P, nt), bs);
   }
   nt = ceil_div(P, pw);  // drop slices that would start past the partition
   const int64_t S = ceil_div(cap, P);
