@@ -75,7 +75,8 @@ def make_workload(name: str, seed: int = 0):
         # geom_14x2_D64_B32_L1024
         _, hh, d, b, l = name.split("_")
         hq, hkv = hh.split("x")
-        return workloads.geometry(int(hq), int(hkv), int(d[1:]), int(b[1:]), int(l[1:]), seed)
+        return workloads.geometry(int(hq), int(hkv), int(d[1:]), int(b[1:]), int(l[1:]), seed,
+                                  kv_dtype=kv)
     if name.startswith("short_"):
         # short_B32_L64_bf16_bs16
         _, b, l, dt, bs = name.split("_")

@@ -34,12 +34,13 @@
 //     are one 16x16 output of D/32 v_mfma_f32_16x16x32 (bf16 or f16 inputs,
 //     exact products, fp32 sums), read from LDS in the operand order; one
 //     multiply by scale*log2(e) puts the softmax in base 2 (v_exp_f32).
-//   * softmax: per head column, a running maximum that only moves when a
-//     ballot finds a tile maximum above it (then the accumulators are
-//     rescaled); each lane keeps its own partial sum of weights.
-//   * PV: per 16-dim block, a 16x16x32 MFMA of V^T (read from LDS with the
-//     transposing ds_read_b64_tr_b16) and the weights split into 16-bit
-//     terms, accumulating in fp32.
+//   * softmax: per head column, a reference maximum that only moves when a
+//     ballot finds a tile maximum more than 2^8 (f16: 2^6) above it (then
+//     the accumulators are rescaled); each lane keeps its own partial sum of
+//     weights.
+//   * PV: per 16-dim block and 16-bit weight term, a 16x16x16 MFMA of V^T
+//     (read from LDS with the transposing ds_read_b64_tr_b16) and the
+//     weights, accumulating in fp32.
 //   * end of slice: each head's D sums sit in the 4 lanes of its column;
 //     the NT slices of a head are merged through LDS.
 //   * S == 1: the workgroup writes `out`, rounded to the dtype.
@@ -236,6 +237,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr_t;
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -263,7 +265,7 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // the subnormal range.
 template <bool BF16>
 struct Weights {
-  u32x4 hi_lo;   // k 0..3: hi of the lane's 4 tokens, k 4..7: lo
+  u32x4 hi_lo;   // words 0, 1: hi of the lane's 4 tokens; words 2, 3: lo
   uint32_t lo2[2];  // bf16 only: the third term of the 4 tokens
 };
 template <bool BF16>
@@ -284,7 +286,27 @@ __device__ __forceinline__ Weights<BF16> split_weights(const float (&p)[4]) {
 template <bool BF16>
 struct WeightBias {
   static constexpr float log2 = BF16 ? 0.f : 8.f;
+  // the running maximum that serves as the weights' reference moves only
+  // when a tile's maximum exceeds it by more than `lazy` (log2 units): the
+  // result does not depend on the reference, and the accumulators are
+  // rescaled far less often. Weights then stay below 2^(lazy + log2): 2^8
+  // for bf16, 2^14 for f16 (whose largest finite value is 65504).
+  static constexpr float lazy = BF16 ? 8.f : 6.f;
 };
+
+// v_mfma_f32_16x16x16: A lane l = row l%16, k 4(l/16) .. +4; B lane l =
+// column l%16, the same k; two 32-bit words (four 16-bit values) each
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma_16x16x16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                               f32x4 c) {
+  const u32x2_t a = {a0, a1}, b = {b0, b1};
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, a),
+                                                     __builtin_bit_cast(v4i16_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
 
 // Per-lane state of one wave's online softmax over its token slice. Lane l
 // follows head column l%16 (query head (l%16) % G of the virtual KV head);
@@ -302,11 +324,12 @@ struct WaveState {
 //     lane%16 -> its head): lane l gets the scores of tokens 4(l/16) + i,
 //     i < 4, for its column;
 //   softmax: the tile maximum per column (4 registers, then the 4 rows); the
-//     running maximum only moves when a ballot finds a tile maximum above it;
-//   PV: per 16-dim block, one 16x16x32 MFMA with A = V^T (row = dim, k = the
-//     lane's 4 tokens, twice) and B = those tokens' weights (hi in k 0..3, lo
-//     in k 4..7), which is the layout the scores came out in; for bf16 a
-//     second one adds the third weight term.
+//     reference maximum only moves when a ballot finds a tile maximum more
+//     than WeightBias::lazy above it;
+//   PV: per 16-dim block, 16x16x16 MFMAs with A = V^T (row = dim, k = the
+//     lane's 4 tokens) and B = those tokens' weights, which is the layout
+//     the scores came out in: one for the hi terms, one for lo, and for
+//     bf16 a third for lo2.
 // The math of one tile: ka[s] the K tile as score-MFMA A operands, v01/v23
 // the V^T operand of each 16-dim block (16-bit values of tokens 4(lane/16)
 // + 0,1 and + 2,3 for dim lane%16 of the block).
@@ -338,7 +361,7 @@ __device__ __forceinline__ void tile_math(WaveState<D>& st, const u32x4 (&ka)[Ge
     }
   }
   const float tm = max_rows(fmaxf(fmaxf(s_[0], s_[1]), fmaxf(s_[2], s_[3])));
-  if (__builtin_amdgcn_ballot_w64(tm > st.m) != 0) {
+  if (__builtin_amdgcn_ballot_w64(tm > st.m + WeightBias<BF16>::lazy) != 0) {
     const float mn = fmaxf(st.m, tm);
     const float alpha = exp2_fast(st.m - mn);  // 1 where the maximum stays, 0 from -inf
     st.m = mn;
@@ -347,16 +370,23 @@ __device__ __forceinline__ void tile_math(WaveState<D>& st, const u32x4 (&ka)[Ge
     for (int m = 0; m < kM; ++m) st.acc[m] *= alpha;
   }
   float pr[4];
+  const float mref = BF16 ? st.m : st.m - WeightBias<BF16>::log2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - st.m + WeightBias<BF16>::log2);
+  for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s_[i] - mref);
   st.lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const Weights<BF16> wb = split_weights<BF16>(pr);
+  // PV: one 16x16x16 MFMA per weight term and 16-dim block, A = V^T exactly
+  // as the transposing read delivered it (dim lane%16, the lane's 4 tokens)
 #pragma unroll
-  for (int m = 0; m < kM; ++m) {
-    st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01[m], v23[m], v01[m], v23[m]}, wb.hi_lo, st.acc[m]);
-    if constexpr (BF16)  // k 4..7 of this one are zero on both sides
-      st.acc[m] = mfma_16x16x32<BF16>(u32x4{v01[m], v23[m], 0u, 0u},
-                                      u32x4{wb.lo2[0], wb.lo2[1], 0u, 0u}, st.acc[m]);
+  for (int m = 0; m < kM; ++m)
+    st.acc[m] = mfma_16x16x16<BF16>(v01[m], v23[m], wb.hi_lo[0], wb.hi_lo[1], st.acc[m]);
+#pragma unroll
+  for (int m = 0; m < kM; ++m)
+    st.acc[m] = mfma_16x16x16<BF16>(v01[m], v23[m], wb.hi_lo[2], wb.hi_lo[3], st.acc[m]);
+  if constexpr (BF16) {
+#pragma unroll
+    for (int m = 0; m < kM; ++m)
+      st.acc[m] = mfma_16x16x16<BF16>(v01[m], v23[m], wb.lo2[0], wb.lo2[1], st.acc[m]);
   }
 }
 
@@ -472,6 +502,65 @@ __device__ __forceinline__ Owner make_owner(int u, int G, int kM) {
   o.nown = kM / p2;
   o.active = o.copy < p2;
   return o;
+}
+
+// LSE merge of nb <= W owned dim blocks of one head (dims dim0 + 16 w ..
+// +4, w < nb) over its n_live published partitions (rows slot0 + i of the
+// partial buffers), in order, KB partitions per batch of loads: the partial
+// outputs weighted by exp2(lse_i - max), normalised, rounded to the dtype
+// and stored at op + 16 w.
+template <bool BF16, int W, int KB>
+__device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                             uint32_t slot0, int n_live, uint32_t D,
+                                             uint32_t dim0, int nb, float out_scale,
+                                             uint16_t* op) {
+  float M = -INFINITY, den = 0.f;
+  f32x4 acc[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) acc[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < n_live; i0 += KB) {
+    float lse[KB];
+    f32x4 x[KB][W];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      // partitions past n_live and blocks past nb read zeros (and are
+      // skipped below)
+      const bool ok = i0 + u < n_live;
+      const uint32_t slot = slot0 + (uint32_t)(i0 + u);
+      const uint32_t off = (slot * D + dim0) * 4;
+#pragma unroll
+      for (int w = 0; w < W; ++w)
+        x[u][w] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ro, ok && w < nb ? off + 64 * w : kOutOfBlock, 0, kCoherent));
+      lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
+    }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
+    const float alpha = exp2_fast(M - bm);  // 0 on the first batch
+    den *= alpha;
+#pragma unroll
+    for (int w = 0; w < W; ++w) acc[w] *= alpha;
+    M = bm;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (i0 + u < n_live) {
+        const float wt = exp2_fast(lse[u] - M);
+        den += wt;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[w][e] = fmaf(wt, x[u][w][e], acc[w][e]);
+      }
+    }
+  }
+  const float inv = out_scale / den;
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+    if (w < nb) store4<BF16>(op + 16 * w, acc[w], inv);
 }
 
 template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
@@ -791,61 +880,29 @@ void pd_decode_kernel(const KArgs a) {
 
     // ---- last workgroup: LSE merge over the n_live partitions, in order.
     // It reads only the published partials, so the NT slice waves of a head
-    // share it: wave ts merges its share of the lane's owned dim blocks, two
-    // per pass (at G <= 4, D = 128: one block per wave with NT = 2).
-    constexpr int kBatch = 8;
+    // share it: wave ts merges its share (per) of the lane's owned dim
+    // blocks, in passes of two blocks (eight partitions per batch of loads)
+    // or, when it has more, four blocks (four partitions per batch).
     uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
+    const uint32_t hrow = (uint32_t)(h * a.S);  // the head's partition 0
     const int per = (nown + a.NT - 1) / a.NT;
     const int kb = ts * per, ke = min(nown, kb + per);
+    if (kOwn <= 2 || per <= 2) {
 #pragma unroll
-    for (int k0 = 0; k0 < kOwn; k0 += 2) {
-      if (kb + k0 >= ke) break;
-      const bool two = kb + k0 + 1 < ke;
-      const uint32_t dim0 = (uint32_t)(d0 + 16 * (kb + k0));
-      float M = -INFINITY, den = 0.f;
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      for (int i0 = 0; i0 < n_live; i0 += kBatch) {
-        float lse[kBatch];
-        f32x4 x0[kBatch], x1[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          // partitions past n_live read zeros and are skipped below
-          const bool ok = i0 + u < n_live;
-          const uint32_t slot = (uint32_t)(h * a.S + i0 + u);
-          const uint32_t off = ok ? (slot * D + dim0) * 4 : kOutOfBlock;
-          x0[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0,
-                                                                                  kCoherent));
-          x1[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                ro, ok && two ? off + 64 : kOutOfBlock, 0,
-                                                kCoherent));
-          lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
-        }
-        float bm = M;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-          if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
-        const float alpha = exp2_fast(M - bm);  // 0 on the first batch
-        den *= alpha;
-        acc0 *= alpha;
-        acc1 *= alpha;
-        M = bm;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (i0 + u < n_live) {
-            const float wt = exp2_fast(lse[u] - M);
-            den += wt;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              acc0[e] = fmaf(wt, x0[u][e], acc0[e]);
-              acc1[e] = fmaf(wt, x1[u][e], acc1[e]);
-            }
-          }
-        }
+      for (int k0 = 0; k0 < kOwn; k0 += 2) {
+        if (kb + k0 >= ke) break;
+        merge_blocks<BF16, 2, 8>(ro, rl, hrow, n_live, (uint32_t)D,
+                                 (uint32_t)(d0 + 16 * (kb + k0)), min(2, ke - kb - k0),
+                                 a.out_scale, op + 16 * (kb + k0));
       }
-      const float inv = a.out_scale / den;
-      store4<BF16>(op + 16 * (kb + k0), acc0, inv);
-      if (two) store4<BF16>(op + 16 * (kb + k0 + 1), acc1, inv);
+    } else if constexpr (kOwn > 2) {
+#pragma unroll
+      for (int k0 = 0; k0 < kOwn; k0 += 4) {
+        if (kb + k0 >= ke) break;
+        merge_blocks<BF16, 4, 4>(ro, rl, hrow, n_live, (uint32_t)D,
+                                 (uint32_t)(d0 + 16 * (kb + k0)), min(4, ke - kb - k0),
+                                 a.out_scale, op + 16 * (kb + k0));
+      }
     }
   }
 }

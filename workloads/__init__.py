@@ -314,9 +314,9 @@ def large(seed: int = 0, B: int = 64, L: int = 4096, kv_dtype: str = "") -> Case
 
 
 def geometry(Hq: int, Hkv: int, D: int, B: int, L: int, seed: int = 0, dtype: str = "bf16",
-             block_size: int = 16) -> Case:
+             block_size: int = 16, kv_dtype: str = "") -> Case:
     """B sequences of L tokens at another head geometry (the pages' 14/2 D64
     route, MQA 32/1, ...), N(0, 1) inputs, scale 1/sqrt(D) rounded to float32."""
-    return make_case(f"geom_{Hq}x{Hkv}_D{D}_B{B}_L{L}", B, L, dtype=dtype, block_size=block_size,
-                     Hq=Hq, Hkv=Hkv, D=D, seed=seed,
-                     scale=float(np.float32(1.0 / math.sqrt(D))))
+    return make_case(f"geom_{Hq}x{Hkv}_D{D}_B{B}_L{L}{_suffix(kv_dtype)}", B, L, dtype=dtype,
+                     block_size=block_size, Hq=Hq, Hkv=Hkv, D=D, seed=seed,
+                     scale=float(np.float32(1.0 / math.sqrt(D))), kv_dtype=kv_dtype)
