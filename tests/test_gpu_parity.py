@@ -195,3 +195,41 @@ def test_needle(where):
             blk = c.block_table[b, t // bs]
             for h in range(32):
                 assert np.array_equal(out[b, h], c.v_cache[blk, t % bs, h // 4]), (where, s, b, h)
+
+
+RAMPS = {0.02: [1000, 777, 16, 1024], 0.05: [1000, 777, 16, 1024],
+         0.6: [300, 77, 16, 64], -0.03: [1000, 777, 16, 1024]}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("slope", sorted(RAMPS))
+def test_scores_that_rise_or_fall_through_the_context(dtype, slope):
+    # All query heads of a sequence share q0 and token t's key is a multiple
+    # of q0, so every score is close to slope * t - c (plus a little noise,
+    # c the largest slope * t): the maximum then keeps rising by less than a
+    # tile's worth, or by much more (0.6 per token, about 14 in log2 units
+    # per tile), or falls. The kernel's softmax reference lags the running
+    # maximum, its weights grow up to their bound between moves; the result
+    # must not depend on that. The shift keeps the scores that carry weight
+    # near 0: scores of 60 and more carry the fp32 rounding of their dot
+    # products (about 1e-5 of a score) past the 1-ulp gate on outputs that
+    # cancel to near zero, in any fp32 evaluation.
+    lens = RAMPS[slope]
+    c = workloads.make_case(f"ramp_{dtype}_{slope}", len(lens), lens, dtype=dtype,
+                            block_size=16, seed=21)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    widen = lambda bits: torch.from_numpy(bits.view(np.int16)).view(tdt).float()
+    pack = lambda x: x.to(tdt).view(torch.int16).numpy().view(np.uint16)
+    rng = np.random.default_rng(5)
+    for b, L in enumerate(lens):
+        q0 = widen(c.q[b, 0])
+        c.q[b] = c.q[b, 0][None, :]
+        unit = q0 / (float(c.scale) * float((q0 * q0).sum()))
+        top = max(slope * t for t in range(L))
+        for t in range(L):
+            blk, off = c.block_table[b, t // 16], t % 16
+            for g in range(c.Hkv):
+                noise = torch.from_numpy(rng.normal(0, 0.01, c.D).astype(np.float32))
+                c.k_cache[blk, off, g] = pack((slope * t - top) * unit + noise)
+    for s in (None, 1, 3):
+        check_case(c, num_splits=s, what=f"{c.name} S={s}")
