@@ -1,0 +1,89 @@
+"""GPU parity at the limits of the shapes the library takes.
+
+The largest batch the grid allows (65,535 sequences, one workgroup row
+each), outputs sampled across the whole batch against the oracle, planned
+and split (the split using every arrival counter the workspace holds); a
+split that would need more counters is refused before anything is
+launched. And block ids more than 4 GiB into
+the pool: the K/V addresses are 64-bit, so a case whose blocks sit past that
+point gives the same bits as the same case in a small pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import compare, device_case, out_bits, run_library
+
+pytestmark = pytest.mark.gpu
+
+
+def max_batch_case(Hq, Hkv, seed):
+    B = 65535
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 21, size=B).astype(np.int32)   # 0 .. 2 blocks of 16
+    need = int(sum(-(-int(L) // 16) for L in lens))
+    return workloads.make_case(f"max_batch_{Hq}x{Hkv}", B, lens, dtype="bf16", block_size=16,
+                               Hq=Hq, Hkv=Hkv, D=64, seed=seed, scale=float(np.float32(0.125)),
+                               max_blocks_per_seq=2, pool_blocks=max(1, need))
+
+
+def check_rows(c, got):
+    # every 257th sequence, the last one and some empty ones, against the oracle
+    lens = c.context_lens
+    pick = np.unique(np.concatenate([np.arange(0, c.B, 257), [c.B - 1],
+                                     np.nonzero(lens == 0)[0][:8]]))
+    ref, _ = oracle.attention(c.q[pick], c.k_cache, c.v_cache, c.block_table[pick],
+                              lens[pick], scale=c.scale, dtype=c.dtype)
+    compare(got[pick], ref, c.dtype, what=f"{c.name} rows={len(pick)}")
+
+
+def test_largest_batch_three_kv_heads():
+    # the planned call has S = 1; a split would need 65,535 x 3 arrival
+    # counters, more than the workspace holds, and is refused
+    import paged_gqa_decode_02_amd as pd
+    c = max_batch_case(12, 3, seed=41)
+    print(c.describe(), flush=True)
+    assert pd.paged_decode_plan(c.B, 12, 3, 64, 2, 16, torch.bfloat16)[0] == 1
+    check_rows(c, out_bits(run_library(c)))
+    with pytest.raises(pd.PagedDecodeError) as e:
+        run_library(c, num_splits=2)
+    assert e.value.code == 7  # PD_ERR_UNSUPPORTED, before any launch
+
+
+def test_largest_batch_split_uses_every_counter():
+    # 65,535 sequences x one KV head: the split path's counters 0 .. 65,534
+    c = max_batch_case(8, 1, seed=43)
+    print(c.describe(), flush=True)
+    check_rows(c, out_bits(run_library(c, num_splits=2)))
+
+
+@pytest.mark.parametrize("kv", ["", "fp8"])
+def test_block_ids_past_4_gib_of_pool(kv):
+    lens = [300, 17, 1024]
+    c = workloads.make_case(f"far_blocks{'_' + kv if kv else ''}", len(lens), lens,
+                            dtype="bf16", block_size=16, seed=42, kv_dtype=kv)
+    print(c.describe(), flush=True)
+    small = out_bits(run_library(c))
+    q, k, v, bt, cl = device_case(c)
+    block_bytes = k[0].numel() * k.element_size()       # 32 KiB (16-bit) or 16 KiB (FP8)
+    base = (4 << 30) // block_bytes + 1000               # first far id: past 4 GiB
+    nb = base + c.num_blocks
+    kb = torch.zeros((nb,) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    vb = torch.zeros_like(kb)
+    kb[base:] = k
+    vb[base:] = v
+    bt_far = bt + base
+    import paged_gqa_decode_02_amd as pd
+    if c.fp8:
+        far = pd.paged_decode_attention_fp8(q, kb, vb, bt_far, cl, k_scale=c.k_scale,
+                                            v_scale=c.v_scale, scale=c.scale)
+    else:
+        far = pd.paged_decode_attention(q, kb, vb, bt_far, cl, scale=c.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(far), small)
+    ref, _ = oracle.attention_case(c)
+    compare(small, ref, c.dtype, what=c.name)
+    del kb, vb
+    torch.cuda.empty_cache()
