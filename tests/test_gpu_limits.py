@@ -6,7 +6,8 @@ and split (the split using every arrival counter the workspace holds); a
 split that would need more counters is refused before anything is
 launched. And block ids more than 4 GiB into
 the pool: the K/V addresses are 64-bit, so a case whose blocks sit past that
-point gives the same bits as the same case in a small pool.
+point gives the same bits as the same case in a small pool, for the decode,
+the RoPE + KV write and the block moves.
 """
 import numpy as np
 import pytest
@@ -85,5 +86,64 @@ def test_block_ids_past_4_gib_of_pool(kv):
     assert np.array_equal(out_bits(far), small)
     ref, _ = oracle.attention_case(c)
     compare(small, ref, c.dtype, what=c.name)
+    del kb, vb
+    torch.cuda.empty_cache()
+
+
+def far_pool(k, v, base):
+    """Copies of (k, v) [NB, ...] at block ids base .. base + NB of a pool of
+    zeros that size (the copies start past 4 GiB)."""
+    nb = base + k.shape[0]
+    kb = torch.zeros((nb,) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+    vb = torch.zeros_like(kb)
+    kb[base:] = k
+    vb[base:] = v
+    return kb, vb
+
+
+def test_rope_write_to_slots_past_4_gib():
+    from workloads import rope as wrope
+    import paged_gqa_decode_02_amd as pd
+    case = wrope.scatter(64, seed=44, pad_every=9)
+    dt = workloads.DTYPES[case.dtype]
+    qkv = case.torch_qkv().cuda()
+    q, k, v = qkv[:, :case.Hq], qkv[:, case.Hq:case.Hq + case.Hkv], qkv[:, case.Hq + case.Hkv:]
+    kc, vc = (t.cuda() for t in case.torch_caches())
+    block_bytes = kc[0].numel() * 2
+    base = (4 << 30) // block_bytes + 100
+    kb, vb = far_pool(kc, vc, base)
+    pos = torch.from_numpy(case.positions).cuda()
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    far_slots = torch.where(slots >= 0, slots + base * case.block_size, slots)
+    table = pd.rope_cos_sin_table(case.max_position, case.D, case.base)
+    q_small = pd.rope_paged_kv_write(q, k, v, pos, slots, table, kc, vc)
+    q_far = pd.rope_paged_kv_write(q, k, v, pos, far_slots, table, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(q_small.view(torch.int16), q_far.view(torch.int16))
+    assert torch.equal(kb[base:].view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(vb[base:].view(torch.int16), vc.view(torch.int16))
+    assert not bool(kb[:base].view(torch.int16).any())   # nothing written below the copies
+    del kb, vb
+    torch.cuda.empty_cache()
+
+
+def test_block_moves_past_4_gib():
+    from workloads import blocks as wb
+    import paged_gqa_decode_02_amd as pd
+    case = wb.pool(96, seed=45)
+    kc, vc = (t.cuda() for t in case.torch_caches())
+    base = (4 << 30) // case.block_bytes + 100
+    kb, vb = far_pool(kc, vc, base)
+    pairs = torch.from_numpy(wb.copy_pairs(96, 30, seed=46)).cuda()
+    ids = torch.from_numpy(wb.block_ids(96, 40, seed=47)).cuda()
+    pd.paged_kv_copy_blocks(kc, vc, pairs)
+    pd.paged_kv_copy_blocks(kb, vb, pairs + base)
+    g_small = pd.paged_kv_gather_blocks(kc, vc, ids)
+    g_far = pd.paged_kv_gather_blocks(kb, vb, ids + base)
+    torch.cuda.synchronize()
+    for a, b in zip(g_small, g_far):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(kb[base:].view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(vb[base:].view(torch.int16), vc.view(torch.int16))
     del kb, vb
     torch.cuda.empty_cache()
