@@ -26,10 +26,26 @@ go to cache slot slot_mapping[t] (block slot // block_size, row slot %
 block_size) of caches laid out [num_blocks, block_size, Hkv, D]; a negative
 slot writes nothing (a padding token).
 
+The write into an FP8 cache (``rope_kv_write_fp8``; the home page's "Next
+boundaries" name FP8 KV-cache compression) stores OCP E4M3FN codes with one
+float32 scale per tensor, the format the FP8 decode reads: the code of a
+value x is the E4M3FN value nearest to x / scale (ties to the even code),
+with magnitudes beyond the largest finite 448 held at 448 rather than
+turned into NaN (a reading: the pages give no rule). A code is an integer
+decided by floating point, so it is decided in the precision the kernel
+uses, float32, in a fixed order of operations: for a key pair (x, y) with
+table entries (c, s), x' = fl(fl(x c) - fl(y s)) and y' = fl(fl(y c) +
+fl(x s)), fl the float32 rounding; then fl(x' / k_scale) is encoded. A
+value is widened exactly and fl(v / v_scale) encoded. The rotated query
+stays 16-bit as in ``rope_kv_write``.
+
 Parity status: pinned by ``tests/test_oracle_rope.py`` (identity at position
 0, closed forms at D = 2 and D = 4, the complex-multiplication form of the
 rotation, the relative-position property, a pure-Python brute force, and
-round trips of the cache write through a block table).
+round trips of the cache write through a block table; the E4M3FN encoder
+against torch's CPU cast on every in-range input tried, on every code's own
+value and on the midpoints between codes, and its saturation by closed form;
+the float32 key rotation within its rounding bound of the fp64 one).
 """
 from __future__ import annotations
 
@@ -108,3 +124,83 @@ def rope_kv_write(q, k, v, positions, slot_mapping, table, k_cache, v_cache, *, 
     kc[slots[live]] = round_to_dtype(k_rot[live], dtype)
     vc[slots[live]] = v[live]
     return q_rot, k_rot, kc.reshape(k_cache.shape), vc.reshape(v_cache.shape)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3FN) cache write
+
+def _e4m3_values() -> np.ndarray:
+    """The values of the non-negative finite E4M3FN codes 0x00 .. 0x7E, in
+    code order (which is value order): exponent field e (bias 7) and
+    fraction f, value f/8 * 2^-6 for e = 0, (1 + f/8) * 2^(e-7) otherwise."""
+    codes = np.arange(0x7F)
+    e, f = codes >> 3, codes & 7
+    return np.where(e == 0, f / 8.0 * 2.0 ** -6, (1.0 + f / 8.0) * 2.0 ** (e - 7.0))
+
+
+def fp8_encode(x) -> np.ndarray:
+    """float32 values -> E4M3FN codes (uint8): the nearest code value, ties
+    to the even code, magnitudes above 448 held at 448 (0x7E), NaN to 0x7F
+    with its sign; the sign bit is the input's (so -0.0 gives 0x80)."""
+    x = np.asarray(x, np.float32)
+    vals = _e4m3_values()
+    a = np.abs(x.astype(np.float64))
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, vals[-1]))
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)  # vals[hi] >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == vals[hi], hi, code)
+    sign = np.signbit(x).astype(np.int64) << 7
+    out = np.where(nan, 0x7F, code) | sign
+    return out.astype(np.uint8)
+
+
+def rotate_f32(x, y, c, s):
+    """The float32 rotation of pairs (x, y) by (c, s), in the order the FP8
+    write fixes: (fl(fl(x c) - fl(y s)), fl(fl(y c) + fl(x s)))."""
+    x, y, c, s = (np.asarray(t, np.float32) for t in (x, y, c, s))
+    return (np.float32(x * c) - np.float32(y * s)).astype(np.float32), \
+           (np.float32(y * c) + np.float32(x * s)).astype(np.float32)
+
+
+def rope_kv_write_fp8(q, k, v, positions, slot_mapping, table, k_cache, v_cache, *, dtype: str,
+                      k_scale: float, v_scale: float):
+    """The fused step with an FP8 cache.
+
+    As ``rope_kv_write``, with k_cache, v_cache uint8 E4M3FN codes
+    [num_blocks, block_size, Hkv, D] and float32 scales. Returns (q_rot,
+    k_cache_after, v_cache_after): q_rot fp64 [T, Hq, D] unrounded; at each
+    written slot the key codes encode fl(x' / k_scale) for the float32
+    rotation x' of ``rotate_f32`` and the value codes fl(v / v_scale); every
+    other byte is unchanged.
+    """
+    ks, vs = np.float32(k_scale), np.float32(v_scale)
+    if not (np.isfinite(ks) and ks > 0 and np.isfinite(vs) and vs > 0):
+        raise ValueError("scales must be finite and positive")
+    k_cache = np.asarray(k_cache, np.uint8)
+    v_cache = np.asarray(v_cache, np.uint8)
+    dummy = np.zeros(k_cache.shape, np.uint16)
+    # shape, position and slot checks and the query rotation are the 16-bit step's
+    q_rot, _, _, _ = rope_kv_write(q, k, v, positions, slot_mapping, table, dummy, dummy,
+                                   dtype=dtype)
+    pos = np.asarray(positions, np.int64)
+    slots = np.asarray(slot_mapping, np.int64)
+    live = slots >= 0
+    D = q.shape[2]
+    h = D // 2
+    tab = np.asarray(table, np.float32)[pos][:, None, :]       # [T, 1, D]
+    kw = widen(np.asarray(k, np.uint16), dtype).astype(np.float32)
+    x1, x2 = rotate_f32(kw[..., :h], kw[..., h:], tab[..., :h], tab[..., h:])
+    k_rot = np.concatenate([x1, x2], axis=-1)
+    k_codes = fp8_encode((k_rot / ks).astype(np.float32))
+    v_codes = fp8_encode((widen(np.asarray(v, np.uint16), dtype).astype(np.float32) / vs)
+                         .astype(np.float32))
+    NB, bs, Hkv, _ = k_cache.shape
+    kc = np.array(k_cache, copy=True).reshape(NB * bs, Hkv, D)
+    vc = np.array(v_cache, copy=True).reshape(NB * bs, Hkv, D)
+    kc[slots[live]] = k_codes[live]
+    vc[slots[live]] = v_codes[live]
+    return q_rot, kc.reshape(k_cache.shape), vc.reshape(v_cache.shape)

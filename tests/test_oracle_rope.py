@@ -203,3 +203,98 @@ def test_oracle_rejects_bad_inputs():
     with pytest.raises(ValueError):
         rope.rope_kv_write(*args, case.positions, np.array([0, 1, case.num_blocks * 16]), table,
                            case.k_cache, case.v_cache, dtype="bf16")
+
+
+# ---------------------------------------------------------------------------
+# the FP8 (E4M3FN) cache write
+
+
+def torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_encode_gives_every_code_back():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    vals = oracle.widen_fp8(codes).astype(np.float32)
+    assert np.array_equal(rope.fp8_encode(vals), codes)
+
+
+def test_fp8_encode_matches_torch_inside_the_range():
+    # torch's CPU cast rounds to nearest-even; checked on log-uniform values
+    # over the whole range (subnormals included), every code's midpoint with
+    # its neighbour, and one float32 step either side of each midpoint
+    rng = np.random.default_rng(0)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 200000)).astype(np.float32)
+    x = mag * np.where(rng.random(mag.size) < 0.5, -1, 1).astype(np.float32)
+    vals = oracle.widen_fp8(np.arange(0x7F, dtype=np.uint8))
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)      # exact in float32
+    near = np.concatenate([mid, np.nextafter(mid, np.float32(0)),
+                           np.nextafter(mid, np.float32(1000))])
+    x = np.concatenate([x, near, -near]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(rope.fp8_encode(x), torch_e4m3(x))
+
+
+def test_fp8_encode_ties_go_to_the_even_code():
+    vals = oracle.widen_fp8(np.arange(0x7F, dtype=np.uint8))
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    got = rope.fp8_encode(mid).astype(int)
+    lo = np.arange(0x7E)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+
+
+def test_fp8_encode_holds_large_magnitudes_at_448():
+    x = np.array([448.0, 450.0, 464.0, 464.03125, 480.0, 1e6, 3e38, np.inf], np.float32)
+    assert np.all(rope.fp8_encode(x) == 0x7E)
+    assert np.all(rope.fp8_encode(-x) == 0xFE)
+    assert rope.fp8_encode(np.float32(np.nan)) & 0x7F == 0x7F
+    assert rope.fp8_encode(np.float32(-0.0)) == 0x80 and rope.fp8_encode(np.float32(0.0)) == 0
+
+
+def test_float32_key_rotation_is_within_its_rounding_of_the_exact_one():
+    rng = np.random.default_rng(1)
+    x, y = (rng.standard_normal(100000).astype(np.float32) for _ in range(2))
+    a = rng.uniform(0, 2 * np.pi, 100000)
+    c, s = np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+    x1, y1 = rope.rotate_f32(x, y, c, s)
+    X, Y, C, S = (t.astype(np.float64) for t in (x, y, c, s))
+    u = 2.0 ** -24
+    # three roundings: of each product and of the sum
+    assert np.all(np.abs(x1 - (X * C - Y * S)) <= u * (np.abs(X * C) + np.abs(Y * S)) * 2.01 + 1e-45)
+    assert np.all(np.abs(y1 - (Y * C + X * S)) <= u * (np.abs(Y * C) + np.abs(X * S)) * 2.01 + 1e-45)
+    # and the order is the stated one: products rounded first
+    assert np.array_equal(x1, (np.float32(x * c) - np.float32(y * s)).astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fp8_write_codes_stand_for_the_scaled_16bit_write(dtype):
+    case = wrope.scatter(24, Hq=4, Hkv=2, D=64, dtype=dtype, block_size=16, seed=5,
+                         pad_every=5, max_position=4096)
+    tab = rope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    ks, vs = 0.0125, 0.0078125
+    kc0 = np.full(case.k_cache.shape, 0x11, np.uint8)
+    vc0 = np.full(case.v_cache.shape, 0x22, np.uint8)
+    q_rot8, kc, vc = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
+                                            case.slot_mapping, tab, kc0, vc0, dtype=dtype,
+                                            k_scale=ks, v_scale=vs)
+    q_rot, k_rot, _, _ = rope.rope_kv_write(case.q, case.k, case.v, case.positions,
+                                            case.slot_mapping, tab, case.k_cache,
+                                            case.v_cache, dtype=dtype)
+    assert np.array_equal(q_rot8, q_rot)
+    live = case.slot_mapping >= 0
+    s = case.slot_mapping[live].astype(np.int64)
+    kf = kc.reshape(-1, case.Hkv, case.D)
+    vf = vc.reshape(-1, case.Hkv, case.D)
+    # each code is the nearest E4M3FN value to the scaled exact key/value:
+    # within half a code step (2^-4 relative, or 2^-10 absolute below 2^-6)
+    kd = oracle.widen_fp8(kf[s]) * ks
+    vd = oracle.widen_fp8(vf[s]) * vs
+    kr, vr = k_rot[live], oracle.widen(case.v, dtype)[live]
+    # (the factor 1.0001 covers the float32 rotation and division)
+    assert np.all(np.abs(kd - kr) <= 2.0 ** -4 * np.abs(kr) * 1.0001 + 2.0 ** -10 * ks)
+    assert np.all(np.abs(vd - vr) <= 2.0 ** -4 * np.abs(vr) * 1.0001 + 2.0 ** -10 * vs)
+    # nothing else was touched
+    untouched = np.ones(kf.shape[0], bool)
+    untouched[s] = False
+    assert np.all(kf[untouched] == 0x11) and np.all(vf[untouched] == 0x22)
