@@ -198,7 +198,19 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
 
 
 ROPE_CASES = ("scatter_T1", "scatter_T8", "scatter_T32", "scatter_T64", "scatter_T128",
-              "scatter_T512", "prefill_4x4096")
+              "scatter_T512", "prefill_4x4096", "scatter_T64_fp8", "prefill_4x4096_fp8")
+
+
+def rope_fp8_scales(case, torch):
+    """Per-tensor scales of an FP8 cache write, from the inputs' largest
+    magnitudes (keys: times sqrt 2, the most a rotation can grow a
+    coordinate): amax / 448, so no code saturates."""
+    import workloads
+    x = torch.from_numpy(case.qkv.view(np.int16)).view(workloads.DTYPES[case.dtype]).float()
+    H, G = case.Hq, case.Hkv
+    k_amax = float(x[:, H:H + G].abs().max()) * math.sqrt(2.0)
+    v_amax = float(x[:, H + G:].abs().max())
+    return max(k_amax, 1e-30) / 448.0, max(v_amax, 1e-30) / 448.0
 
 
 def rope_check(case, qkv, qo, vc, torch):
@@ -213,21 +225,44 @@ def rope_check(case, qkv, qo, vc, torch):
     n1 = torch.hypot(r[..., :h], r[..., h:])
     ulp = 2.0 ** -7 if case.dtype == "bf16" else 2.0 ** -10
     norm_ok = bool((n1 - n0).abs().le(ulp * n0 + 1e-6).all())
+    finite = bool(torch.isfinite(r).all())
+    chk = {"finite": finite, "pair_norms_kept": norm_ok}
+    if vc is None:  # the caller checks the cache itself
+        return finite and norm_ok, chk
     live = torch.from_numpy(case.slot_mapping).cuda().long()
     live = live[live >= 0]
     vrows = vc.view(-1, case.Hkv, D)[live]
     v_in = qkv[:, H + case.Hkv:][torch.from_numpy(case.slot_mapping >= 0).cuda()]
     v_ok = bool(torch.equal(vrows.view(torch.int16), v_in.reshape(vrows.shape).view(torch.int16)))
-    finite = bool(torch.isfinite(r).all())
-    return finite and norm_ok and v_ok, {"finite": finite, "pair_norms_kept": norm_ok,
-                                         "values_copied_exactly": v_ok}
+    chk["values_copied_exactly"] = v_ok
+    return finite and norm_ok and v_ok, chk
+
+
+def rope_check_fp8(case, qkv, qo, vc, torch, vs):
+    """Oracle-free checks of one RoPE write into an FP8 cache: q_out as in
+    rope_check, and each value code within half an E4M3FN step of value /
+    v_scale, held at 448 (torch's own float8 widening)."""
+    H, G, D = case.Hq, case.Hkv, case.D
+    ok16, chk = rope_check(case, qkv, qo, None, torch)
+    live = torch.from_numpy(case.slot_mapping).cuda().long()
+    live = live[live >= 0]
+    got = vc.view(-1, G, D)[live].view(torch.float8_e4m3fn).float()
+    v_in = qkv[:, H + G:][torch.from_numpy(case.slot_mapping >= 0).cuda()].float() / vs
+    v_in = v_in.reshape(got.shape).clamp(-448.0, 448.0)
+    close = bool(((got - v_in).abs() <= 2.0 ** -4 * v_in.abs() + 2.0 ** -10).all())
+    chk["value_codes_nearest"] = close
+    return ok16 and close, chk
 
 
 def bench_rope(name, torch, pd, table, iters=200, warmup=20):
     """RoPE + paged KV write at the decode geometry (Hq/Hkv 32/8, D 128,
     bf16, block size 16): T tokens at random positions into distinct random
-    slots, or a 4 x 4,096-token prefill through block tables."""
+    slots, or a 4 x 4,096-token prefill through block tables; a "_fp8"
+    suffix writes E4M3FN codes into an FP8 cache instead."""
     from workloads import rope as wrope
+    fp8 = name.endswith("_fp8")
+    if fp8:
+        name = name[:-4]
     if name.startswith("scatter_T"):
         case = wrope.scatter(int(name[len("scatter_T"):]), seed=1)
     else:
@@ -237,7 +272,11 @@ def bench_rope(name, torch, pd, table, iters=200, warmup=20):
 
     def up():
         qkv = case.torch_qkv().cuda()
-        kc, vc = (t.cuda() for t in case.torch_caches())
+        if fp8:
+            kc, vc = (torch.zeros(case.k_cache.shape, dtype=torch.uint8, device="cuda")
+                      for _ in range(2))
+        else:
+            kc, vc = (t.cuda() for t in case.torch_caches())
         return (qkv, kc, vc, torch.from_numpy(case.positions).cuda(),
                 torch.from_numpy(case.slot_mapping).cuda(),
                 torch.empty((case.T, case.Hq, case.D), dtype=dt, device="cuda"))
@@ -251,19 +290,28 @@ def bench_rope(name, torch, pd, table, iters=200, warmup=20):
     reps = [base] + [up() for _ in range(R - 1)]
     H, G = case.Hq, case.Hkv
 
+    ks, vs = rope_fp8_scales(case, torch) if fp8 else (1.0, 1.0)
+
     def call(i):
         qkv, kc, vc, pos, slots, qo = reps[i % R]
-        pd.rope_paged_kv_write(qkv[:, :H], qkv[:, H:H + G], qkv[:, H + G:], pos, slots, table,
-                               kc, vc, q_out=qo)
+        if fp8:
+            pd.rope_paged_kv_write_fp8(qkv[:, :H], qkv[:, H:H + G], qkv[:, H + G:], pos, slots,
+                                       table, kc, vc, q_out=qo, k_scale=ks, v_scale=vs)
+        else:
+            pd.rope_paged_kv_write(qkv[:, :H], qkv[:, H:H + G], qkv[:, H + G:], pos, slots,
+                                   table, kc, vc, q_out=qo)
 
     call(0)
     torch.cuda.synchronize()
-    ok, chk = rope_check(case, base[0], base[5], base[2], torch)
+    if fp8:
+        ok, chk = rope_check_fp8(case, base[0], base[5], base[2], torch, vs)
+    else:
+        ok, chk = rope_check(case, base[0], base[5], base[2], torch)
     if not ok:
         return {"check": "FAIL", **chk}
     ms = time_calls(call, iters, warmup, torch)
     ms_g = time_graph(call, max(R, (iters // R) * R), torch)
-    nbytes = case.algorithmic_bytes()
+    nbytes = case.algorithmic_bytes(1 if fp8 else 2)
     res = {"tokens": case.T, "us_per_call": round(ms * 1e3, 3),
            "us_per_call_graph": round(ms_g * 1e3, 3),
            "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),

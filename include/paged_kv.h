@@ -97,6 +97,38 @@ int32_t rope_paged_kv_write(const void* q, const void* k, const void* v,
                             int32_t dtype, void* stream);
 
 /*
+ * The same step into an FP8 KV cache (Loom Kernels home page, "Next
+ * boundaries": FP8 KV-cache compression; the cache paged_decode_attention_fp8
+ * reads). k_cache and v_cache hold one OCP E4M3FN code per element in the
+ * same [num_blocks, block_size, Hkv, D] layout; q, k, v and q_out stay
+ * 16-bit of dtype, and q_out is written exactly as rope_paged_kv_write
+ * writes it. At each named slot:
+ *
+ *   k code = E(fl(x' * fl(1 / k_scale))),  v code = E(fl(v * fl(1 / v_scale)))
+ *
+ * where x' is the key rotated in float32 in a fixed order, x'[i] =
+ * fl(fl(x[i] c) - fl(x[i+D/2] s)) and x'[i+D/2] = fl(fl(x[i+D/2] c) +
+ * fl(x[i] s)) (fl the float32 rounding, nearest-even, no fused
+ * multiply-add), v is widened exactly, and E gives the E4M3FN code of the
+ * nearest value (ties to the even code), holding magnitudes beyond the
+ * largest finite 448 at 448 and NaN as 0x7F. The decode then reads the
+ * value code * scale, so one scale per tensor serves the whole cache.
+ *
+ * Arguments, layouts, contract and errors as rope_paged_kv_write, except:
+ * k_cache and v_cache are 8-byte aligned (PD_ERR_ALIGN otherwise) and span
+ * num_blocks * block_size * Hkv * D bytes; k_scale and v_scale are finite
+ * and positive (PD_ERR_VALUE otherwise).
+ */
+int32_t rope_paged_kv_write_fp8(const void* q, const void* k, const void* v,
+                                int64_t q_row_stride, int64_t k_row_stride,
+                                int64_t v_row_stride, const int32_t* positions,
+                                const int32_t* slot_mapping, const float* cos_sin,
+                                int32_t max_position, void* q_out, void* k_cache, void* v_cache,
+                                int32_t num_blocks, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t block_size, int32_t dtype, float k_scale, float v_scale,
+                                void* stream);
+
+/*
  * KV-cache block movement (Loom Kernels home page, "Next boundaries":
  * KV-cache movement, block copy, gather, scatter and compact work for prefix
  * reuse and preemption). A block is one [block_size, Hkv, D] slab of a cache,

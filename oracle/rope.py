@@ -29,15 +29,16 @@ slot writes nothing (a padding token).
 The write into an FP8 cache (``rope_kv_write_fp8``; the home page's "Next
 boundaries" name FP8 KV-cache compression) stores OCP E4M3FN codes with one
 float32 scale per tensor, the format the FP8 decode reads: the code of a
-value x is the E4M3FN value nearest to x / scale (ties to the even code),
-with magnitudes beyond the largest finite 448 held at 448 rather than
-turned into NaN (a reading: the pages give no rule). A code is an integer
-decided by floating point, so it is decided in the precision the kernel
-uses, float32, in a fixed order of operations: for a key pair (x, y) with
-table entries (c, s), x' = fl(fl(x c) - fl(y s)) and y' = fl(fl(y c) +
-fl(x s)), fl the float32 rounding; then fl(x' / k_scale) is encoded. A
-value is widened exactly and fl(v / v_scale) encoded. The rotated query
-stays 16-bit as in ``rope_kv_write``.
+value x is the E4M3FN value nearest to x times the float32 reciprocal of
+the scale (ties to the even code), with magnitudes beyond the largest
+finite 448 held at 448 rather than turned into NaN (readings: the pages give
+no quantisation rule). A code is an integer decided by floating point, so
+it is decided in the precision the kernel uses, float32, in a fixed order
+of operations: for a key pair (x, y) with table entries (c, s), x' =
+fl(fl(x c) - fl(y s)) and y' = fl(fl(y c) + fl(x s)), fl the float32
+rounding; then fl(x' * r_k) is encoded, r_k = fl(1 / k_scale). A value is
+widened exactly and fl(v * r_v) encoded, r_v = fl(1 / v_scale). The rotated
+query stays 16-bit as in ``rope_kv_write``.
 
 Parity status: pinned by ``tests/test_oracle_rope.py`` (identity at position
 0, closed forms at D = 2 and D = 4, the complex-multiplication form of the
@@ -173,9 +174,9 @@ def rope_kv_write_fp8(q, k, v, positions, slot_mapping, table, k_cache, v_cache,
     As ``rope_kv_write``, with k_cache, v_cache uint8 E4M3FN codes
     [num_blocks, block_size, Hkv, D] and float32 scales. Returns (q_rot,
     k_cache_after, v_cache_after): q_rot fp64 [T, Hq, D] unrounded; at each
-    written slot the key codes encode fl(x' / k_scale) for the float32
-    rotation x' of ``rotate_f32`` and the value codes fl(v / v_scale); every
-    other byte is unchanged.
+    written slot the key codes encode fl(x' * fl(1 / k_scale)) for the
+    float32 rotation x' of ``rotate_f32`` and the value codes fl(v * fl(1 /
+    v_scale)); every other byte is unchanged.
     """
     ks, vs = np.float32(k_scale), np.float32(v_scale)
     if not (np.isfinite(ks) and ks > 0 and np.isfinite(vs) and vs > 0):
@@ -195,8 +196,9 @@ def rope_kv_write_fp8(q, k, v, positions, slot_mapping, table, k_cache, v_cache,
     kw = widen(np.asarray(k, np.uint16), dtype).astype(np.float32)
     x1, x2 = rotate_f32(kw[..., :h], kw[..., h:], tab[..., :h], tab[..., h:])
     k_rot = np.concatenate([x1, x2], axis=-1)
-    k_codes = fp8_encode((k_rot / ks).astype(np.float32))
-    v_codes = fp8_encode((widen(np.asarray(v, np.uint16), dtype).astype(np.float32) / vs)
+    rk, rv = np.float32(1) / ks, np.float32(1) / vs      # float32 reciprocals
+    k_codes = fp8_encode((k_rot * rk).astype(np.float32))
+    v_codes = fp8_encode((widen(np.asarray(v, np.uint16), dtype).astype(np.float32) * rv)
                          .astype(np.float32))
     NB, bs, Hkv, _ = k_cache.shape
     kc = np.array(k_cache, copy=True).reshape(NB * bs, Hkv, D)

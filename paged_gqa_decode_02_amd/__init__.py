@@ -225,6 +225,8 @@ lib.rope_cos_sin_table.restype = _I
 lib.rope_paged_kv_write.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _P, _I, _P, _P, _P, _I,
                                     _I, _I, _I, _I, _I, _I, _P]
 lib.rope_paged_kv_write.restype = _I
+lib.rope_paged_kv_write_fp8.argtypes = lib.rope_paged_kv_write.argtypes[:-1] + [_F, _F, _P]
+lib.rope_paged_kv_write_fp8.restype = _I
 
 
 def _handle(stream, device):
@@ -256,20 +258,15 @@ def _rows(name, t, H, D):
     return int(t.stride(0)) if t.shape[0] > 1 else H * D
 
 
-def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out=None,
-                        *, stream=None):
-    """RoPE + paged KV-cache write (``rope_paged_kv_write``) on the current
-    (or given) stream.
-
-    q [T,Hq,D], k/v [T,Hkv,D] (f16 or bf16; views into one packed QKV array
-    are fine as long as each head is contiguous); positions, slot_mapping
-    int32 [T]; cos_sin float32 [max_position, D] (``rope_cos_sin_table``);
-    k_cache/v_cache [num_blocks,block_size,Hkv,D] (written in place). Returns
-    q_out [T,Hq,D] (allocated when not given; may be q itself).
-    """
-    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype or \
-            k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q, k, v and the caches must share one dtype, float16 or bfloat16")
+def _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out, fp8):
+    """Checked pointer and size arguments shared by the two RoPE writes."""
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype, float16 or bfloat16")
+    if fp8:
+        if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype:
+            raise ValueError("FP8 caches must be float8_e4m3fn (or uint8 codes), both alike")
+    elif k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("the caches must have q's dtype")
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or not k_cache.is_contiguous() or \
             not v_cache.is_contiguous():
         raise ValueError("k_cache/v_cache must be contiguous [num_blocks,block_size,Hkv,D]")
@@ -288,11 +285,42 @@ def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_ca
         q_out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
     if tuple(q_out.shape) != (T, Hq, D) or q_out.dtype != q.dtype or not q_out.is_contiguous():
         raise ValueError("q_out must be a contiguous [T, Hq, D] tensor of q's dtype")
-    rc = lib.rope_paged_kv_write(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), qs, ks, vs, positions.data_ptr(),
-        slot_mapping.data_ptr(), cos_sin.data_ptr(), int(cos_sin.shape[0]), q_out.data_ptr(),
-        k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[q.dtype],
-        _handle(stream, q.device))
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), qs, ks, vs, positions.data_ptr(),
+            slot_mapping.data_ptr(), cos_sin.data_ptr(), int(cos_sin.shape[0]), q_out.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[q.dtype]]
+    return args, q_out
+
+
+def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out=None,
+                        *, stream=None):
+    """RoPE + paged KV-cache write (``rope_paged_kv_write``) on the current
+    (or given) stream.
+
+    q [T,Hq,D], k/v [T,Hkv,D] (f16 or bf16; views into one packed QKV array
+    are fine as long as each head is contiguous); positions, slot_mapping
+    int32 [T]; cos_sin float32 [max_position, D] (``rope_cos_sin_table``);
+    k_cache/v_cache [num_blocks,block_size,Hkv,D] (written in place). Returns
+    q_out [T,Hq,D] (allocated when not given; may be q itself).
+    """
+    args, q_out = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
+                             False)
+    rc = lib.rope_paged_kv_write(*args, _handle(stream, q.device))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return q_out
+
+
+def rope_paged_kv_write_fp8(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                            q_out=None, *, k_scale, v_scale, stream=None):
+    """The RoPE + KV write into an FP8 cache (``rope_paged_kv_write_fp8``):
+    as ``rope_paged_kv_write`` with k_cache/v_cache float8_e4m3fn (or uint8)
+    [num_blocks,block_size,Hkv,D] receiving the E4M3FN codes of the rotated
+    key times the float32 reciprocal of k_scale and of the value times that
+    of v_scale. Returns q_out (16-bit)."""
+    args, q_out = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
+                             True)
+    rc = lib.rope_paged_kv_write_fp8(*args, float(k_scale), float(v_scale),
+                                     _handle(stream, q.device))
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return q_out

@@ -97,6 +97,8 @@ struct RopeLaunch {
   int32_t num_blocks;
   int32_t T, Hq, Hkv, D, block_size, dtype;
   void* stream;
+  bool kv_fp8 = false;  // caches hold E4M3FN codes (1 byte per element)
+  float k_scale = 1.0f, v_scale = 1.0f;
 };
 int32_t launch_rope_kv_write(const RopeLaunch& l);
 int32_t launch_rope_table(float* table, int32_t max_position, int32_t D, double base,

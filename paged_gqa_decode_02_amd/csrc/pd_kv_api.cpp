@@ -30,6 +30,8 @@ size_t rows_bytes(int64_t T, int64_t stride, int64_t row_elems) {
   return T > 0 ? (size_t)(((T - 1) * stride + row_elems) * 2) : 0;
 }
 
+bool positive_finite(float x) { return x > 0.0f && isfinite(x); }
+
 int32_t rope_write_impl(const pd::RopeLaunch& l) {
   if (l.dtype != PD_DTYPE_F16 && l.dtype != PD_DTYPE_BF16) return PD_ERR_DTYPE;
   if (l.T < 0 || l.Hq < 1 || l.Hkv < 1 || l.Hq > 1024 || l.Hkv > 1024 || l.D < 1 ||
@@ -44,17 +46,21 @@ int32_t rope_write_impl(const pd::RopeLaunch& l) {
   const int64_t units = (int64_t)l.T * (l.Hq + 2 * l.Hkv) * (l.D / 16);
   if (units > ((int64_t)1 << 31) - 256) return PD_ERR_SHAPE;
   if ((int64_t)l.max_position * l.D > ((int64_t)1 << 31)) return PD_ERR_SHAPE;
+  if (l.kv_fp8 && (!positive_finite(l.k_scale) || !positive_finite(l.v_scale)))
+    return PD_ERR_VALUE;
   if (l.T == 0) return PD_OK;
   if (!l.q || !l.k || !l.v || !l.positions || !l.slot_mapping || !l.cos_sin || !l.q_out ||
       !l.k_cache || !l.v_cache)
     return PD_ERR_NULL;
+  const uintptr_t cache_align = l.kv_fp8 ? 8 : 16;  // FP8 codes move 8 bytes at a time
   if (!aligned(l.q, 16) || !aligned(l.k, 16) || !aligned(l.v, 16) || !aligned(l.q_out, 16) ||
-      !aligned(l.k_cache, 16) || !aligned(l.v_cache, 16) || !aligned(l.cos_sin, 16) ||
+      !aligned(l.k_cache, cache_align) || !aligned(l.v_cache, cache_align) ||
+      !aligned(l.cos_sin, 16) ||
       !aligned(l.positions, 4) || !aligned(l.slot_mapping, 4) || l.q_row_stride % 8 ||
       l.k_row_stride % 8 || l.v_row_stride % 8)
     return PD_ERR_ALIGN;
 
-  const size_t cache_bytes = (size_t)l.num_blocks * l.block_size * kvrow * 2;
+  const size_t cache_bytes = (size_t)l.num_blocks * l.block_size * kvrow * (l.kv_fp8 ? 1 : 2);
   const Range q{l.q, rows_bytes(l.T, l.q_row_stride, qrow)};
   const Range k{l.k, rows_bytes(l.T, l.k_row_stride, kvrow)};
   const Range v{l.v, rows_bytes(l.T, l.v_row_stride, kvrow)};
@@ -139,6 +145,28 @@ int32_t rope_paged_kv_write(const void* q, const void* k, const void* v, int64_t
                      positions, slot_mapping, cos_sin, max_position, q_out,     k_cache,
                      v_cache,  num_blocks, T,        Hq,           Hkv,          D,
                      block_size, dtype,   stream};
+    return rope_write_impl(l);
+  } catch (...) {
+    return PD_ERR_INTERNAL;
+  }
+}
+
+int32_t rope_paged_kv_write_fp8(const void* q, const void* k, const void* v,
+                                int64_t q_row_stride, int64_t k_row_stride,
+                                int64_t v_row_stride, const int32_t* positions,
+                                const int32_t* slot_mapping, const float* cos_sin,
+                                int32_t max_position, void* q_out, void* k_cache, void* v_cache,
+                                int32_t num_blocks, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t block_size, int32_t dtype, float k_scale, float v_scale,
+                                void* stream) {
+  try {
+    pd::RopeLaunch l{q,        k,         v,         q_row_stride, k_row_stride, v_row_stride,
+                     positions, slot_mapping, cos_sin, max_position, q_out,     k_cache,
+                     v_cache,  num_blocks, T,        Hq,           Hkv,          D,
+                     block_size, dtype,   stream};
+    l.kv_fp8 = true;
+    l.k_scale = k_scale;
+    l.v_scale = v_scale;
     return rope_write_impl(l);
   } catch (...) {
     return PD_ERR_INTERNAL;

@@ -22,6 +22,15 @@
 // rounds each output once to the dtype, round-to-nearest-even; value units
 // are a bit-for-bit copy.
 //
+// Into an FP8 cache (home page, "Next boundaries": FP8 KV-cache
+// compression) the K/V units store OCP E4M3FN codes, one byte per element,
+// with one float32 scale per tensor: the code of x is the E4M3FN value
+// nearest to x times the float32 reciprocal of the scale, ties to even,
+// magnitudes past 448 held at 448. Keys are rotated in float32 in a fixed
+// order, x' = fl(fl(x c) - fl(y s)) and y' = fl(fl(y c) + fl(x s)) (no fused
+// multiply-add), then multiplied by fl(1 / k_scale); values are widened
+// exactly and multiplied by fl(1 / v_scale). The query output stays 16-bit.
+//
 // The table kernel evaluates theta_i, the angle and its cosine and sine in
 // fp64 and rounds each entry once to float32, so the table is the float32
 // rounding of the exact one whatever the position (a float32 angle would be
@@ -56,6 +65,7 @@ struct RopeArgs {
   int32_t T, Hq, Hkv, D;
   int32_t units_head;   // D / 16
   int32_t units_token;  // (Hq + 2 Hkv) * D / 16
+  float k_inv, v_inv;  // FP8 caches: code = E4M3FN(x * inv), inv = fl(1 / scale)
 };
 
 // 8 16-bit values (one 16-byte chunk) <-> fp32, exact widening and
@@ -87,7 +97,51 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)lo | ((uint32_t)hi << 16);
 }
 
-template <bool BF16>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// float32 -> OCP E4M3FN code (sign, 4 exponent bits with bias 7, 3 fraction
+// bits): nearest value, ties to even; magnitudes from 464 up (whose nearest
+// would be the NaN code) are held at 448 (0x7E); NaN gives 0x7F. Both ranges
+// are computed and one kept by selects, so no lane branches.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  // below 2^-6: steps of 2^-9, codes 0 .. 8 (the input clamped so that the
+  // conversion stays in range where this result is not kept)
+  const uint32_t sub =
+      (uint32_t)__builtin_rintf(fminf(__builtin_bit_cast(float, a), 0.015625f) * 512.0f);
+  // from 2^-6: keep 3 of the 23 fraction bits (nearest-even), rebias 127 -> 7
+  const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  uint32_t c = a < 0x3c800000u ? sub : nrm;
+  c = a >= 0x43e80000u ? 0x7eu : c;
+  c = a > 0x7f800000u ? 0x7fu : c;
+  return sign | c;
+}
+
+// Rotation of the pairs (x[i], y[i]) in the order the FP8 write fixes.
+__device__ __forceinline__ void rotate_exact(const float (&x)[8], const float (&y)[8],
+                                             const float (&c)[8], const float (&s)[8],
+                                             float (&rx)[8], float (&ry)[8]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xc = x[i] * c[i], ys = y[i] * s[i], yc = y[i] * c[i], xs = x[i] * s[i];
+    rx[i] = xc - ys;
+    ry[i] = yc + xs;
+  }
+}
+
+// 8 values -> 8 codes of x * inv (inv the float32 reciprocal of the scale),
+// byte i = value i.
+__device__ __forceinline__ u32x2 codes8(const float (&x)[8], float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i / 4] |= e4m3_code(x[i] * inv) << (8 * (i % 4));
+  return u32x2{w[0], w[1]};
+}
+
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void rope_kv_write_kernel(const RopeArgs a) {
   const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t t = g / a.units_token;
@@ -111,6 +165,34 @@ __global__ __launch_bounds__(kThreads) void rope_kv_write_kernel(const RopeArgs 
   // padding (negative slot) and slots outside the pool write no K/V
   if ((uint32_t)pos >= (uint32_t)a.max_position) return;
   if (!is_q && (slot < 0 || (int64_t)slot >= a.num_slots)) return;
+  if constexpr (FP8) {
+    if (!is_q) {
+      // one byte per cached element: codes of 8 elements at 8 j and their
+      // partners at D/2 + 8 j
+      char* dst = (is_k ? a.k_cache : a.v_cache) + ((int64_t)slot * a.Hkv + hk) * a.D;
+      float e1[8], e2[8];
+      widen8<BF16>(x1, e1);
+      widen8<BF16>(x2, e2);
+      u32x2 w1, w2;
+      if (is_k) {
+        const float* row = a.table + (int64_t)pos * a.D + 8 * j;
+        const f32x4 c0 = *(const f32x4*)row, c1 = *(const f32x4*)(row + 4);
+        const f32x4 s0 = *(const f32x4*)(row + a.D / 2), s1 = *(const f32x4*)(row + a.D / 2 + 4);
+        const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        float r1[8], r2[8];
+        rotate_exact(e1, e2, c, s, r1, r2);
+        w1 = codes8(r1, a.k_inv);
+        w2 = codes8(r2, a.k_inv);
+      } else {
+        w1 = codes8(e1, a.v_inv);
+        w2 = codes8(e2, a.v_inv);
+      }
+      *(u32x2*)(dst + 8 * j) = w1;
+      *(u32x2*)(dst + a.D / 2 + 8 * j) = w2;
+      return;
+    }
+  }
   char* dst = is_q ? a.q_out + (t * a.Hq + h) * head_bytes
                    : (is_k ? a.k_cache : a.v_cache) + ((int64_t)slot * a.Hkv + hk) * head_bytes;
   if (!is_v) {
@@ -185,14 +267,23 @@ int32_t launch_rope_kv_write(const RopeLaunch& l) {
   a.D = l.D;
   a.units_head = l.D / 16;
   a.units_token = (l.Hq + 2 * l.Hkv) * a.units_head;
+  // correctly rounded float32 reciprocals, once on the host
+  a.k_inv = 1.0f / l.k_scale;
+  a.v_inv = 1.0f / l.v_scale;
   const int64_t n = (int64_t)l.T * a.units_token;
   const unsigned blocks = (unsigned)((n + kThreads - 1) / kThreads);
-  if (l.dtype == PD_DTYPE_BF16)
-    hipLaunchKernelGGL(rope_kv_write_kernel<true>, dim3(blocks), dim3(kThreads), 0,
-                       (hipStream_t)l.stream, a);
-  else
-    hipLaunchKernelGGL(rope_kv_write_kernel<false>, dim3(blocks), dim3(kThreads), 0,
-                       (hipStream_t)l.stream, a);
+  const hipStream_t st = (hipStream_t)l.stream;
+  const bool bf16 = l.dtype == PD_DTYPE_BF16;
+  if (l.kv_fp8) {
+    if (bf16)
+      hipLaunchKernelGGL((rope_kv_write_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((rope_kv_write_kernel<false, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+  } else if (bf16) {
+    hipLaunchKernelGGL((rope_kv_write_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((rope_kv_write_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

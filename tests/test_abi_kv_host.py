@@ -82,6 +82,41 @@ def test_rope_write_in_place_q_passes_the_alias_check():
     assert rope_call(qo=1 * GB, pos=4 * GB + 2) == CODES["PD_ERR_ALIGN"]
 
 
+def rope_call_fp8(k_scale=0.01, v_scale=0.02, **over):
+    T, Hq, Hkv, D, bs, NB, MP = 8, 32, 8, 128, 16, 64, 4096
+    a = dict(q=1 * GB, k=2 * GB, v=3 * GB, qs=Hq * D, ks=Hkv * D, vs=Hkv * D, pos=4 * GB,
+             slots=5 * GB, table=6 * GB, maxpos=MP, qo=7 * GB, kc=8 * GB, vc=9 * GB, nb=NB,
+             T=T, Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=BF16)
+    a.update(over)
+    return pd.lib.rope_paged_kv_write_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"],
+                                          a["pos"], a["slots"], a["table"], a["maxpos"],
+                                          a["qo"], a["kc"], a["vc"], a["nb"], a["T"], a["Hq"],
+                                          a["Hkv"], a["D"], a["bs"], a["dtype"], k_scale,
+                                          v_scale, 0)
+
+
+@pytest.mark.parametrize("over,code", ROPE_ERRORS)
+def test_fp8_rope_write_argument_errors(over, code):
+    # the 16-bit write's checks hold for the FP8 one
+    assert rope_call_fp8(**over) == CODES[code]
+
+
+@pytest.mark.parametrize("ks,vs", [(0.0, 1.0), (-1.0, 1.0), (float("inf"), 1.0),
+                                   (float("nan"), 1.0), (1.0, 0.0), (1.0, float("nan"))])
+def test_fp8_rope_write_scales_must_be_finite_and_positive(ks, vs):
+    assert rope_call_fp8(k_scale=ks, v_scale=vs) == CODES["PD_ERR_VALUE"]
+    assert rope_call_fp8(k_scale=ks, v_scale=vs, T=0) == CODES["PD_ERR_VALUE"]
+
+
+def test_fp8_rope_write_caches_need_8_byte_alignment_and_span_one_byte_per_element():
+    assert rope_call_fp8(kc=8 * GB + 4) == CODES["PD_ERR_ALIGN"]
+    # 8-byte aligned caches pass the alignment check and fail on the overlap
+    # instead (k_cache spans 64 x 16 x 8 x 128 = 1 MiB of codes)
+    assert rope_call_fp8(kc=8 * GB + 8, vc=8 * GB + 8 + (1 << 20) - 64) == CODES["PD_ERR_ALIAS"]
+    assert rope_call(kc=8 * GB + 8, vc=8 * GB + (2 << 20)) == CODES["PD_ERR_ALIGN"]
+    assert rope_call_fp8(T=0, q=0, k=0, v=0, pos=0, slots=0, table=0, qo=0, kc=0, vc=0) == 0
+
+
 TABLE_ERRORS = [
     (dict(maxpos=0), "PD_ERR_SHAPE"),
     (dict(dim=0), "PD_ERR_SHAPE"),

@@ -211,3 +211,91 @@ def test_graph_replay_reads_positions_at_replay():
         c2 = wrope.RopeCase(case.name, 32, 32, 8, 128, "bf16", 16, case.max_position, case.base,
                             case.qkv, new_pos, case.slot_mapping, case.k_cache, case.v_cache, 0)
         check_write(c2, (out_bits(qo), out_bits(kc), out_bits(vc)))
+
+
+# ---------------------------------------------------------------------------
+# the write into an FP8 cache: codes bit for bit against the oracle's
+
+
+def run_write_fp8(case, kc8, vc8, k_scale, v_scale, *, packed=True):
+    """Upload, call rope_paged_kv_write_fp8 over caches holding the codes
+    kc8/vc8, return (q_out bits, k codes, v codes)."""
+    qkv = to_dev(case.qkv, case.dtype)
+    if packed:
+        q, k, v = qkv[:, :case.Hq], qkv[:, case.Hq:case.Hq + case.Hkv], qkv[:, case.Hq + case.Hkv:]
+    else:
+        q, k, v = (to_dev(a, case.dtype) for a in (case.q, case.k, case.v))
+    kc = torch.from_numpy(np.ascontiguousarray(kc8)).cuda().view(torch.float8_e4m3fn)
+    vc = torch.from_numpy(np.ascontiguousarray(vc8)).cuda().view(torch.float8_e4m3fn)
+    pos = torch.from_numpy(case.positions).cuda()
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    tab = gpu_table(case.max_position, case.D, case.base)
+    qo = pd.rope_paged_kv_write_fp8(q, k, v, pos, slots, tab, kc, vc, k_scale=k_scale,
+                                    v_scale=v_scale)
+    torch.cuda.synchronize()
+    return out_bits(qo), kc.view(torch.uint8).cpu().numpy(), vc.view(torch.uint8).cpu().numpy()
+
+
+def random_codes(shape, seed):
+    # any bytes but the two NaN codes, so untouched slots are checkable
+    c = np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 1, c).astype(np.uint8)
+
+
+FP8_CASES = [
+    # T, Hq, Hkv, D, dtype, bs, pad, k_scale, v_scale
+    (64, 32, 8, 128, "bf16", 16, 0, 0.01, 0.01),
+    (33, 32, 8, 128, "f16", 32, 4, 0.0078125, 0.015625),    # power-of-two scales
+    (40, 14, 2, 64, "bf16", 16, 7, 0.02, 0.005),
+    (16, 8, 4, 256, "f16", 16, 0, 0.03, 0.04),
+    (128, 32, 8, 128, "bf16", 16, 9, 0.002, 0.003),          # many codes held at 448
+]
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,dtype,bs,pad,ks,vs", FP8_CASES)
+@pytest.mark.parametrize("packed", [True, False])
+def test_fp8_write_codes_match_oracle_bit_for_bit(T, Hq, Hkv, D, dtype, bs, pad, ks, vs, packed):
+    case = wrope.scatter(T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, block_size=bs, pad_every=pad,
+                         max_position=32768, seed=T + D + 1)
+    print(case.describe(), f"fp8 ks={ks} vs={vs}", "packed" if packed else "separate", flush=True)
+    kc8 = random_codes(case.k_cache.shape, T)
+    vc8 = random_codes(case.v_cache.shape, T + 1)
+    qo, kc, vc = run_write_fp8(case, kc8, vc8, ks, vs, packed=packed)
+    tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    q_rot, kc_ref, vc_ref = orope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
+                                                    case.slot_mapping, tab, kc8, vc8,
+                                                    dtype=dtype, k_scale=ks, v_scale=vs)
+    compare(qo, q_rot, dtype, what=f"{case.name} q_out")
+    assert np.array_equal(kc, kc_ref), f"{case.name}: K codes differ at {np.argwhere(kc != kc_ref)[:4]}"
+    assert np.array_equal(vc, vc_ref), f"{case.name}: V codes differ"
+    if ks == 0.002:  # the case meant to hit the saturation
+        assert np.count_nonzero((kc_ref & 0x7F) == 0x7E) > 0
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_fp8_write_then_fp8_decode(bs):
+    """The FP8 write feeds the FP8 decode: each sequence's new token goes to
+    position L-1 through its block table, then paged decode attention reads
+    the codes."""
+    dec = workloads.make_case("feed8", 8, [1, 16, 17, 100, 255, 256, 513, 1000], dtype="bf16",
+                              block_size=bs, seed=9, kv_dtype="fp8")
+    case = wrope.decode_step(dec, seed=10)
+    print(case.describe(), "fp8", flush=True)
+    qo, kc, vc = run_write_fp8(case, dec.k_cache, dec.v_cache, dec.k_scale, dec.v_scale)
+    tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    q_rot, kc_ref, vc_ref = orope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
+                                                    case.slot_mapping, tab, dec.k_cache,
+                                                    dec.v_cache, dtype="bf16",
+                                                    k_scale=dec.k_scale, v_scale=dec.v_scale)
+    compare(qo, q_rot, "bf16", what="feed8 q_out")
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    # decode over the GPU-written codes with the GPU-rotated q, against the
+    # oracle over the same bytes
+    import dataclasses
+    fed = dataclasses.replace(dec, q=qo, k_cache=kc, v_cache=vc)
+    for s in (None, 1, 3):
+        out = run_library(fed, num_splits=s)
+        ref, _ = oracle.attention_fp8(qo, kc, vc, dec.block_table, dec.context_lens,
+                                      scale=dec.scale, dtype="bf16", k_scale=dec.k_scale,
+                                      v_scale=dec.v_scale)
+        compare(out_bits(out), ref, "bf16", what=f"feed8 decode S={s}")

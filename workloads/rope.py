@@ -68,14 +68,15 @@ class RopeCase:
     def num_blocks(self) -> int:
         return int(self.k_cache.shape[0])
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, cache_bytes: int = 2) -> int:
         """Bytes one call must move: q, k, v in; rotated q out; k and v rows of
-        the written slots; one cos/sin row per token; positions and slots."""
+        the written slots (``cache_bytes`` per element: 2, or 1 for an FP8
+        cache); one cos/sin row per token; positions and slots."""
         es = 2
         live = int((self.slot_mapping >= 0).sum())
         qkv_in = self.T * (self.Hq + 2 * self.Hkv) * self.D * es
         q_out = self.T * self.Hq * self.D * es
-        kv_out = 2 * live * self.Hkv * self.D * es
+        kv_out = 2 * live * self.Hkv * self.D * cache_bytes
         table = self.T * self.D * 4
         return qkv_in + q_out + kv_out + table + 8 * self.T
 
