@@ -147,3 +147,73 @@ def test_workspace_init_zeroes_the_whole_workspace():
     pd.paged_decode_workspace_init(ws)
     torch.cuda.synchronize()
     assert torch.count_nonzero(ws).item() == 0
+
+
+@pytest.mark.parametrize("kv", ["", "fp8"])
+def test_decode_step_graph_write_then_attend(kv):
+    """A whole decode step captured in one HIP graph: the RoPE + KV write of
+    each sequence's new token at position L - 1 (through its block table),
+    then paged decode attention over the updated cache with the rotated q.
+    Replayed four times with new q/k/v, positions, slots and lengths written
+    between replays, each replay bitwise equal to the same two calls made
+    eagerly on a second copy of the cache (out and every cache byte)."""
+    fp8 = kv == "fp8"
+    B, Hq, Hkv, D, bs, MB = 4, 32, 8, 128, 16, 64
+    c = workloads.make_case(f"step{'_' + kv if kv else ''}", B, [300, 17, 1000, 64],
+                            dtype="bf16", block_size=bs, seed=25, max_blocks_per_seq=MB,
+                            kv_dtype=kv)
+    ks, vs = (c.k_scale, c.v_scale) if fp8 else (1.0, 1.0)
+    q0, k0, v0, bt, cl = device_case(c)
+    tab = pd.rope_cos_sin_table(MB * bs, D, 1e6)
+    lens = c.context_lens.astype(np.int64).copy()
+
+    def step_inputs(rep):
+        g = np.random.default_rng(100 + rep)
+        qkv = torch.from_numpy(g.standard_normal((B, Hq + 2 * Hkv, D)).astype(np.float32))
+        L = np.minimum(lens + 1, MB * bs)
+        pos = (L - 1).astype(np.int32)
+        slots = (c.block_table[np.arange(B), pos // bs].astype(np.int64) * bs + pos % bs)
+        return qkv.to(torch.bfloat16).cuda(), torch.from_numpy(pos).cuda(), \
+            torch.from_numpy(slots.astype(np.int32)).cuda(), torch.from_numpy(L.astype(np.int32)).cuda()
+
+    def run_step(qkv, pos, slots, L, kc, vc, q_out, out, ws):
+        q, k, v = qkv[:, :Hq], qkv[:, Hq:Hq + Hkv], qkv[:, Hq + Hkv:]
+        if fp8:
+            pd.rope_paged_kv_write_fp8(q, k, v, pos, slots, tab, kc, vc, q_out=q_out,
+                                       k_scale=ks, v_scale=vs)
+            pd.paged_decode_attention_fp8(q_out, kc, vc, bt, L, out, k_scale=ks, v_scale=vs,
+                                          scale=c.scale, workspace=ws)
+        else:
+            pd.rope_paged_kv_write(q, k, v, pos, slots, tab, kc, vc, q_out=q_out)
+            pd.paged_decode_attention(q_out, kc, vc, bt, L, out, scale=c.scale, workspace=ws)
+
+    # the graph's state and the eager copy
+    kc_g, vc_g = k0.clone(), v0.clone()
+    kc_e, vc_e = k0.clone(), v0.clone()
+    qkv_g, pos_g, slots_g, L_g = step_inputs(0)
+    q_out_g = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out_g = torch.empty_like(q_out_g)
+    ws_g = pd.alloc_workspace(q_out_g, kc_g, bt)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on a side stream, as capture requires
+        run_step(qkv_g, pos_g, slots_g, L_g, kc_g.clone(), vc_g.clone(), q_out_g, out_g, ws_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_step(qkv_g, pos_g, slots_g, L_g, kc_g, vc_g, q_out_g, out_g, ws_g)
+    for rep in range(4):
+        qkv, pos, slots, L = step_inputs(rep)
+        for dst, src in ((qkv_g, qkv), (pos_g, pos), (slots_g, slots), (L_g, L)):
+            dst.copy_(src)
+        graph.replay()
+        q_out_e = torch.empty_like(q_out_g)
+        out_e = torch.empty_like(out_g)
+        run_step(qkv, pos, slots, L, kc_e, vc_e, q_out_e, out_e, pd.alloc_workspace(q_out_e, kc_e, bt))
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), rep
+        assert torch.equal(kc_g.view(torch.uint8), kc_e.view(torch.uint8)), rep
+        assert torch.equal(vc_g.view(torch.uint8), vc_e.view(torch.uint8)), rep
+        assert bool(torch.isfinite(out_g.float()).all())
+        lens = L.cpu().numpy().astype(np.int64)
