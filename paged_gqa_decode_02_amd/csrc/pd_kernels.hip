@@ -35,9 +35,9 @@
 //     exact products, fp32 sums), read from LDS in the operand order; one
 //     multiply by scale*log2(e) puts the softmax in base 2 (v_exp_f32).
 //   * softmax: per head column, a reference maximum that only moves when a
-//     ballot finds a tile maximum more than 2^8 (f16: 2^6) above it (then
-//     the accumulators are rescaled); each lane keeps its own partial sum of
-//     weights.
+//     ballot finds a tile maximum more than 8 (f16: 6) above it in log2
+//     units, i.e. a weight above 2^8 (2^6) (then the accumulators are
+//     rescaled); each lane keeps its own partial sum of weights.
 //   * PV: per 16-dim block and 16-bit weight term, a 16x16x16 MFMA of V^T
 //     (read from LDS with the transposing ds_read_b64_tr_b16) and the
 //     weights, accumulating in fp32.
