@@ -621,7 +621,7 @@ def main():
                      "splitk_B8_L1024_fp8", "ragged_fp8", "geom_14x2_D64_B32_L1024",
                      "geom_14x2_D64_B64_L4096", "geom_32x1_D128_B8_L4096",
                      "geom_32x1_D128_B64_L4096", "geom_32x1_D64_B64_L4096",
-                     "geom_64x8_D128_B16_L4096"):
+                     "geom_64x8_D128_B16_L4096", "geom_14x2_D64_B64_L4096_fp8"):
             others[name] = bench_other(name, torch, pd)
         res["others"] = others
         from workloads import rope as wrope

@@ -184,9 +184,9 @@ size_t paged_decode_workspace_bytes_splits(int32_t B, int32_t Hq, int32_t Hkv, i
  * (k_scale * scale) and to the normalised output (v_scale).
  *
  * Errors as paged_decode_attention, plus PD_ERR_VALUE when k_scale or
- * v_scale is not finite and positive, PD_ERR_SHAPE for num_splits < 0, and
- * PD_ERR_UNSUPPORTED for D != 128 (the FP8 kernels are built for D = 128, at
- * every group size the 16-bit path takes).
+ * v_scale is not finite and positive and PD_ERR_SHAPE for num_splits < 0.
+ * The FP8 kernels take every geometry the 16-bit path takes (D 64 or 128,
+ * group sizes 1 to 32, block size 16 or 32).
  */
 int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* context_lens,

@@ -37,7 +37,6 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   if (st != PD_OK) return st;
   if (!positive_finite(scale)) return PD_ERR_VALUE;
   if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale))) return PD_ERR_VALUE;
-  if (kv_fp8 && D != 128) return PD_ERR_UNSUPPORTED;
   if (B == 0) return PD_OK;  // empty batch: nothing to compute
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PD_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
@@ -97,8 +96,7 @@ const char* paged_decode_strerror(int32_t code) {
     case PD_ERR_ALIAS: return "out overlaps an input or the workspace";
     case PD_ERR_WORKSPACE: return "workspace missing or too small";
     case PD_ERR_UNSUPPORTED:
-      return "shape not supported (needs D 64|128, Hq/Hkv <= 32, block_size 16|32; FP8 caches: "
-             "D 128)";
+      return "shape not supported (needs D 64|128, Hq/Hkv <= 32, block_size 16|32)";
     case PD_ERR_HIP: return "HIP runtime rejected the launch";
     case PD_ERR_INTERNAL: return "internal error";
     case PD_ERR_VALUE: return "scale (and k_scale, v_scale) must be finite and positive";

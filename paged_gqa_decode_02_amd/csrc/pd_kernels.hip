@@ -67,8 +67,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kIdRegs = pd::kMaxWaveBlocks / 64;  // block ids per lane
-constexpr int kD8 = 128;                       // the head dim of the FP8 cache path
-constexpr uint32_t kRowBytes8 = kD8;           // one token row of one KV head, FP8
 constexpr uint32_t kOutOfBlock = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 data format
 constexpr int kStream = 2;                     // cache policy "nt": read once
@@ -201,21 +199,35 @@ struct Geo {
   static constexpr int kBlocks = D / 16;  // 16-dim output blocks (PV MFMAs)
 };
 static_assert(Geo<128>::kLdsTile == 8960 && Geo<64>::kLdsTile == 4480, "tile layout");
-// An FP8 cache (D = 128) stays in its codes in LDS: a tile is 16 rows of 128
-// bytes for K, then for V, as two 1 KiB groups each (8 rows per load
-// instruction, 8 lanes per row), groups 1040 bytes apart; chunk c of row r
-// sits at slot (c + (r & ~1)) mod 8. The tile path reads it in operand order
-// and widens in registers:
+// An FP8 cache stays in its codes in LDS: a tile is 16 rows of D bytes for
+// K, then for V, in 1 KiB groups of one load instruction each (64/(D/16)
+// rows: 8 rows of 128 bytes at D = 128, groups 1040 bytes apart; all 16 rows
+// of 64 bytes at D = 64, unpadded); the D/16 16-byte chunks of a row are
+// rotated: chunk c of row r of a group sits at slot (c + rot(r)) mod D/16,
+// rot(r) = r & ~1 at D = 128 and (0, 2, 1, 3)[r / 4] at D = 64. The tile
+// path reads it in operand order and widens in registers:
 //   K: ds_read_b64 of token lane%16, dims 32s + 8(lane/16) .. +8;
 //   V: ds_read_b64_tr_b8, source lane 16g + a + 2k giving token 4g + k%4,
 //      dims 16(m + k/4) + 8a .. +8, so that lane l receives dim 16m +
 //      l%16 of tokens 4(l/16)..+4 (bytes 0..3) and dim 16(m+1) + l%16 of
 //      the same tokens (bytes 4..7): two 16-dim blocks per read.
 // Within each half-wave these reads touch 32 distinct 8-byte bank slots
-// (no bank conflicts; measured with the LDS conflict counter).
-constexpr uint32_t kGroup8 = 1024 + 16;
-constexpr uint32_t kKTile8 = 2 * kGroup8;
-constexpr uint32_t kStage8 = 4 * kGroup8;  // 4160
+// (no bank conflicts; measured with the LDS conflict counter at D = 128).
+template <int D>
+struct Geo8 {
+  static constexpr uint32_t kRowBytes = D;                  // one FP8 row of one KV head
+  static constexpr int kChunks = D / 16;                    // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 64 / kChunks;         // rows per 1 KiB load
+  static constexpr int kGroups = kTileTok / kRowsPerLoad;   // loads per tile and tensor
+  static constexpr uint32_t kGroup = D == 128 ? 1024 + 16 : 1024;
+  static constexpr uint32_t kKTile = kGroups * kGroup;
+  static constexpr uint32_t kStage = 2 * kKTile;
+  // rotation of the chunks of row r (< kRowsPerLoad) of a group
+  __host__ __device__ static constexpr int rot(int r) {
+    return D == 128 ? (r & ~1) : (((r >> 2) & 1) << 1) | (r >> 3);
+  }
+};
+static_assert(Geo8<128>::kStage == 4160 && Geo8<64>::kStage == 2048, "FP8 tile layout");
 // the slice merge's per-wave scratch: G * (D + 2) floats for G <= 16
 template <int D>
 constexpr uint32_t merge_bytes() { return 16u * (D + 2) * 4u; }
@@ -227,7 +239,7 @@ constexpr uint32_t merge_bytes() { return 16u * (D + 2) * 4u; }
 #endif
 constexpr uint32_t kLdsBytes = 160 * 1024;
 template <int D, bool KV8>
-constexpr uint32_t stage_bytes() { return KV8 ? kStage8 : Geo<D>::kLdsTile; }
+constexpr uint32_t stage_bytes() { return KV8 ? Geo8<D>::kStage : Geo<D>::kLdsTile; }
 template <int D, bool KV8>
 constexpr int tile_buffers(int nw) {
   return PD_NBUF >= 3 && 3 * nw * stage_bytes<D, KV8>() <= kLdsBytes ? 3 : 2;
@@ -424,24 +436,26 @@ __device__ __forceinline__ uint32_t widen_pair(uint32_t x) {
 
 typedef __attribute__((address_space(3))) v2i32_t* lds_v2i32_ptr_t;
 
-// One 16-token FP8 tile (D = 128) at kt: K codes widened into the score
-// MFMA's A operand, V^T codes (two 16-dim blocks per transposing read)
-// widened into the PV operand; then the same math as the 16-bit tile.
-template <bool BF16>
-__device__ __forceinline__ void tile_compute_fp8(WaveState<kD8>& st, const char* kt,
-                                                 const u32x4 (&qb)[4], const uint32_t (&koff)[4],
-                                                 const uint32_t (&voff)[4], int tok_row0,
+// One 16-token FP8 tile at kt: K codes widened into the score MFMA's A
+// operand, V^T codes (two 16-dim blocks per transposing read) widened into
+// the PV operand; then the same math as the 16-bit tile.
+template <bool BF16, int D>
+__device__ __forceinline__ void tile_compute_fp8(WaveState<D>& st, const char* kt,
+                                                 const u32x4 (&qb)[D / 32],
+                                                 const uint32_t (&koff)[D / 32],
+                                                 const uint32_t (&voff)[D / 32], int tok_row0,
                                                  int tw1, bool partial, float c) {
-  u32x4 ka[4];
+  constexpr int kS = D / 32;
+  u32x4 ka[kS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < kS; ++s) {
     const u32x2_t x = *(const u32x2_t*)(kt + koff[s]);
     ka[s] = u32x4{widen_pair<BF16, false>(x[0]), widen_pair<BF16, true>(x[0]),
                   widen_pair<BF16, false>(x[1]), widen_pair<BF16, true>(x[1])};
   }
-  uint32_t v01[8], v23[8];
+  uint32_t v01[2 * kS], v23[2 * kS];
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
+  for (int mm = 0; mm < kS; ++mm) {
     const v2i32_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr_t)(kt + voff[mm]));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -449,7 +463,7 @@ __device__ __forceinline__ void tile_compute_fp8(WaveState<kD8>& st, const char*
       v23[2 * mm + u] = widen_pair<BF16, true>((uint32_t)x[u]);
     }
   }
-  tile_math<BF16, kD8>(st, ka, v01, v23, qb, tok_row0, tw1, partial, c);
+  tile_math<BF16, D>(st, ka, v01, v23, qb, tok_row0, tw1, partial, c);
 }
 
 // Block id number idx (< 256, wave-uniform) of the wave's range.
@@ -566,12 +580,12 @@ __device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu
 template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const KArgs a) {
-  static_assert(!KV8 || D == kD8, "the FP8 path is built for D = 128");
   using Gm = Geo<D>;
   constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
   constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
   constexpr int kNBuf = tile_buffers<D, KV8>(NW);
-  constexpr int kLoads = KV8 ? 4 : 2 * Gm::kGroups;  // load instructions per tile
+  using G8 = Geo8<D>;
+  constexpr int kLoads = KV8 ? 2 * G8::kGroups : 2 * Gm::kGroups;  // load instructions per tile
   constexpr int kWaitTile = waitcnt_vm((kNBuf - 1) * kLoads);
   constexpr uint32_t kStage = stage_bytes<D, KV8>();
   // one array per tile buffer, so the compiler can wait for exactly the
@@ -652,35 +666,38 @@ void pd_decode_kernel(const KArgs a) {
   const int nst = __builtin_amdgcn_readfirstlane(
       tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
-  constexpr uint32_t kRow = KV8 ? kRowBytes8 : Gm::kRowBytes;
-  constexpr int kChunks = KV8 ? 8 : Gm::kChunks;  // 16-byte chunks per row as loaded
+  constexpr uint32_t kRow = KV8 ? G8::kRowBytes : Gm::kRowBytes;
+  constexpr int kChunks = KV8 ? G8::kChunks : Gm::kChunks;  // 16-byte chunks per row as loaded
   const uint32_t tok_bytes = (a.Hkv / a.HS) * kRow;  // physical KV heads
   // global offsets of this lane's 16 bytes in load instruction 0 of a tile:
-  // a 16-bit row takes C lanes (64 / C rows per instruction), chunks
-  // rotated; an FP8 row takes 8 lanes (8 rows per instruction), in order
+  // a row takes C lanes (64 / C rows per instruction), the chunks in the
+  // rotated order of the tile layouts above
   const int lrow = lane / kChunks;
   const int lsl = lane % kChunks;
   const uint32_t head_off = (uint32_t)lrow * tok_bytes + (uint32_t)gk * kRow;
   const uint32_t koff_g =
-      head_off + (uint32_t)(KV8 ? (lsl - (lrow & ~1) + 8) % 8 : (lsl - lrow + kChunks) % kChunks) *
+      head_off + (uint32_t)(KV8 ? (lsl - G8::rot(lrow) + kChunks) % kChunks
+                                : (lsl - lrow + kChunks) % kChunks) *
                      16u;
   const uint32_t voff_g =
-      head_off +
-      (uint32_t)(KV8 ? (lsl - (lrow & ~1) + 8) % 8 : (lsl - 2 * lrow + 2 * kChunks) % kChunks) * 16u;
+      head_off + (uint32_t)(KV8 ? (lsl - G8::rot(lrow) + kChunks) % kChunks
+                                : (lsl - 2 * lrow + 2 * kChunks) % kChunks) *
+                     16u;
   // LDS offsets of the two read patterns (see the tile layouts above)
   uint32_t koff[kS], voff[kM];
-  uint32_t koff8[4], voff8[4];  // FP8 tiles
+  uint32_t koff8[kS], voff8[kS];  // FP8 tiles
   if constexpr (KV8) {
+    constexpr int R8 = G8::kRowsPerLoad;
     auto at = [](int t, int chunk, int half) -> uint32_t {
-      return (uint32_t)(t / 8) * kGroup8 + (uint32_t)(t % 8) * kRowBytes8 +
-             16u * (uint32_t)((chunk + ((t % 8) & ~1)) % 8) + 8u * (uint32_t)half;
+      return (uint32_t)(t / R8) * G8::kGroup + (uint32_t)(t % R8) * G8::kRowBytes +
+             16u * (uint32_t)((chunk + G8::rot(t % R8)) % G8::kChunks) + 8u * (uint32_t)half;
     };
 #pragma unroll
-    for (int s = 0; s < 4; ++s) koff8[s] = at(lane & 15, 2 * s + (row >> 1), row & 1);
+    for (int s = 0; s < kS; ++s) koff8[s] = at(lane & 15, 2 * s + (row >> 1), row & 1);
     const int j = lane & 15, a8 = j & 1, k8 = j >> 1;
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
-      voff8[mm] = kKTile8 + at(4 * row + (k8 & 3), 2 * mm + (k8 >> 2), a8);
+    for (int mm = 0; mm < kS; ++mm)
+      voff8[mm] = G8::kKTile + at(4 * row + (k8 & 3), 2 * mm + (k8 >> 2), a8);
   }
   {
     constexpr int C = Gm::kChunks, R = Gm::kRowsPerLoad;
@@ -721,8 +738,8 @@ void pd_decode_kernel(const KArgs a) {
       // turn the selects into a divergent branch around the loads (which
       // would issue a load twice and break the exact wait counts)
       asm("" : "+v"(ko), "+v"(vo));
-      const uint32_t kd = KV8 ? n * kGroup8 : n * Gm::kKGroup;
-      const uint32_t vd = KV8 ? kKTile8 + n * kGroup8 : Gm::kKTile + n * Gm::kVGroup;
+      const uint32_t kd = KV8 ? n * G8::kGroup : n * Gm::kKGroup;
+      const uint32_t vd = KV8 ? G8::kKTile + n * G8::kGroup : Gm::kKTile + n * Gm::kVGroup;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kt + kd), 16, ko, 0, 0, kStream);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(kt + vd), 16, vo, 0, 0, kStream);
     }
@@ -750,7 +767,7 @@ void pd_decode_kernel(const KArgs a) {
       if (j < nst) {
         const int tile0 = tw0 + kTileTok * j;
         if constexpr (KV8)
-          tile_compute_fp8<BF16>(st, tile_buf(d), qb, koff8, voff8, tile0 + 4 * row, tw1,
+          tile_compute_fp8<BF16, D>(st, tile_buf(d), qb, koff8, voff8, tile0 + 4 * row, tw1,
                                  tile0 + kTileTok > tw1, c);
         else
           tile_compute<BF16, D>(st, tile_buf(d), qb, koff, voff, tile0 + 4 * row, tw1,
@@ -940,12 +957,15 @@ hipError_t pick_dtype(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, boo
                : pick_block<false, false, KV8, D, FAST>(ka, grid, bs, nw, st);
 }
 
-// Instances: D = 64 and 128 for 16-bit caches, D = 128 for FP8 caches; each
-// with a compile-time epilogue for G <= 4 query heads per virtual KV head
-// (FAST) and a general one.
+// Instances: D = 64 and 128 for 16-bit and for FP8 caches; each with a
+// compile-time epilogue for G <= 4 query heads per virtual KV head (FAST)
+// and a general one.
 hipError_t pick_geometry(const KArgs& ka, dim3 grid, int bs, int nw, bool bf16, bool split,
                          bool kv8, int D, hipStream_t st) {
   const bool fast = ka.G <= 4;
+  if (kv8 && D == 64)
+    return fast ? pick_dtype<true, 64, true>(ka, grid, bs, nw, bf16, split, st)
+                : pick_dtype<true, 64, false>(ka, grid, bs, nw, bf16, split, st);
   if (kv8)
     return fast ? pick_dtype<true, 128, true>(ka, grid, bs, nw, bf16, split, st)
                 : pick_dtype<true, 128, false>(ka, grid, bs, nw, bf16, split, st);
@@ -990,14 +1010,13 @@ int32_t launch(const Launch& l) {
   ka.scale_log2 = l.scale * 1.4426950408889634f * (l.kv_fp8 ? l.k_scale : 1.0f);
   ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
-                 (l.kv_fp8 ? kRowBytes8 : 2u * (uint32_t)l.shape.D);
+                 (l.kv_fp8 ? 1u : 2u) * (uint32_t)l.shape.D;
   const dim3 grid(l.plan.splits, ka.Hkv / l.plan.heads_per_group, l.shape.B);
   const int nw = l.plan.heads_per_group * l.plan.slices;
   // each wave owns a tile's bytes of every tile buffer of its workgroup; the
   // slice merge needs G * (D + 2) floats of them per wave, so G <= 16
   if (nw < 1 || nw > kMaxWaves || hs < 1 || ka.Hkv % l.plan.heads_per_group != 0 ||
-      ka.G * ka.Hkv != l.shape.Hq || ka.G > 16 || (l.shape.D != 64 && l.shape.D != 128) ||
-      (l.kv_fp8 && l.shape.D != kD8))
+      ka.G * ka.Hkv != l.shape.Hq || ka.G > 16 || (l.shape.D != 64 && l.shape.D != 128))
     return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;

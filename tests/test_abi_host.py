@@ -222,13 +222,14 @@ def test_fp8_entry_point_empty_batch_is_a_no_op():
         CODES["PD_OK"]
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 64), (32, 1, 128), (28, 4, 128)])
-def test_fp8_entry_point_rejects_geometries_it_is_not_built_for(Hq, Hkv, D):
-    # the FP8 kernels are built for D = 128
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 64), (14, 2, 64), (32, 1, 128), (28, 4, 128),
+                                      (32, 8, 96), (32, 8, 256)])
+def test_fp8_entry_point_takes_the_16_bit_geometries(Hq, Hkv, D):
+    # the FP8 kernels are built for D = 64 and 128, like the 16-bit ones
     f = pd.lib.paged_decode_attention_fp8
     args = [BASE, BASE + (1 << 24), BASE + (2 << 24), BASE + (3 << 24), BASE + (3 << 24) + 4096,
             1, BASE + (4 << 24), 2, Hq, Hkv, D, 16, 0.125, BF16]
-    want = "PD_ERR_UNSUPPORTED" if D != 128 else "PD_ERR_NULL"
+    want = "PD_ERR_UNSUPPORTED" if D not in (64, 128) else "PD_ERR_NULL"
     if want == "PD_ERR_NULL":   # supported: make it fail on a null output instead of launching
         args[6] = 0
     assert f(*args, 1.0, 1.0, 0, 0, 0, 0) == CODES[want]

@@ -157,12 +157,35 @@ def test_fp8_binding_rejects_mismatched_inputs():
     assert e.value.code == 10
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(14, 2), (32, 1), (8, 8), (64, 8), (20, 1)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 128), (32, 1, 128), (8, 8, 128), (64, 8, 128),
+                                      (20, 1, 128), (14, 2, 64), (32, 8, 64), (32, 1, 64),
+                                      (8, 8, 64), (21, 1, 64)])
 @pytest.mark.parametrize("splits", [None, 3])
-def test_fp8_other_group_sizes(Hq, Hkv, splits):
-    # odd groups, MQA (two virtual KV heads), MHA, G = 8 and 20 at D = 128
+def test_fp8_other_group_sizes(Hq, Hkv, D, splits):
+    # odd groups, MQA (two or three virtual KV heads), MHA, G = 8 and 20 at
+    # D = 128, and the same kinds at D = 64 (the 14/2 D64 geometry included)
     lens = [1, 37, 700, 1024, 513, 0]
-    c = workloads.make_case(f"fp8_{Hq}x{Hkv}", len(lens), lens, dtype="bf16", block_size=16,
-                            Hq=Hq, Hkv=Hkv, seed=90 + Hq, kv_dtype="fp8")
+    c = workloads.make_case(f"fp8_{Hq}x{Hkv}_D{D}", len(lens), lens, dtype="bf16",
+                            block_size=16, Hq=Hq, Hkv=Hkv, D=D, seed=90 + Hq + D,
+                            scale=float(np.float32(1.0 / np.sqrt(D))), kv_dtype="fp8")
     note(f"{c.describe()} S={splits}")
     check_case(c, num_splits=splits, what=f"{c.name} S={splits}")
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 32)])
+def test_fp8_d64_every_tail(dtype, bs):
+    lens = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 300]
+    c = workloads.make_case(f"fp8_tails_D64_{dtype}_bs{bs}", len(lens), lens, dtype=dtype,
+                            block_size=bs, Hq=14, Hkv=2, D=64, seed=97,
+                            scale=float(np.float32(0.125)), kv_dtype="fp8")
+    note(c.describe())
+    for s in (None, 1, 2, 5):
+        check_case(c, num_splits=s, what=f"{c.name} S={s}")
+
+
+def test_fp8_d64_full_size():
+    # the 14/2 D64 geometry at B64 x 4,096 tokens over an FP8 cache, planned,
+    # every output against the oracle
+    c = workloads.geometry(14, 2, 64, 64, 4096, seed=0, kv_dtype="fp8")
+    note(c.describe())
+    check_case(c)
