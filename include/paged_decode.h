@@ -53,7 +53,7 @@
  *
  * Errors: every entry point returns PD_OK or one of the codes below and
  * writes nothing when it fails before launching. No C++ exception crosses
- * the ABI. Supported now: D = 64 or 128; any G = Hq / Hkv from 1 to 32
+ * the ABI. Supported now: D = 64 or 128; any G = Hq / Hkv from 1 to 128
  * (MHA, GQA with odd groups such as 14/2, MQA such as 32/1); block_size 16
  * or 32; dtype f16 or bf16. Other valid shapes return PD_ERR_UNSUPPORTED.
  */
@@ -81,7 +81,7 @@ extern "C" {
 #define PD_ERR_ALIGN 4         /* q/k/v/out not 16-byte, tables not 4-byte, workspace not 256-byte aligned */
 #define PD_ERR_ALIAS 5         /* out overlaps q, block_table, context_lens or the workspace */
 #define PD_ERR_WORKSPACE 6     /* workspace missing or smaller than required */
-#define PD_ERR_UNSUPPORTED 7   /* valid but not built (D, group size > 32, block size) */
+#define PD_ERR_UNSUPPORTED 7   /* valid but not built (D, group size > 128, block size) */
 #define PD_ERR_HIP 8           /* the HIP runtime rejected a launch */
 #define PD_ERR_INTERNAL 9      /* unexpected internal failure */
 #define PD_ERR_VALUE 10        /* scale is not a finite positive number */
@@ -186,7 +186,7 @@ size_t paged_decode_workspace_bytes_splits(int32_t B, int32_t Hq, int32_t Hkv, i
  * Errors as paged_decode_attention, plus PD_ERR_VALUE when k_scale or
  * v_scale is not finite and positive and PD_ERR_SHAPE for num_splits < 0.
  * The FP8 kernels take every geometry the 16-bit path takes (D 64 or 128,
- * group sizes 1 to 32, block size 16 or 32).
+ * group sizes 1 to 128, block size 16 or 32).
  */
 int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* block_table, const int32_t* context_lens,

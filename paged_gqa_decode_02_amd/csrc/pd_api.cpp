@@ -96,7 +96,7 @@ const char* paged_decode_strerror(int32_t code) {
     case PD_ERR_ALIAS: return "out overlaps an input or the workspace";
     case PD_ERR_WORKSPACE: return "workspace missing or too small";
     case PD_ERR_UNSUPPORTED:
-      return "shape not supported (needs D 64|128, Hq/Hkv <= 32, block_size 16|32)";
+      return "shape not supported (needs D 64|128, Hq/Hkv <= 128, block_size 16|32)";
     case PD_ERR_HIP: return "HIP runtime rejected the launch";
     case PD_ERR_INTERNAL: return "internal error";
     case PD_ERR_VALUE: return "scale (and k_scale, v_scale) must be finite and positive";

@@ -9,7 +9,7 @@ namespace pd {
 
 // Geometries the decode kernels are built for: head dim 64 or 128 (FP8
 // caches: 128), and up to kMaxGroup query heads per KV head.
-constexpr int kMaxGroup = 32;
+constexpr int kMaxGroup = 128;
 
 struct Shape {
   int32_t B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype;

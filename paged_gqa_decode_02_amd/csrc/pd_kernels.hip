@@ -5,8 +5,8 @@
 // a paged K/V cache; the G = Hq / Hkv query heads that share a KV head are
 // served by one pass over that head's K/V bytes, and a long context is cut
 // into partitions whose normalised partial outputs and log-sum-exps are
-// merged. Built for head dims D = 64 and 128 and any G up to 32 (MQA at
-// 32/1 included). The query heads of a wave fill the 16 columns of an MFMA
+// merged. Built for head dims D = 64 and 128 and any G up to 128 (MQA such
+// as 32/1 or 64/1 included). The query heads of a wave fill the 16 columns of an MFMA
 // block (spare columns repeat heads); a KV head with more than 16 query
 // heads is served by HS "virtual" KV heads of G / HS <= 16 query heads each,
 // whose waves sit in one workgroup and read the same K/V blocks together.

@@ -96,7 +96,7 @@ def test_plan_rejects_what_the_attention_call_rejects():
             pd.paged_decode_plan(1, 32, 8, D, 4, 16, BF16)
         assert e.value.code == CODES["PD_ERR_UNSUPPORTED"]
     with pytest.raises(pd.PagedDecodeError) as e:
-        pd.paged_decode_plan(1, 33, 1, 128, 4, 16, BF16)   # 33 query heads per KV head
+        pd.paged_decode_plan(1, 129, 1, 128, 4, 16, BF16)   # 129 query heads per KV head
     assert e.value.code == CODES["PD_ERR_UNSUPPORTED"]
     with pytest.raises(pd.PagedDecodeError) as e:
         pd.paged_decode_plan(1, 30, 8, 128, 4, 16, BF16)
@@ -134,7 +134,7 @@ def call(**over):
     (dict(dtype=5), "PD_ERR_DTYPE"),
     (dict(D=96), "PD_ERR_UNSUPPORTED"),
     (dict(D=256), "PD_ERR_UNSUPPORTED"),
-    (dict(Hq=8 * 33), "PD_ERR_UNSUPPORTED"),
+    (dict(Hq=8 * 129), "PD_ERR_UNSUPPORTED"),
     (dict(Hq=30), "PD_ERR_SHAPE"),
     (dict(bs=8), "PD_ERR_UNSUPPORTED"),
     (dict(bs=0), "PD_ERR_SHAPE"),

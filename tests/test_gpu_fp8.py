@@ -159,7 +159,7 @@ def test_fp8_binding_rejects_mismatched_inputs():
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 128), (32, 1, 128), (8, 8, 128), (64, 8, 128),
                                       (20, 1, 128), (14, 2, 64), (32, 8, 64), (32, 1, 64),
-                                      (8, 8, 64), (21, 1, 64)])
+                                      (8, 8, 64), (21, 1, 64), (64, 1, 128), (128, 1, 64)])
 @pytest.mark.parametrize("splits", [None, 3])
 def test_fp8_other_group_sizes(Hq, Hkv, D, splits):
     # odd groups, MQA (two or three virtual KV heads), MHA, G = 8 and 20 at

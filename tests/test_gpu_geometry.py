@@ -4,7 +4,8 @@ First, other KV-head counts with four query heads per KV head: KV heads pair
 up in a workgroup only when Hkv is even, and the planner's choices change
 with B * Hkv (one, two, three, four and sixteen KV heads). Then other group
 sizes and head dims: the Qwen2.5-style 14/2 at D 64, MQA 32/1 (two virtual
-KV heads of 16), MHA (G = 1), G = 2, 3, 5, 8, 16, 20 and D 64 at 32/8. All
+KV heads of 16), MHA (G = 1), G = 2, 3, 5, 8, 16, 20, up to 128 (eight
+virtual KV heads) and D 64 at 32/8. All
 with ragged (and empty) contexts that leave partial tiles, both dtypes and
 block sizes, the planned split count and forced ones.
 """
@@ -71,6 +72,10 @@ OTHER = [
     (21, 1, 128, "f16", 16),    # G = 21: three virtual KV heads of 7 (odd split)
     (17, 1, 64, "bf16", 32),    # G = 17 (prime): 17 virtual KV heads of 1
     (48, 2, 128, "bf16", 16),   # G = 24: two virtual KV heads of 12, two KV heads
+    (64, 1, 128, "bf16", 16),   # G = 64: four virtual KV heads of 16
+    (128, 1, 64, "f16", 32),    # G = 128: eight virtual KV heads of 16
+    (96, 2, 128, "bf16", 16),   # G = 48: three virtual KV heads of 16, two KV heads
+    (40, 1, 128, "f16", 16),    # G = 40: four virtual KV heads of 10
 ]
 
 

@@ -22,7 +22,8 @@ LENS = [1, 15, 16, 17, 100, 255, 256, 1000, 0, 33]
 
 GEOMS = [(32, 8, 128, "bf16", 16, ""), (32, 8, 128, "f16", 32, ""), (14, 2, 64, "bf16", 16, ""),
          (32, 1, 128, "f16", 16, ""), (21, 1, 128, "bf16", 32, ""), (17, 1, 64, "bf16", 16, ""),
-         (32, 8, 128, "bf16", 16, "fp8"), (32, 1, 128, "f16", 32, "fp8")]
+         (32, 8, 128, "bf16", 16, "fp8"), (32, 1, 128, "f16", 32, "fp8"),
+         (64, 1, 128, "bf16", 16, ""), (128, 1, 64, "f16", 16, "fp8")]
 
 
 def make(Hq, Hkv, D, dtype, bs, kv, seed, lens=LENS):

@@ -360,9 +360,9 @@ def test_matches_a_dense_numpy_formulation(dtype):
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(14, 2, 64), (32, 1, 64), (8, 8, 16), (20, 1, 32),
-                                     (6, 2, 128), (32, 1, 128)])
+                                     (6, 2, 128), (32, 1, 128), (64, 1, 64), (128, 1, 32)])
 def test_matches_the_dense_formulation_at_other_geometries(Hq, Hkv, D):
-    # odd group sizes (G = 7, 20, 3), MQA (G = 32), MHA (G = 1), D = 16..128:
+    # odd group sizes (G = 7, 20, 3), MQA (G = 32, 64, 128), MHA (G = 1), D = 16..128:
     # query head h reads KV head h // G
     G = Hq // Hkv
     c, dt = small_case(B=3, Hq=Hq, Hkv=Hkv, D=D, bs=8, ctx=(1, 9, 23), dtype="bf16", seed=G + D)

@@ -16,7 +16,7 @@ MAX_WAVE_BLOCKS, MAX_WAVES = 256, 8
 
 GEOMS = [(32, 8, 128), (32, 8, 64), (14, 2, 64), (32, 1, 128), (32, 1, 64), (8, 8, 128),
          (20, 1, 128), (64, 4, 64), (21, 1, 128), (17, 1, 64), (48, 2, 128), (64, 8, 128),
-         (28, 4, 128), (40, 8, 128)]
+         (28, 4, 128), (40, 8, 128), (64, 1, 128), (128, 1, 64), (96, 2, 128), (40, 1, 128)]
 BATCHES = (1, 2, 3, 8, 16, 32, 64, 256)
 CONTEXTS = (16, 48, 1000, 1024, 4096, 9306, 20001, 65536, 131072)
 
@@ -79,7 +79,7 @@ def test_fp8_plans_keep_the_partitions_of_the_16_bit_plan(probe):
 
 
 def test_the_planner_rejects_what_the_kernels_are_not_built_for(probe):
-    rows = [(1, 32, 8, 96, 4, 16, 1, 0, 0), (1, 33, 1, 128, 4, 16, 1, 0, 0),
+    rows = [(1, 32, 8, 96, 4, 16, 1, 0, 0), (1, 129, 1, 128, 4, 16, 1, 0, 0),
             (1, 32, 8, 128, 4, 8, 1, 0, 0), (1, 32, 8, 128, 4, 16, 2, 0, 0),
             (1, 30, 8, 128, 4, 16, 1, 0, 0), (65536, 32, 8, 128, 4, 16, 1, 0, 0)]
     st = [x[0] for x in probe(rows)]
