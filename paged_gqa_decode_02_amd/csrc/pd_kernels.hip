@@ -24,7 +24,7 @@
 //     access cannot leave the block; lanes past the context get an offset
 //     beyond the block and read nothing. Each 128-bit load instruction of a
 //     wave reads 1 KiB: four whole 256-byte rows (D = 128) or eight 128-byte
-//     rows (D = 64). One or two tiles stay in flight while the oldest is
+//     rows (D = 64) of 16-bit values, or eight or sixteen rows of FP8 codes. One or two tiles stay in flight while the oldest is
 //     computed; the loads use the streaming (nt) cache policy since every
 //     K/V byte is read once.
 //   * block ids: each lane loads up to four block-table entries of the
@@ -212,7 +212,8 @@ static_assert(Geo<128>::kLdsTile == 8960 && Geo<64>::kLdsTile == 4480, "tile lay
 //      l%16 of tokens 4(l/16)..+4 (bytes 0..3) and dim 16(m+1) + l%16 of
 //      the same tokens (bytes 4..7): two 16-dim blocks per read.
 // Within each half-wave these reads touch 32 distinct 8-byte bank slots
-// (no bank conflicts; measured with the LDS conflict counter at D = 128).
+// (no bank conflicts: measured with the LDS conflict counter at D = 128,
+// enumerated lane by lane at D = 64).
 template <int D>
 struct Geo8 {
   static constexpr uint32_t kRowBytes = D;                  // one FP8 row of one KV head
