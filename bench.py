@@ -437,8 +437,36 @@ def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls
     base = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": calls,
             "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
-                      f"{calls} oracle calls, fp64, {used} threads"}
+                      f"{calls} oracle calls, fp64, {used} threads",
+            "cpu_model": cpu_model()}
+    # one single-thread call on a smaller sample of the same sequences
+    n1 = max(1, min(nseq, 4))
+    t1 = time.perf_counter()
+    if case.fp8:
+        oracle.attention_fp8(case.q[:n1], case.k_cache, case.v_cache, case.block_table[:n1],
+                             case.context_lens[:n1], scale=case.scale, dtype=case.dtype,
+                             k_scale=case.k_scale, v_scale=case.v_scale, nthreads=1)
+    else:
+        oracle.attention(case.q[:n1], case.k_cache, case.v_cache, case.block_table[:n1],
+                         case.context_lens[:n1], scale=case.scale, dtype=case.dtype, nthreads=1)
+    dt1 = time.perf_counter() - t1
+    b1 = (2048 if case.fp8 else 4096) * int(case.context_lens[:n1].astype("int64").sum()) + 16384 * n1
+    base["single_thread"] = {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
+                             "seconds_per_call": round(dt1, 3), "sequences": n1}
     return base, ok, errs
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def launch_floor(torch, pd, iters=200):
