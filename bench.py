@@ -124,8 +124,38 @@ def time_calls(fn, iters: int, warmup: int, torch) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def time_graph(fn, iters: int, torch) -> float:
-    """Average ms per call when `iters` calls are captured in one HIP graph."""
+def time_samples(fn, iters: int, samples: int, torch, check=None) -> list:
+    """ms per call of each of `samples` back-to-back blocks of `iters` calls,
+    every block between its own pair of HIP events; `check()` (if given) runs
+    after each block, outside the timed span."""
+    out = []
+    for _ in range(samples):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / iters)
+        if check is not None:
+            check()
+    return out
+
+
+def sample_stats(ms_list) -> dict:
+    """Median, min and max µs per call over timing samples."""
+    us = sorted(m * 1e3 for m in ms_list)
+    n = len(us)
+    med = us[n // 2] if n % 2 else 0.5 * (us[n // 2 - 1] + us[n // 2])
+    return {"n": n, "median_us": round(med, 3), "min_us": round(us[0], 3),
+            "max_us": round(us[-1], 3)}
+
+
+def graph_of(fn, iters: int, torch):
+    """`iters` calls captured in one HIP graph, after three eager calls on the
+    capture stream; the graph has been replayed once."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -139,13 +169,29 @@ def time_graph(fn, iters: int, torch) -> float:
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
+    return g
+
+
+def time_graph(fn, iters: int, torch) -> float:
+    """Average ms per call when `iters` calls are captured in one HIP graph."""
+    return time_graph_samples(fn, iters, 1, torch)[0]
+
+
+def time_graph_samples(fn, iters: int, samples: int, torch, check=None) -> list:
+    """ms per call of each of `samples` replays of one graph of `iters` calls."""
+    g = graph_of(fn, iters, torch)
+    out = []
+    for _ in range(samples):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / iters)
+        if check is not None:
+            check()
+    return out
 
 
 def replicas_for(case, torch, pd, min_bytes=1 << 30):
@@ -160,7 +206,7 @@ def replicas_for(case, torch, pd, min_bytes=1 << 30):
     return reps, outs, wss, foot
 
 
-def bench_other(name, torch, pd, iters=200, warmup=20):
+def bench_other(name, torch, pd, iters=200, warmup=20, samples=7):
     case = make_workload(name)
     reps, outs, wss, foot = replicas_for(case, torch, pd)
     R = len(reps)
@@ -177,9 +223,11 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
     ok, chk = self_check(outs[0], first, torch)
     if not ok:
         return {"check": "FAIL", **chk}
-    ms = time_calls(call, iters, warmup, torch)
+    time_calls(call, iters, warmup, torch)
+    st = sample_stats(time_samples(call, iters, samples, torch))
     iters_g = max(R, (iters // R) * R)
-    ms_g = time_graph(call, iters_g, torch)
+    gt = sample_stats(time_graph_samples(call, iters_g, samples, torch))
+    ms, ms_g = st["median_us"] * 1e-3, gt["median_us"] * 1e-3
     S, P = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
                                 case.block_size, torch.bfloat16 if case.dtype == "bf16"
                                 else torch.float16)
@@ -189,7 +237,8 @@ def bench_other(name, torch, pd, iters=200, warmup=20):
            "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
            "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
            "algorithmic_bytes": nbytes, "splits": S, "partition_tokens": P,
-           "replicas": R, "rotated_bytes": R * foot, "check": chk}
+           "replicas": R, "rotated_bytes": R * foot, "check": chk,
+           "samples": {"calls_per_sample": iters, "stream": st, "graph": gt}}
     if case.fp8:
         res["kv_dtype"] = "fp8_e4m3fn"
     del reps, outs, wss
@@ -558,6 +607,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--samples", type=int, default=7,
+                    help="further timed blocks of --steps calls, stream and graph")
     ap.add_argument("--workload", default="large")
     ap.add_argument("--splits", type=int, default=None, help="force the split count")
     ap.add_argument("--seed", type=int, default=0)
@@ -577,6 +628,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py: this library runs on one GPU; there is no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+    if args.samples < 1 or args.steps < 1:
+        print("bench.py: --steps and --samples must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -617,7 +671,19 @@ def main():
     first = out.clone()
     ms = time_calls(call, args.steps, args.warmup, torch)
     torch.cuda.synchronize()
-    stable = bool(torch.equal(first.view(torch.int16), out.view(torch.int16)))
+    stable = [bool(torch.equal(first.view(torch.int16), out.view(torch.int16)))]
+
+    def same_bits():
+        stable.append(bool(torch.equal(first.view(torch.int16), out.view(torch.int16))))
+
+    # further samples of the same K calls, stream launches and then one graph
+    # of K calls replayed, each sample followed by a bit comparison of `out`
+    samp = {"calls_per_sample": args.steps,
+            "stream": sample_stats(time_samples(call, args.steps, args.samples, torch,
+                                                same_bits)),
+            "graph": sample_stats(time_graph_samples(call, args.steps, args.samples, torch,
+                                                     same_bits))}
+    stable = all(stable)
     nbytes = case.algorithmic_bytes()
     gbps = nbytes / (ms * 1e-3) / 1e9
 
@@ -639,7 +705,7 @@ def main():
                       "algorithmic_bytes": nbytes},
            "parity": {"ok": ok, "bitwise_stable_over_timed_calls": stable,
                       **{k2: round(v2, 6) for k2, v2 in err.items()}},
-           "roofline": roof}
+           "roofline": roof, "samples": samp}
     if not args.no_others:
         res["context"] = {"launch_floor": launch_floor(torch, pd), "d2d_copy_roof": copy_roof(torch)}
         others = {}
@@ -650,7 +716,7 @@ def main():
                      "geom_14x2_D64_B64_L4096", "geom_32x1_D128_B8_L4096",
                      "geom_32x1_D128_B64_L4096", "geom_32x1_D64_B64_L4096",
                      "geom_64x8_D128_B16_L4096", "geom_14x2_D64_B64_L4096_fp8"):
-            others[name] = bench_other(name, torch, pd)
+            others[name] = bench_other(name, torch, pd, samples=args.samples)
         res["others"] = others
         from workloads import rope as wrope
         table = pd.rope_cos_sin_table(32768, 128, wrope.QWEN_BASE)
