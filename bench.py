@@ -461,9 +461,10 @@ def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls
     share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     nthreads = max(1, min(16, share or 1))
     sub_cl = case.context_lens[:nseq]
-    calls, used = 0, 0
+    calls, used, times = 0, 0, []
     t0 = time.perf_counter()
     while calls < max_calls and (calls == 0 or time.perf_counter() - t0 < min_seconds):
+        tc = time.perf_counter()
         if case.fp8:
             ref, _, used = oracle.attention_fp8(case.q[:nseq], case.k_cache, case.v_cache,
                                                 case.block_table[:nseq], sub_cl, scale=case.scale,
@@ -476,7 +477,9 @@ def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls
                                             dtype=case.dtype, nthreads=nthreads,
                                             return_threads=True)
         calls += 1
-    dt = (time.perf_counter() - t0) / calls
+        times.append(time.perf_counter() - tc)
+    times.sort()
+    dt = times[calls // 2] if calls % 2 else 0.5 * (times[calls // 2 - 1] + times[calls // 2])
     nbytes = (2048 if case.fp8 else 4096) * int(sub_cl.astype("int64").sum()) + 16384 * nseq
     g = oracle.widen(gpu_bits[:nseq], case.dtype)
     err = np.abs(g - ref)
@@ -485,8 +488,9 @@ def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls
             "max_rel_gt_1e-2": float((err / np.maximum(np.abs(ref), 1e-2)).max())}
     base = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": calls,
+            "seconds_min": round(times[0], 3), "seconds_max": round(times[-1], 3),
             "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
-                      f"{calls} oracle calls, fp64, {used} threads",
+                      f"median of {calls} oracle calls, fp64, {used} threads",
             "cpu_model": cpu_model()}
     # one single-thread call on a smaller sample of the same sequences
     n1 = max(1, min(nseq, 4))
