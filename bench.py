@@ -206,6 +206,14 @@ def replicas_for(case, torch, pd, min_bytes=1 << 30):
     return reps, outs, wss, foot
 
 
+def overhead_bytes(case, S: int) -> dict:
+    """Bytes a call moves beyond the algorithmic ones (not counted in GB/s):
+    the block table and context lengths it reads, and at S > 1 the fp32
+    partial outputs and log-sum-exps, written once and read back once."""
+    return {"block_table": 4 * case.B * case.max_blocks_per_seq, "context_lens": 4 * case.B,
+            "split_workspace_each_way": 4 * case.B * case.Hq * S * (case.D + 1) if S > 1 else 0}
+
+
 def bench_other(name, torch, pd, iters=200, warmup=20, samples=7):
     case = make_workload(name)
     reps, outs, wss, foot = replicas_for(case, torch, pd)
@@ -236,8 +244,8 @@ def bench_other(name, torch, pd, iters=200, warmup=20, samples=7):
            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
            "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
-           "algorithmic_bytes": nbytes, "splits": S, "partition_tokens": P,
-           "replicas": R, "rotated_bytes": R * foot, "check": chk,
+           "algorithmic_bytes": nbytes, "overhead_bytes": overhead_bytes(case, S),
+           "splits": S, "partition_tokens": P, "replicas": R, "rotated_bytes": R * foot, "check": chk,
            "samples": {"calls_per_sample": iters, "stream": st, "graph": gt}}
     if case.fp8:
         res["kv_dtype"] = "fp8_e4m3fn"
@@ -706,7 +714,7 @@ def main():
                       "Hq": case.Hq, "Hkv": case.Hkv, "head_dim": case.D,
                       "block_size": case.block_size, "splits": S, "partition_tokens": P,
                       "kv_dtype": "fp8_e4m3fn" if case.fp8 else case.dtype,
-                      "algorithmic_bytes": nbytes},
+                      "algorithmic_bytes": nbytes, "overhead_bytes": overhead_bytes(case, S)},
            "parity": {"ok": ok, "bitwise_stable_over_timed_calls": stable,
                       **{k2: round(v2, 6) for k2, v2 in err.items()}},
            "roofline": roof, "samples": samp}
