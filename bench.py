@@ -12,9 +12,10 @@ bandwidth-bound large decode: batch 64, context 4,096, Hq/Hkv 32/8, D 128,
 bf16, block size 16, whose 1 GiB of K+V per call does not fit the 256 MB
 Infinity Cache, so every call streams from HBM.
 
-Before timing, the oracle leg (the fp64 CPU oracle, also timed as
-`cpu_baseline`) checks the output of the timed configuration on its sampled
-sequences; a case that fails is not timed. The secondary workloads get checks
+Before timing, one call of the fp64 CPU oracle checks the output of the
+timed configuration on its sampled sequences; a case that fails is not timed.
+After the GPU timing, further oracle calls on the same sequences give
+`cpu_baseline` (the median call). The secondary workloads get checks
 that need no oracle (finite, bit-for-bit repeatable); their parity is what
 the GPU tests cover.
 
@@ -459,41 +460,62 @@ def bench_blocks(name, torch, pd, iters=100, warmup=10):
     return res
 
 
-def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls: int = 25):
-    """The oracle leg: time the fp64 oracle on the first `nseq` sequences of
-    the workload, repeating the call until at least `min_seconds` have
-    passed, and hold the GPU output of those sequences to the parity tests'
-    allclose gate against the oracle's result. Returns (baseline, ok, errors)."""
+def _oracle_call(case, nseq: int, nthreads: int):
+    """One oracle call on the first `nseq` sequences; (result, threads used)."""
+    import oracle
+    cl = case.context_lens[:nseq]
+    if case.fp8:
+        ref, _, used = oracle.attention_fp8(case.q[:nseq], case.k_cache, case.v_cache,
+                                            case.block_table[:nseq], cl, scale=case.scale,
+                                            dtype=case.dtype, k_scale=case.k_scale,
+                                            v_scale=case.v_scale, nthreads=nthreads,
+                                            return_threads=True)
+    else:
+        ref, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
+                                        case.block_table[:nseq], cl, scale=case.scale,
+                                        dtype=case.dtype, nthreads=nthreads, return_threads=True)
+    return ref, used
+
+
+def oracle_threads() -> int:
+    share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(16, share or 1))
+
+
+def oracle_parity(case, gpu_bits, nseq: int):
+    """The parity gate of the oracle leg: one fp64 oracle call on the first
+    `nseq` sequences, the GPU output of those sequences held to the parity
+    tests' allclose gate. Returns (ok, errors, timing) where timing seeds the
+    baseline's call times."""
     import numpy as np
     import oracle
-    share = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    nthreads = max(1, min(16, share or 1))
-    sub_cl = case.context_lens[:nseq]
-    calls, used, times = 0, 0, []
+    nthreads = oracle_threads()
     t0 = time.perf_counter()
-    while calls < max_calls and (calls == 0 or time.perf_counter() - t0 < min_seconds):
-        tc = time.perf_counter()
-        if case.fp8:
-            ref, _, used = oracle.attention_fp8(case.q[:nseq], case.k_cache, case.v_cache,
-                                                case.block_table[:nseq], sub_cl, scale=case.scale,
-                                                dtype=case.dtype, k_scale=case.k_scale,
-                                                v_scale=case.v_scale, nthreads=nthreads,
-                                                return_threads=True)
-        else:
-            ref, _, used = oracle.attention(case.q[:nseq], case.k_cache, case.v_cache,
-                                            case.block_table[:nseq], sub_cl, scale=case.scale,
-                                            dtype=case.dtype, nthreads=nthreads,
-                                            return_threads=True)
-        calls += 1
-        times.append(time.perf_counter() - tc)
-    times.sort()
-    dt = times[calls // 2] if calls % 2 else 0.5 * (times[calls // 2 - 1] + times[calls // 2])
-    nbytes = (2048 if case.fp8 else 4096) * int(sub_cl.astype("int64").sum()) + 16384 * nseq
+    ref, used = _oracle_call(case, nseq, nthreads)
+    first = time.perf_counter() - t0
     g = oracle.widen(gpu_bits[:nseq], case.dtype)
     err = np.abs(g - ref)
     ok = bool(np.all(np.isfinite(g)) and np.all(err <= 1e-2 + 1e-2 * np.abs(ref)))
     errs = {"sequences_checked": int(nseq), "max_abs": float(err.max()),
             "max_rel_gt_1e-2": float((err / np.maximum(np.abs(ref), 1e-2)).max())}
+    return ok, errs, {"nseq": nseq, "nthreads": nthreads, "used": used, "times": [first]}
+
+
+def cpu_baseline(case, timing, min_seconds: float = 10.0, max_calls: int = 25):
+    """The oracle's timing: repeat the parity gate's call (same sequences,
+    same threads) until at least `min_seconds` of calls have passed, report
+    the median call, and add one single-thread call on a smaller sample."""
+    nseq, nthreads, used = timing["nseq"], timing["nthreads"], timing["used"]
+    times = list(timing["times"])
+    while len(times) < max_calls and sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        _, used = _oracle_call(case, nseq, nthreads)
+        times.append(time.perf_counter() - t0)
+    calls = len(times)
+    times.sort()
+    dt = times[calls // 2] if calls % 2 else 0.5 * (times[calls // 2 - 1] + times[calls // 2])
+    sub_cl = case.context_lens[:nseq]
+    nbytes = (2048 if case.fp8 else 4096) * int(sub_cl.astype("int64").sum()) + 16384 * nseq
     base = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle", "seconds_per_call": round(dt, 3), "calls": calls,
             "seconds_min": round(times[0], 3), "seconds_max": round(times[-1], 3),
@@ -503,18 +525,12 @@ def cpu_baseline(case, gpu_bits, nseq: int, min_seconds: float = 10.0, max_calls
     # one single-thread call on a smaller sample of the same sequences
     n1 = max(1, min(nseq, 4))
     t1 = time.perf_counter()
-    if case.fp8:
-        oracle.attention_fp8(case.q[:n1], case.k_cache, case.v_cache, case.block_table[:n1],
-                             case.context_lens[:n1], scale=case.scale, dtype=case.dtype,
-                             k_scale=case.k_scale, v_scale=case.v_scale, nthreads=1)
-    else:
-        oracle.attention(case.q[:n1], case.k_cache, case.v_cache, case.block_table[:n1],
-                         case.context_lens[:n1], scale=case.scale, dtype=case.dtype, nthreads=1)
+    _oracle_call(case, n1, 1)
     dt1 = time.perf_counter() - t1
     b1 = (2048 if case.fp8 else 4096) * int(case.context_lens[:n1].astype("int64").sum()) + 16384 * n1
     base["single_thread"] = {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
                              "seconds_per_call": round(dt1, 3), "sequences": n1}
-    return base, ok, errs
+    return base
 
 
 def cpu_model() -> str:
@@ -672,10 +688,10 @@ def main():
     call(0)
     torch.cuda.synchronize()
     # correctness before timing: the oracle leg checks the sampled sequences
-    ok, err, baseline = None, {}, None
+    ok, err, timing = None, {}, None
     if not args.no_cpu_baseline:
         bits = out.cpu().view(torch.int16).numpy().view("uint16")
-        baseline, ok, err = cpu_baseline(case, bits, min(args.cpu_seqs, case.B))
+        ok, err, timing = oracle_parity(case, bits, min(args.cpu_seqs, case.B))
         if not ok:
             print(json.dumps({"metric": METRIC, "error": "parity check failed", **err}))
             sys.exit(1)
@@ -734,8 +750,8 @@ def main():
         table = pd.rope_cos_sin_table(32768, 128, wrope.QWEN_BASE)
         res["rope_kv_write"] = {n: bench_rope(n, torch, pd, table) for n in ROPE_CASES}
         res["kv_block_moves"] = {n: bench_blocks(n, torch, pd) for n in BLOCK_CASES}
-    if baseline is not None:
-        res["cpu_baseline"] = baseline
+    if timing is not None:  # the oracle's timing repeats run after the GPU's
+        res["cpu_baseline"] = cpu_baseline(case, timing)
     print(json.dumps(res), flush=True)
 
 
