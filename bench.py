@@ -636,7 +636,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--samples", type=int, default=7,
-                    help="further timed blocks of --steps calls, stream and graph")
+                    help="further timed blocks of --steps calls, stream and graph "
+                         "(0: none, only the timed block)")
     ap.add_argument("--workload", default="large")
     ap.add_argument("--splits", type=int, default=None, help="force the split count")
     ap.add_argument("--seed", type=int, default=0)
@@ -657,8 +658,8 @@ def main():
         print("bench.py: this library runs on one GPU; there is no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         sys.exit(2)
-    if args.samples < 1 or args.steps < 1:
-        print("bench.py: --steps and --samples must be at least 1", file=sys.stderr)
+    if args.samples < 0 or args.steps < 1:
+        print("bench.py: --steps must be at least 1 and --samples at least 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -706,11 +707,13 @@ def main():
 
     # further samples of the same K calls, stream launches and then one graph
     # of K calls replayed, each sample followed by a bit comparison of `out`
-    samp = {"calls_per_sample": args.steps,
-            "stream": sample_stats(time_samples(call, args.steps, args.samples, torch,
-                                                same_bits)),
-            "graph": sample_stats(time_graph_samples(call, args.steps, args.samples, torch,
-                                                     same_bits))}
+    samp = None
+    if args.samples > 0:
+        samp = {"calls_per_sample": args.steps,
+                "stream": sample_stats(time_samples(call, args.steps, args.samples, torch,
+                                                    same_bits)),
+                "graph": sample_stats(time_graph_samples(call, args.steps, args.samples, torch,
+                                                         same_bits))}
     stable = all(stable)
     nbytes = case.algorithmic_bytes()
     gbps = nbytes / (ms * 1e-3) / 1e9
