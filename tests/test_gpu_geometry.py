@@ -76,6 +76,12 @@ OTHER = [
     (128, 1, 64, "f16", 32),    # G = 128: eight virtual KV heads of 16
     (96, 2, 128, "bf16", 16),   # G = 48: three virtual KV heads of 16, two KV heads
     (40, 1, 128, "f16", 16),    # G = 40: four virtual KV heads of 10
+    (12, 2, 128, "bf16", 16),   # G = 6
+    (72, 8, 128, "bf16", 32),   # G = 9
+    (11, 1, 128, "bf16", 16),   # G = 11 (prime, one wave of 11 heads)
+    (30, 2, 64, "f16", 16),     # G = 15
+    (33, 1, 64, "bf16", 16),    # G = 33: three virtual KV heads of 11
+    (100, 1, 128, "f16", 16),   # G = 100: ten virtual KV heads of 10
 ]
 
 
