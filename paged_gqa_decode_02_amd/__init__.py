@@ -67,6 +67,16 @@ class PagedDecodeError(RuntimeError):
         super().__init__(f"{STATUS_NAMES.get(self.code, self.code)}: {paged_decode_strerror(self.code)}")
 
 
+def _on_gpu(dev, **tensors):
+    """Every given tensor must live on the GPU `dev`: the library takes device
+    pointers only, and a host pointer reaching a kernel faults the GPU."""
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, not {dev}")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be a GPU tensor on {dev} (got {t.device})")
+
+
 def paged_decode_abi_version() -> int:
     return int(lib.paged_decode_abi_version())
 
@@ -108,6 +118,9 @@ def _shape(q, k_cache, block_table):
 
 def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
     """Zero a workspace on the current (or given) stream with the library's fill kernel."""
+    _on_gpu(workspace.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     st = stream if stream is not None else torch.cuda.current_stream(workspace.device)
     handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
     rc = lib.paged_decode_workspace_init(workspace.data_ptr(),
@@ -123,6 +136,15 @@ def alloc_workspace(q, k_cache, block_table, num_splits=None) -> torch.Tensor:
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     paged_decode_workspace_init(ws)
     return ws
+
+
+def _checked_out(q, out):
+    """`out` as given (same shape and dtype as q, contiguous) or a new one."""
+    if out is None:
+        return torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    return out
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=None, *,
@@ -148,12 +170,15 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=N
     B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
     if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
-    if out is None:
-        out = torch.empty_like(q)
+    _on_gpu(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+            context_lens=context_lens, out=out, workspace=workspace)
+    out = _checked_out(q, out)
     if scale is None:
         scale = D ** -0.5
     if workspace is None:
         workspace = alloc_workspace(q, k_cache, block_table, num_splits)
+    elif not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
     args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
@@ -198,12 +223,15 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, o
     B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
     if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
-    if out is None:
-        out = torch.empty_like(q)
+    _on_gpu(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+            context_lens=context_lens, out=out, workspace=workspace)
+    out = _checked_out(q, out)
     if scale is None:
         scale = D ** -0.5
     if workspace is None:
         workspace = alloc_workspace(q, k_cache, block_table, num_splits)
+    elif not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
     rc = lib.paged_decode_attention_fp8(
@@ -239,6 +267,7 @@ def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=Non
     embedding (``rope_cos_sin_table``), built on the GPU."""
     if out is None:
         out = torch.empty((max_position, rotary_dim), dtype=torch.float32, device=device)
+    _on_gpu(out.device)
     if out.dtype != torch.float32 or not out.is_contiguous() or \
             tuple(out.shape) != (max_position, rotary_dim):
         raise ValueError("out must be a contiguous float32 [max_position, rotary_dim] tensor")
@@ -260,6 +289,8 @@ def _rows(name, t, H, D):
 
 def _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out, fp8):
     """Checked pointer and size arguments shared by the two RoPE writes."""
+    _on_gpu(q.device, k=k, v=v, positions=positions, slot_mapping=slot_mapping, cos_sin=cos_sin,
+            k_cache=k_cache, v_cache=v_cache, q_out=q_out)
     if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype, float16 or bfloat16")
     if fp8:
@@ -340,6 +371,7 @@ lib.paged_kv_remap_block_table.restype = _I
 
 def _pool(k_cache, v_cache):
     """(num_blocks, block_bytes, v pointer) of a cache pair; v_cache may be None."""
+    _on_gpu(k_cache.device, v_cache=v_cache)
     if not k_cache.is_contiguous() or k_cache.dim() < 1:
         raise ValueError("k_cache must be a contiguous [num_blocks, ...] tensor")
     if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype
@@ -360,6 +392,7 @@ def paged_kv_copy_blocks(k_cache, v_cache, pairs, *, stream=None):
     """Block pairs[i, 1] of each cache becomes a copy of block pairs[i, 0]
     (``paged_kv_copy_blocks``); pairs: device int32 [n, 2]. In place."""
     nb, bb, vp = _pool(k_cache, v_cache)
+    _on_gpu(k_cache.device, pairs=pairs)
     _ids(pairs, "pairs")
     if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be [n, 2]")
@@ -380,6 +413,7 @@ def paged_kv_gather_blocks(k_cache, v_cache, ids, k_out=None, v_out=None, *, str
         k_out = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
     if v_cache is not None and v_out is None:
         v_out = torch.empty(shape, dtype=k_cache.dtype, device=k_cache.device)
+    _on_gpu(k_cache.device, ids=ids, k_out=k_out, v_out=v_out)
     for t in (k_out, v_out):
         if t is not None and (tuple(t.shape) != shape or t.dtype != k_cache.dtype
                               or not t.is_contiguous()):
@@ -400,6 +434,7 @@ def paged_kv_scatter_blocks(k_in, v_in, ids, k_cache, v_cache, *, stream=None):
     _ids(ids, "ids")
     n = int(ids.numel())
     shape = (n,) + tuple(k_cache.shape[1:])
+    _on_gpu(k_cache.device, ids=ids, k_in=k_in, v_in=v_in)
     for t in (k_in, v_in):
         if t is not None and (tuple(t.shape) != shape or t.dtype != k_cache.dtype
                               or not t.is_contiguous()):
@@ -431,6 +466,7 @@ def paged_kv_compact_plan(live):
 def paged_kv_remap_block_table(block_table, remap, *, stream=None):
     """In place: every entry e of the device int32 block table with
     0 <= e < len(remap) becomes remap[e] (``paged_kv_remap_block_table``)."""
+    _on_gpu(block_table.device, remap=remap)
     _ids(block_table, "block_table")
     _ids(remap, "remap")
     rc = lib.paged_kv_remap_block_table(block_table.data_ptr(), int(block_table.numel()),
