@@ -446,8 +446,32 @@ def bench_blocks(name, torch, pd, iters=100, warmup=10):
             pd.paged_kv_copy_blocks(kc, vc, pairs)
             pd.paged_kv_remap_block_table(table, remap)
         nbytes = 2 * 2 * n * bb + 8 * n + 8 * table.numel() + 4 * nb
+    kc0, vc0 = pools[0]
+    if kind == "compact":
+        before = (kc0.clone(), vc0.clone())
     call(0)
     torch.cuda.synchronize()
+
+    def same(a, b):
+        return bool(torch.equal(a.view(torch.int16), b.view(torch.int16)))
+
+    # oracle-free check of the first call: every moved block holds its
+    # source's bytes (and the remapped table its new ids)
+    if kind == "copy":
+        src, dst = pairs[:, 0].long(), pairs[:, 1].long()
+        res["check"] = {"blocks_copied_exactly": same(kc0[dst], kc0[src]) and
+                        same(vc0[dst], vc0[src])}
+    elif kind in ("gather", "scatter"):
+        ko, vo = bufs[0]
+        res["check"] = {"blocks_moved_exactly": same(kc0[ids.long()], ko) and
+                        same(vc0[ids.long()], vo)}
+    else:
+        src, dst = pairs[:, 0].long(), pairs[:, 1].long()
+        want = np.where(bt >= 0, remap_h.numpy()[np.maximum(bt, 0)], bt)
+        res["check"] = {"blocks_copied_exactly": same(kc0[dst], before[0][src]) and
+                        same(vc0[dst], before[1][src]),
+                        "table_remapped": bool(np.array_equal(table.cpu().numpy(), want))}
+        del before
     ms = time_calls(call, iters, warmup, torch)
     ms_g = time_graph(call, iters, torch)
     res.update({"blocks": n, "us_per_call": round(ms * 1e3, 3),
