@@ -40,7 +40,9 @@
  * 0 <= context_lens[b] <= max_blocks_per_seq * block_size, and every block
  * id the first ceil(L / block_size) entries of a row hold is in
  * [0, num_blocks). Entries past those, and cache slots at or after L in the
- * last block, are never read.
+ * last block, are never read. Outside that range the kernels still read
+ * only the row: a length above max_blocks_per_seq * block_size is taken as
+ * that, and a negative length as 0 (zero output rows).
  *
  * Workspace contract (split plans, S > 1): the first 256 KiB of a
  * workspace hold arrival counters, at every shape, and must be zero when a

@@ -642,8 +642,9 @@ void pd_decode_kernel(const KArgs a) {
   for (int m = 0; m < kM; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // wave-uniform by construction; readfirstlane lets the compiler keep the
-  // loop bounds and block addresses in scalar registers
-  const int L = __builtin_amdgcn_readfirstlane(a.cl[b]);
+  // loop bounds and block addresses in scalar registers. A length past the
+  // row's MB blocks counts as MB blocks (a negative one is an empty context).
+  const int L = min(__builtin_amdgcn_readfirstlane(a.cl[b]), a.MB * BS);
   if constexpr (!SPLIT) {
     if (L <= 0) {
       // empty context: zero rows for every query head of the group

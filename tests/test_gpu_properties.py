@@ -104,3 +104,44 @@ def test_outputs_lie_within_the_range_of_the_valid_values(geom, splits):
             slack = ulp * np.maximum(np.abs(lo), np.abs(hi)) + 1e-30
             x = g_val[b, g * G:(g + 1) * G]
             assert np.all(x >= lo - slack) and np.all(x <= hi + slack), (b, g, splits)
+
+
+@pytest.mark.parametrize("splits", [None, 1, 3])
+@pytest.mark.parametrize("geom", [GEOMS[0], GEOMS[3], GEOMS[6]], ids=geom_id)
+def test_lengths_outside_the_row_count_as_its_bounds(geom, splits):
+    # a length above the row's capacity (max_blocks_per_seq * block_size) is
+    # taken as the capacity and a negative one as 0: the outputs equal those
+    # of the lengths at the bounds, and the split counters stay clean (the
+    # same workspace then gives the in-range call's bits again)
+    import torch
+    import paged_gqa_decode_02_amd as pd
+    Hq, Hkv, D, dtype, bs, kv = geom
+    MB = 6
+    cap = MB * bs
+    c = workloads.make_case(f"bounds_{Hq}x{Hkv}_{dtype}_bs{bs}{'_' + kv if kv else ''}", 5,
+                            [cap, cap, 7, 0, cap - 1], dtype=dtype, block_size=bs, Hq=Hq,
+                            Hkv=Hkv, D=D, seed=91, max_blocks_per_seq=MB,
+                            scale=float(np.float32(1.0 / np.sqrt(D))), kv_dtype=kv)
+    print(f"{c.describe()} S={splits}", flush=True)
+    from helpers import device_case
+    q, k, v, bt, cl = device_case(c)
+    ws = pd.alloc_workspace(q, k, bt, splits)
+
+    def call(lens):
+        out = torch.full_like(q, float("nan"))
+        if kv:
+            pd.paged_decode_attention_fp8(q, k, v, bt, lens, out, k_scale=c.k_scale,
+                                          v_scale=c.v_scale, scale=c.scale, workspace=ws,
+                                          num_splits=splits)
+        else:
+            pd.paged_decode_attention(q, k, v, bt, lens, out, scale=c.scale, workspace=ws,
+                                      num_splits=splits)
+        torch.cuda.synchronize()
+        return out_bits(out)
+
+    base = call(cl)
+    ref, _ = oracle.attention_case(c)
+    compare(base, ref, c.dtype, what=c.name)
+    wild = torch.tensor([cap + 17, 2**31 - 1, 7, -7, cap - 1], dtype=torch.int32, device="cuda")
+    assert np.array_equal(call(wild), base)
+    assert np.array_equal(call(cl), base)
