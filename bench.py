@@ -367,14 +367,17 @@ def bench_rope(name, torch, pd, table, iters=200, warmup=20):
         ok, chk = rope_check(case, base[0], base[5], base[2], torch)
     if not ok:
         return {"check": "FAIL", **chk}
-    ms = time_calls(call, iters, warmup, torch)
-    ms_g = time_graph(call, max(R, (iters // R) * R), torch)
+    time_calls(call, iters, warmup, torch)
+    st = sample_stats(time_samples(call, iters, 7, torch))
+    gt = sample_stats(time_graph_samples(call, max(R, (iters // R) * R), 7, torch))
+    ms, ms_g = st["median_us"] * 1e-3, gt["median_us"] * 1e-3
     nbytes = case.algorithmic_bytes(1 if fp8 else 2)
     res = {"tokens": case.T, "us_per_call": round(ms * 1e3, 3),
            "us_per_call_graph": round(ms_g * 1e3, 3),
            "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
            "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
-           "algorithmic_bytes": nbytes, "replicas": R, "check": chk}
+           "algorithmic_bytes": nbytes, "replicas": R, "check": chk,
+           "samples": {"calls_per_sample": iters, "stream": st, "graph": gt}}
     del reps, base
     torch.cuda.empty_cache()
     return res
@@ -472,13 +475,16 @@ def bench_blocks(name, torch, pd, iters=100, warmup=10):
                         same(vc0[dst], before[1][src]),
                         "table_remapped": bool(np.array_equal(table.cpu().numpy(), want))}
         del before
-    ms = time_calls(call, iters, warmup, torch)
-    ms_g = time_graph(call, iters, torch)
+    time_calls(call, iters, warmup, torch)
+    st = sample_stats(time_samples(call, iters, 7, torch))
+    gt = sample_stats(time_graph_samples(call, iters, 7, torch))
+    ms, ms_g = st["median_us"] * 1e-3, gt["median_us"] * 1e-3
     res.update({"blocks": n, "us_per_call": round(ms * 1e3, 3),
                 "us_per_call_graph": round(ms_g * 1e3, 3),
                 "GBps_graph": round(nbytes / (ms_g * 1e-3) / 1e9, 1),
                 "frac_of_peak_graph": round(nbytes / (ms_g * 1e-3) / 1e9 / PEAK_GBPS, 4),
-                "algorithmic_bytes": nbytes})
+                "algorithmic_bytes": nbytes,
+                "samples": {"calls_per_sample": iters, "stream": st, "graph": gt}})
     del pools
     torch.cuda.empty_cache()
     return res
