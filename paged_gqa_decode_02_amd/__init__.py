@@ -382,7 +382,7 @@ def _pool(k_cache, v_cache):
     return nb, bb, (v_cache.data_ptr() if v_cache is not None else None)
 
 
-def _ids(t, name, n=None):
+def _ids(t, name):
     if t.dtype != torch.int32 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int32 tensor")
     return t
