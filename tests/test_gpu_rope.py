@@ -6,6 +6,8 @@ rotated q_out and cached keys within the decode path's gates (allclose
 1e-2 + 1e-2|r| and one ulp of RNE(r)) of the unrounded fp64 rotation; the
 cached values bit-exact; every cache slot the call does not name unchanged,
 bit for bit."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -299,3 +301,35 @@ def test_fp8_write_then_fp8_decode(bs):
                                       scale=dec.scale, dtype="bf16", k_scale=dec.k_scale,
                                       v_scale=dec.v_scale)
         compare(out_bits(out), ref, "bf16", what=f"feed8 decode S={s}")
+
+
+def test_positions_and_slots_outside_their_arrays_are_skipped():
+    # the kernel's own bounds checks: a token whose position is outside the
+    # table writes nothing (its q_out row keeps what it held, no K/V); one
+    # whose slot is past the pool writes its rotated q but no K/V, as a
+    # padding token does. Everything else matches the oracle run on the
+    # tokens with valid positions, the bad slots taken as padding.
+    case = wrope.scatter(40, max_position=4096, seed=77)
+    print(case.describe(), "positions/slots out of range", flush=True)
+    T = case.T
+    nslots = case.k_cache.shape[0] * case.block_size
+    bad_pos, bad_slot = np.array([3, 17, 30]), np.array([5, 22])
+    pos, slots = case.positions.copy(), case.slot_mapping.copy()
+    pos[bad_pos] = [case.max_position, -1, 2**31 - 1]
+    slots[bad_slot] = [nslots, 2**31 - 1]
+    qkv = to_dev(case.qkv, case.dtype)
+    q, k, v = qkv[:, :case.Hq], qkv[:, case.Hq:case.Hq + case.Hkv], qkv[:, case.Hq + case.Hkv:]
+    kc, vc = (to_dev(a, case.dtype) for a in (case.k_cache, case.v_cache))
+    sentinel = np.full((T, case.Hq, case.D), 0x1234, np.uint16)
+    qo = to_dev(sentinel, case.dtype)
+    pd.rope_paged_kv_write(q, k, v, torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(),
+                           gpu_table(case.max_position, case.D, case.base), kc, vc, q_out=qo)
+    torch.cuda.synchronize()
+    got_q, got_k, got_v = out_bits(qo), out_bits(kc), out_bits(vc)
+    assert np.all(got_q[bad_pos] == 0x1234)
+    keep = np.setdiff1d(np.arange(T), bad_pos)
+    s2 = case.slot_mapping.copy()
+    s2[bad_slot] = -1
+    sub = dataclasses.replace(case, T=len(keep), qkv=case.qkv[keep], positions=case.positions[keep],
+                              slot_mapping=s2[keep])
+    check_write(sub, (got_q[keep], got_k, got_v))
