@@ -67,14 +67,48 @@ class PagedDecodeError(RuntimeError):
         super().__init__(f"{STATUS_NAMES.get(self.code, self.code)}: {paged_decode_strerror(self.code)}")
 
 
+# The raw HIP stream handle of a device's current stream, without building a
+# torch Stream object per call.
+_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
+def _gpu_index(t, name) -> int:
+    """Index of the GPU holding `t`; a host tensor is refused (the library
+    takes device pointers only, and a host pointer reaching a kernel faults
+    the GPU)."""
+    d = t.get_device()
+    if d < 0:
+        raise ValueError(f"{name} must be a GPU tensor, not on {t.device}")
+    return d
+
+
+def _same_gpu(dev, **tensors):
+    """Every given tensor (None skipped) lives on GPU `dev`."""
+    for name, t in tensors.items():
+        if t is not None and t.get_device() != dev:
+            raise ValueError(f"{name} must be a GPU tensor on cuda:{dev} (got {t.device})")
+
+
 def _on_gpu(dev, **tensors):
-    """Every given tensor must live on the GPU `dev`: the library takes device
-    pointers only, and a host pointer reaching a kernel faults the GPU."""
+    """As _same_gpu, for a torch.device `dev`."""
     if dev.type != "cuda":
         raise ValueError(f"tensors must be on a GPU, not {dev}")
-    for name, t in tensors.items():
-        if t is not None and t.device != dev:
-            raise ValueError(f"{name} must be a GPU tensor on {dev} (got {t.device})")
+    _same_gpu(dev.index if dev.index is not None else torch.cuda.current_device(), **tensors)
+
+
+def _stream_handle(stream, dev: int) -> int:
+    """HIP stream handle: the given stream (a torch stream or a raw handle) or
+    the device's current stream."""
+    if stream is None:
+        return _raw_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _stream_object(stream):
+    """A torch stream for `stream` (a torch stream or a raw handle)."""
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
 
 
 def paged_decode_abi_version() -> int:
@@ -110,6 +144,20 @@ def paged_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks_per_seq, block_size, 
                                                        block_size, dt, int(num_splits)))
 
 
+_NEED = {}  # (shape, dtype, num_splits) -> workspace bytes (a pure function of them)
+
+
+def _workspace_need(B, Hq, Hkv, D, MB, bs, dt, num_splits) -> int:
+    key = (B, Hq, Hkv, D, MB, bs, dt, num_splits)
+    n = _NEED.get(key)
+    if n is None:
+        n = paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, bs, dt, num_splits)
+        if len(_NEED) > 4096:
+            _NEED.clear()
+        _NEED[key] = n
+    return n
+
+
 def _shape(q, k_cache, block_table):
     B, Hq, D = q.shape
     _, bs, Hkv, _ = k_cache.shape
@@ -118,33 +166,128 @@ def _shape(q, k_cache, block_table):
 
 def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
     """Zero a workspace on the current (or given) stream with the library's fill kernel."""
-    _on_gpu(workspace.device)
+    dev = _gpu_index(workspace, "workspace")
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
-    st = stream if stream is not None else torch.cuda.current_stream(workspace.device)
-    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
     rc = lib.paged_decode_workspace_init(workspace.data_ptr(),
-                                         workspace.numel() * workspace.element_size(), handle)
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream, dev))
     if rc != PD_OK:
         raise PagedDecodeError(rc)
 
 
-def alloc_workspace(q, k_cache, block_table, num_splits=None) -> torch.Tensor:
-    """A zeroed device workspace of the size the call needs (at least 256 bytes)."""
+def alloc_workspace(q, k_cache, block_table, num_splits=None, stream=None) -> torch.Tensor:
+    """A zeroed device workspace of the size the call needs (at least 256
+    bytes), allocated and zeroed on the current (or given) stream."""
     B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
-    n = paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, bs, q.dtype, num_splits)
-    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-    paged_decode_workspace_init(ws)
+    _gpu_index(q, "q")
+    n = _workspace_need(B, Hq, Hkv, D, MB, bs, _DTYPE_CODE.get(q.dtype, q.dtype), num_splits)
+    if stream is None:
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+        paged_decode_workspace_init(ws)
+        return ws
+    with torch.cuda.stream(_stream_object(stream)):
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+        paged_decode_workspace_init(ws, stream)
     return ws
 
 
-def _checked_out(q, out):
-    """`out` as given (same shape and dtype as q, contiguous) or a new one."""
+# Workspaces the binding supplies when the caller gives none: one per (GPU,
+# stream), grown when a call needs more and never freed, so that a graph that
+# captured a call keeps a valid pointer. Calls on one stream run in order and
+# leave the counters zero, so they can share it; calls on different streams
+# use different workspaces.
+_WS = {}
+_WS_RETIRED = []
+
+
+def _auto_workspace(q, need, dev, stream):
+    """(pointer, bytes) of a zeroed workspace of at least `need` bytes for a
+    call on `stream` (None: the current stream), or (0, 0) when none is needed."""
+    if need == 0:
+        return 0, 0
+    if stream is not None or torch.cuda.is_current_stream_capturing():
+        # an explicit stream, or a capture: a workspace of this call's own,
+        # allocated and zeroed on the stream the call runs on
+        ws = alloc_workspace_bytes(need, q.device, stream)
+        return ws.data_ptr(), ws.numel(), ws
+    key = (dev, _raw_stream(dev))
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < need:
+        if ws is not None:
+            _WS_RETIRED.append(ws)
+        ws = alloc_workspace_bytes(need, q.device, None)
+        _WS[key] = ws
+    return ws.data_ptr(), ws.numel(), ws
+
+
+def alloc_workspace_bytes(nbytes, device, stream=None) -> torch.Tensor:
+    """A zeroed uint8 device workspace of `nbytes` (at least 256), allocated
+    and zeroed on the current (or given) stream."""
+    n = max(int(nbytes), 256)
+    if stream is None:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        paged_decode_workspace_init(ws)
+        return ws
+    with torch.cuda.stream(_stream_object(stream)):
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        paged_decode_workspace_init(ws, stream)
+    return ws
+
+
+_DECODE_NAMES = ("q", "k_cache", "v_cache", "block_table", "context_lens")
+
+
+def _decode_prep(q, k_cache, v_cache, block_table, context_lens, out, workspace, stream,
+                 num_splits, fp8):
+    """Checks that keep a bad argument from reaching a kernel (host or other-GPU
+    tensors, layouts the library cannot see), then `out` and the workspace.
+    Shape rules the C ABI itself checks are left to it. Returns (dims, dev,
+    out, workspace pointer, workspace bytes, keep-alive)."""
+    dev = _gpu_index(q, "q")
+    for name, t in zip(_DECODE_NAMES, (q, k_cache, v_cache, block_table, context_lens)):
+        if t.get_device() != dev:
+            raise ValueError(f"{name} must be a GPU tensor on cuda:{dev} (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    qs, ks = q.shape, k_cache.shape
+    if len(qs) != 3 or len(ks) != 4 or v_cache.shape != ks or ks[3] != qs[2]:
+        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
+    dt = q.dtype
+    if fp8:
+        if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype or dt not in _DTYPE_CODE:
+            raise ValueError("k_cache/v_cache must be float8_e4m3fn (or uint8 codes), q f16 or bf16")
+    elif k_cache.dtype != dt or v_cache.dtype != dt or dt not in _DTYPE_CODE:
+        raise ValueError("q, k_cache and v_cache must share one dtype, float16 or bfloat16")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    bts = block_table.shape
+    B = qs[0]
+    if len(bts) != 2 or bts[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
+    dims = (B, qs[1], ks[2], qs[2], bts[1], ks[1])
     if out is None:
-        return torch.empty_like(q)
-    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        if stream is None:
+            out = torch.empty_like(q)
+        else:
+            with torch.cuda.stream(_stream_object(stream)):
+                out = torch.empty_like(q)
+    elif out.get_device() != dev:
+        raise ValueError(f"out must be a GPU tensor on cuda:{dev} (got {out.device})")
+    elif out.shape != qs or out.dtype != dt or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
-    return out
+    if workspace is None:
+        need = _workspace_need(*dims, _DTYPE_CODE[dt], num_splits)
+        ws = _auto_workspace(q, need, dev, stream)
+        if ws[0] == 0:
+            return dims, dev, out, 0, 0, None
+        return dims, dev, out, ws[0], ws[1], ws[2]
+    if workspace.get_device() != dev:
+        raise ValueError(f"workspace must be a GPU tensor on cuda:{dev} (got {workspace.device})")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return (dims, dev, out, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            workspace)
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=None, *,
@@ -153,38 +296,20 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=N
 
     q [B,Hq,D], k_cache/v_cache [num_blocks,block_size,Hkv,D] (f16 or bf16,
     contiguous, on the GPU); block_table int32 [B,max_blocks_per_seq];
-    context_lens int32 [B]. ``out`` (same shape/dtype as q) and
-    ``workspace`` are allocated when not given. ``num_splits`` forces the
-    split count (``paged_decode_attention_splits``). Returns ``out``.
+    context_lens int32 [B]. ``out`` (same shape/dtype as q) is allocated when
+    not given. Without a ``workspace`` the binding supplies one: a zeroed
+    buffer kept per (GPU, stream) for calls on the current stream, or one of
+    the call's own, allocated on ``stream``, for calls given a stream or made
+    under graph capture. ``num_splits`` forces the split count
+    (``paged_decode_attention_splits``). Returns ``out``.
     """
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_table", block_table), ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
-    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_table and context_lens must be int32")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or q.dtype not in _DTYPE_CODE:
-        raise ValueError("q, k_cache and v_cache must share one dtype, float16 or bfloat16")
-    B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
-    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
-        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
-    _on_gpu(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-            context_lens=context_lens, out=out, workspace=workspace)
-    out = _checked_out(q, out)
+    (B, Hq, Hkv, D, MB, bs), dev, out, wp, wn, keep = _decode_prep(
+        q, k_cache, v_cache, block_table, context_lens, out, workspace, stream, num_splits, False)
     if scale is None:
         scale = D ** -0.5
-    if workspace is None:
-        workspace = alloc_workspace(q, k_cache, block_table, num_splits)
-    elif not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
-    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
-    args = [q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
             context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
-            _DTYPE_CODE[q.dtype], workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), handle]
+            _DTYPE_CODE[q.dtype], wp, wn, _stream_handle(stream, dev))
     if num_splits is None:
         rc = lib.paged_decode_attention(*args)
     else:
@@ -210,35 +335,14 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, o
     uint8 holding the codes), standing for code * k_scale and code * v_scale;
     q (and out) f16 or bf16 [B,Hq,D]. Otherwise as ``paged_decode_attention``.
     """
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_table", block_table), ("context_lens", context_lens)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
-    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_table and context_lens must be int32")
-    if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype or q.dtype not in _DTYPE_CODE:
-        raise ValueError("k_cache/v_cache must be float8_e4m3fn (or uint8 codes), q f16 or bf16")
-    B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
-    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
-        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
-    _on_gpu(q.device, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
-            context_lens=context_lens, out=out, workspace=workspace)
-    out = _checked_out(q, out)
+    (B, Hq, Hkv, D, MB, bs), dev, out, wp, wn, keep = _decode_prep(
+        q, k_cache, v_cache, block_table, context_lens, out, workspace, stream, num_splits, True)
     if scale is None:
         scale = D ** -0.5
-    if workspace is None:
-        workspace = alloc_workspace(q, k_cache, block_table, num_splits)
-    elif not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
-    handle = st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
     rc = lib.paged_decode_attention_fp8(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
         context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
-        _DTYPE_CODE[q.dtype], float(k_scale), float(v_scale), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), handle,
+        _DTYPE_CODE[q.dtype], float(k_scale), float(v_scale), wp, wn, _stream_handle(stream, dev),
         0 if num_splits is None else int(num_splits))
     if rc != PD_OK:
         raise PagedDecodeError(rc)
@@ -258,8 +362,9 @@ lib.rope_paged_kv_write_fp8.restype = _I
 
 
 def _handle(stream, device):
-    st = stream if stream is not None else torch.cuda.current_stream(device)
-    return st.cuda_stream if hasattr(st, "cuda_stream") else int(st)
+    """HIP stream handle for a call on `device` (a torch.device)."""
+    return _stream_handle(stream, device.index if device.index is not None
+                          else torch.cuda.current_device())
 
 
 def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=None, stream=None):
@@ -267,12 +372,12 @@ def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=Non
     embedding (``rope_cos_sin_table``), built on the GPU."""
     if out is None:
         out = torch.empty((max_position, rotary_dim), dtype=torch.float32, device=device)
-    _on_gpu(out.device)
+    dev = _gpu_index(out, "out")
     if out.dtype != torch.float32 or not out.is_contiguous() or \
             tuple(out.shape) != (max_position, rotary_dim):
         raise ValueError("out must be a contiguous float32 [max_position, rotary_dim] tensor")
     rc = lib.rope_cos_sin_table(out.data_ptr(), int(max_position), int(rotary_dim), float(base),
-                                _handle(stream, out.device))
+                                _stream_handle(stream, dev))
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return out
@@ -280,46 +385,58 @@ def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=Non
 
 def _rows(name, t, H, D):
     """Row stride (elements) of a [T, H, D] view whose heads are contiguous."""
-    if t.dim() != 3 or t.shape[1] != H or t.shape[2] != D:
+    sh = t.shape
+    if len(sh) != 3 or sh[1] != H or sh[2] != D:
         raise ValueError(f"{name} must be [T, {H}, {D}]")
-    if t.shape[0] > 0 and (t.stride(2) != 1 or t.stride(1) != D):
+    st = t.stride()
+    if sh[0] > 0 and (st[2] != 1 or st[1] != D):
         raise ValueError(f"{name}: heads of a token must be contiguous (strides [*, D, 1])")
-    return int(t.stride(0)) if t.shape[0] > 1 else H * D
+    return st[0] if sh[0] > 1 else H * D
 
 
-def _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out, fp8):
-    """Checked pointer and size arguments shared by the two RoPE writes."""
-    _on_gpu(q.device, k=k, v=v, positions=positions, slot_mapping=slot_mapping, cos_sin=cos_sin,
-            k_cache=k_cache, v_cache=v_cache, q_out=q_out)
-    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+def _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out, fp8, stream):
+    """Checked pointer and size arguments shared by the two RoPE writes, and
+    the stream handle (q_out, when not given, is allocated on that stream)."""
+    dev = _gpu_index(q, "q")
+    _same_gpu(dev, k=k, v=v, positions=positions, slot_mapping=slot_mapping, cos_sin=cos_sin,
+              k_cache=k_cache, v_cache=v_cache, q_out=q_out)
+    dt = q.dtype
+    if dt not in _DTYPE_CODE or k.dtype != dt or v.dtype != dt:
         raise ValueError("q, k and v must share one dtype, float16 or bfloat16")
     if fp8:
         if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype:
             raise ValueError("FP8 caches must be float8_e4m3fn (or uint8 codes), both alike")
-    elif k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+    elif k_cache.dtype != dt or v_cache.dtype != dt:
         raise ValueError("the caches must have q's dtype")
-    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or not k_cache.is_contiguous() or \
+    cs = k_cache.shape
+    if len(cs) != 4 or v_cache.shape != cs or not k_cache.is_contiguous() or \
             not v_cache.is_contiguous():
         raise ValueError("k_cache/v_cache must be contiguous [num_blocks,block_size,Hkv,D]")
-    NB, bs, Hkv, D = (int(x) for x in k_cache.shape)
-    T, Hq = int(q.shape[0]), int(q.shape[1])
+    NB, bs, Hkv, D = cs
+    qsh = q.shape
+    T, Hq = qsh[0], qsh[1]
     qs, ks, vs = _rows("q", q, Hq, D), _rows("k", k, Hkv, D), _rows("v", v, Hkv, D)
     if k.shape[0] != T or v.shape[0] != T:
         raise ValueError("q, k and v must have the same number of tokens")
     for name, t in (("positions", positions), ("slot_mapping", slot_mapping)):
         if t.dtype != torch.int32 or t.shape != (T,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 [T] tensor")
-    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != D or \
+    tsh = cos_sin.shape
+    if cos_sin.dtype != torch.float32 or len(tsh) != 2 or tsh[1] != D or \
             not cos_sin.is_contiguous():
         raise ValueError("cos_sin must be a contiguous float32 [max_position, D] tensor")
     if q_out is None:
-        q_out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
-    if tuple(q_out.shape) != (T, Hq, D) or q_out.dtype != q.dtype or not q_out.is_contiguous():
+        if stream is None:
+            q_out = torch.empty((T, Hq, D), dtype=dt, device=q.device)
+        else:
+            with torch.cuda.stream(_stream_object(stream)):
+                q_out = torch.empty((T, Hq, D), dtype=dt, device=q.device)
+    elif q_out.shape != (T, Hq, D) or q_out.dtype != dt or not q_out.is_contiguous():
         raise ValueError("q_out must be a contiguous [T, Hq, D] tensor of q's dtype")
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), qs, ks, vs, positions.data_ptr(),
-            slot_mapping.data_ptr(), cos_sin.data_ptr(), int(cos_sin.shape[0]), q_out.data_ptr(),
-            k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[q.dtype]]
-    return args, q_out
+            slot_mapping.data_ptr(), cos_sin.data_ptr(), tsh[0], q_out.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[dt]]
+    return args, q_out, _stream_handle(stream, dev)
 
 
 def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out=None,
@@ -333,9 +450,9 @@ def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_ca
     k_cache/v_cache [num_blocks,block_size,Hkv,D] (written in place). Returns
     q_out [T,Hq,D] (allocated when not given; may be q itself).
     """
-    args, q_out = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
-                             False)
-    rc = lib.rope_paged_kv_write(*args, _handle(stream, q.device))
+    args, q_out, h = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                                q_out, False, stream)
+    rc = lib.rope_paged_kv_write(*args, h)
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return q_out
@@ -348,10 +465,9 @@ def rope_paged_kv_write_fp8(q, k, v, positions, slot_mapping, cos_sin, k_cache, 
     [num_blocks,block_size,Hkv,D] receiving the E4M3FN codes of the rotated
     key times the float32 reciprocal of k_scale and of the value times that
     of v_scale. Returns q_out (16-bit)."""
-    args, q_out = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
-                             True)
-    rc = lib.rope_paged_kv_write_fp8(*args, float(k_scale), float(v_scale),
-                                     _handle(stream, q.device))
+    args, q_out, h = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                                q_out, True, stream)
+    rc = lib.rope_paged_kv_write_fp8(*args, float(k_scale), float(v_scale), h)
     if rc != PD_OK:
         raise PagedDecodeError(rc)
     return q_out
