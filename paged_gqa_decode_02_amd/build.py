@@ -26,7 +26,7 @@ LIB = os.path.join(LIB_DIR, "libpaged_decode.so")
 ARCH = "gfx950"
 
 SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_blocks.hip", "pd_api.cpp", "pd_kv_api.cpp", "pd_plan.cpp"]
-HEADERS = ["pd_internal.h"]
+HEADERS = ["pd_internal.h", "pd_fp8_code.h"]
 
 
 def hipcc() -> str:

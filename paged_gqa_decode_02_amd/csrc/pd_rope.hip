@@ -42,6 +42,11 @@
 #include "../../include/paged_decode.h"
 #include "pd_internal.h"
 
+// e4m3_code: float32 -> OCP E4M3FN code (nearest value, ties to even,
+// magnitudes from 464 up held at 448, NaN to 0x7F), built for the device
+#define PD_FP8_FN __device__ __forceinline__
+#include "pd_fp8_code.h"
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -98,26 +103,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// float32 -> OCP E4M3FN code (sign, 4 exponent bits with bias 7, 3 fraction
-// bits): nearest value, ties to even; magnitudes from 464 up (whose nearest
-// would be the NaN code) are held at 448 (0x7E); NaN gives 0x7F. Both ranges
-// are computed and one kept by selects, so no lane branches.
-__device__ __forceinline__ uint32_t e4m3_code(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  // below 2^-6: steps of 2^-9, codes 0 .. 8 (the input clamped so that the
-  // conversion stays in range where this result is not kept)
-  const uint32_t sub =
-      (uint32_t)__builtin_rintf(fminf(__builtin_bit_cast(float, a), 0.015625f) * 512.0f);
-  // from 2^-6: keep 3 of the 23 fraction bits (nearest-even), rebias 127 -> 7
-  const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  uint32_t c = a < 0x3c800000u ? sub : nrm;
-  c = a >= 0x43e80000u ? 0x7eu : c;
-  c = a > 0x7f800000u ? 0x7fu : c;
-  return sign | c;
-}
 
 // Rotation of the pairs (x[i], y[i]) in the order the FP8 write fixes.
 __device__ __forceinline__ void rotate_exact(const float (&x)[8], const float (&y)[8],

@@ -216,12 +216,15 @@ def test_graph_replay_reads_positions_at_replay():
 
 
 # ---------------------------------------------------------------------------
-# the write into an FP8 cache: codes bit for bit against the oracle's
+# the write into an FP8 cache: codes against the exact definition (nearest
+# code of the fp64 value, or its neighbour across a midpoint the float32
+# evaluation's error bound reaches), and bit for bit against a float32 model
 
 
-def run_write_fp8(case, kc8, vc8, k_scale, v_scale, *, packed=True):
+def run_write_fp8(case, kc8, vc8, k_scale, v_scale, *, packed=True, table=None):
     """Upload, call rope_paged_kv_write_fp8 over caches holding the codes
-    kc8/vc8, return (q_out bits, k codes, v codes)."""
+    kc8/vc8 (with the given float32 host table as the cos/sin input, else
+    the library's), return (q_out bits, k codes, v codes)."""
     qkv = to_dev(case.qkv, case.dtype)
     if packed:
         q, k, v = qkv[:, :case.Hq], qkv[:, case.Hq:case.Hq + case.Hkv], qkv[:, case.Hq + case.Hkv:]
@@ -231,7 +234,8 @@ def run_write_fp8(case, kc8, vc8, k_scale, v_scale, *, packed=True):
     vc = torch.from_numpy(np.ascontiguousarray(vc8)).cuda().view(torch.float8_e4m3fn)
     pos = torch.from_numpy(case.positions).cuda()
     slots = torch.from_numpy(case.slot_mapping).cuda()
-    tab = gpu_table(case.max_position, case.D, case.base)
+    tab = gpu_table(case.max_position, case.D, case.base) if table is None else \
+        torch.from_numpy(np.ascontiguousarray(table, np.float32)).cuda()
     qo = pd.rope_paged_kv_write_fp8(q, k, v, pos, slots, tab, kc, vc, k_scale=k_scale,
                                     v_scale=v_scale)
     torch.cuda.synchronize()
@@ -254,24 +258,70 @@ FP8_CASES = [
 ]
 
 
+def check_fp8_write(case, kc8, vc8, got_k, got_v, ks, vs, tab, what):
+    """The FP8 write against its plain definition (oracle/rope.py
+    rope_kv_write_fp8): at every written slot each code is the nearest
+    E4M3FN code of the exact (fp64) key or value over its scale, or its
+    neighbour across a midpoint within the float32 error bound of that exact
+    value; every other byte unchanged. Returns the count of neighbour codes."""
+    r = orope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions, case.slot_mapping, tab,
+                                kc8, vc8, dtype=case.dtype, k_scale=ks, v_scale=vs)
+    s = r["slots"]
+    H, D = case.Hkv, case.D
+    written = np.zeros(got_k.reshape(-1, H, D).shape[0], bool)
+    written[s] = True
+    gk, gv = got_k.reshape(-1, H, D), got_v.reshape(-1, H, D)
+    for name, g, c0 in (("K", gk, kc8), ("V", gv, vc8)):
+        assert np.array_equal(g[~written], c0.reshape(-1, H, D)[~written]), \
+            f"{what}: {name} bytes outside the written slots changed"
+    ok_k, n_k = orope.fp8_codes_within_rounding(gk[s], r["k_exact"], r["k_eps"])
+    ok_v, n_v = orope.fp8_codes_within_rounding(gv[s], r["v_exact"], r["v_eps"])
+    for name, ok, ex, g in (("K", ok_k, r["k_exact"], gk[s]), ("V", ok_v, r["v_exact"], gv[s])):
+        if not ok.all():
+            i = np.unravel_index(np.argmin(ok), ok.shape)
+            raise AssertionError(f"{what}: {name} code 0x{int(g[i]):02x} at {i} for exact "
+                                 f"value {ex[i]!r} (nearest 0x{int(orope.fp8_encode_exact(ex[i])):02x})")
+    print(f"{what}: {ok_k.size + ok_v.size} codes, {n_k} K and {n_v} V neighbour codes "
+          f"across a midpoint", flush=True)
+    return r, n_k + n_v
+
+
 @pytest.mark.parametrize("T,Hq,Hkv,D,dtype,bs,pad,ks,vs", FP8_CASES)
 @pytest.mark.parametrize("packed", [True, False])
-def test_fp8_write_codes_match_oracle_bit_for_bit(T, Hq, Hkv, D, dtype, bs, pad, ks, vs, packed):
+def test_fp8_write_codes_against_the_exact_definition(T, Hq, Hkv, D, dtype, bs, pad, ks, vs,
+                                                      packed):
     case = wrope.scatter(T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, block_size=bs, pad_every=pad,
                          max_position=32768, seed=T + D + 1)
     print(case.describe(), f"fp8 ks={ks} vs={vs}", "packed" if packed else "separate", flush=True)
     kc8 = random_codes(case.k_cache.shape, T)
     vc8 = random_codes(case.v_cache.shape, T + 1)
-    qo, kc, vc = run_write_fp8(case, kc8, vc8, ks, vs, packed=packed)
     tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
-    q_rot, kc_ref, vc_ref = orope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
-                                                    case.slot_mapping, tab, kc8, vc8,
-                                                    dtype=dtype, k_scale=ks, v_scale=vs)
-    compare(qo, q_rot, dtype, what=f"{case.name} q_out")
+    qo, kc, vc = run_write_fp8(case, kc8, vc8, ks, vs, packed=packed, table=tab)
+    r, _ = check_fp8_write(case, kc8, vc8, kc, vc, ks, vs, tab, case.name)
+    compare(qo, r["q_rot"], dtype, what=f"{case.name} q_out")
+    if ks == 0.002:  # the case meant to hit the saturation
+        assert np.count_nonzero((kc & 0x7F) == 0x7E) > 0
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,dtype,bs,pad,ks,vs", FP8_CASES)
+def test_fp8_write_codes_match_the_float32_model_bit_for_bit(T, Hq, Hkv, D, dtype, bs, pad, ks,
+                                                             vs):
+    """Regression check: the kernel's codes equal, bit for bit, those of a
+    float32 model of its evaluation order (oracle/rope.py
+    rope_kv_write_fp8_f32_model), which the exact-definition test above
+    bounds; a change in the kernel's arithmetic shows here first."""
+    case = wrope.scatter(T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, block_size=bs, pad_every=pad,
+                         max_position=32768, seed=T + D + 1)
+    print(case.describe(), f"fp8 ks={ks} vs={vs} float32 model", flush=True)
+    kc8 = random_codes(case.k_cache.shape, T)
+    vc8 = random_codes(case.v_cache.shape, T + 1)
+    tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    _, kc, vc = run_write_fp8(case, kc8, vc8, ks, vs, table=tab)
+    _, kc_ref, vc_ref = orope.rope_kv_write_fp8_f32_model(
+        case.q, case.k, case.v, case.positions, case.slot_mapping, tab, kc8, vc8, dtype=dtype,
+        k_scale=ks, v_scale=vs)
     assert np.array_equal(kc, kc_ref), f"{case.name}: K codes differ at {np.argwhere(kc != kc_ref)[:4]}"
     assert np.array_equal(vc, vc_ref), f"{case.name}: V codes differ"
-    if ks == 0.002:  # the case meant to hit the saturation
-        assert np.count_nonzero((kc_ref & 0x7F) == 0x7E) > 0
 
 
 @pytest.mark.parametrize("bs", [16, 32])
@@ -283,14 +333,12 @@ def test_fp8_write_then_fp8_decode(bs):
                               block_size=bs, seed=9, kv_dtype="fp8")
     case = wrope.decode_step(dec, seed=10)
     print(case.describe(), "fp8", flush=True)
-    qo, kc, vc = run_write_fp8(case, dec.k_cache, dec.v_cache, dec.k_scale, dec.v_scale)
     tab = orope.cos_sin_table_f32(case.max_position, case.D, case.base)
-    q_rot, kc_ref, vc_ref = orope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
-                                                    case.slot_mapping, tab, dec.k_cache,
-                                                    dec.v_cache, dtype="bf16",
-                                                    k_scale=dec.k_scale, v_scale=dec.v_scale)
-    compare(qo, q_rot, "bf16", what="feed8 q_out")
-    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    qo, kc, vc = run_write_fp8(case, dec.k_cache, dec.v_cache, dec.k_scale, dec.v_scale,
+                               table=tab)
+    r, _ = check_fp8_write(case, dec.k_cache, dec.v_cache, kc, vc, dec.k_scale, dec.v_scale, tab,
+                           "feed8")
+    compare(qo, r["q_rot"], "bf16", what="feed8 q_out")
     # decode over the GPU-written codes with the GPU-rotated q, against the
     # oracle over the same bytes
     import dataclasses

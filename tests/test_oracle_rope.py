@@ -275,26 +275,148 @@ def test_fp8_write_codes_stand_for_the_scaled_16bit_write(dtype):
     ks, vs = 0.0125, 0.0078125
     kc0 = np.full(case.k_cache.shape, 0x11, np.uint8)
     vc0 = np.full(case.v_cache.shape, 0x22, np.uint8)
-    q_rot8, kc, vc = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions,
-                                            case.slot_mapping, tab, kc0, vc0, dtype=dtype,
-                                            k_scale=ks, v_scale=vs)
+    r = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions, case.slot_mapping, tab,
+                               kc0, vc0, dtype=dtype, k_scale=ks, v_scale=vs)
+    kc, vc = r["k_cache"], r["v_cache"]
     q_rot, k_rot, _, _ = rope.rope_kv_write(case.q, case.k, case.v, case.positions,
                                             case.slot_mapping, tab, case.k_cache,
                                             case.v_cache, dtype=dtype)
-    assert np.array_equal(q_rot8, q_rot)
+    assert np.array_equal(r["q_rot"], q_rot)
     live = case.slot_mapping >= 0
     s = case.slot_mapping[live].astype(np.int64)
+    assert np.array_equal(r["slots"], s)
     kf = kc.reshape(-1, case.Hkv, case.D)
     vf = vc.reshape(-1, case.Hkv, case.D)
-    # each code is the nearest E4M3FN value to the scaled exact key/value:
-    # within half a code step (2^-4 relative, or 2^-10 absolute below 2^-6)
+    # each code is the nearest E4M3FN value to the exact key/value over the
+    # scale: within half a code step (2^-4 relative, or 2^-10 absolute below
+    # 2^-6; exact division and exact rotation, so no slack)
     kd = oracle.widen_fp8(kf[s]) * ks
     vd = oracle.widen_fp8(vf[s]) * vs
     kr, vr = k_rot[live], oracle.widen(case.v, dtype)[live]
-    # (the factor 1.0001 covers the float32 rotation and division)
-    assert np.all(np.abs(kd - kr) <= 2.0 ** -4 * np.abs(kr) * 1.0001 + 2.0 ** -10 * ks)
-    assert np.all(np.abs(vd - vr) <= 2.0 ** -4 * np.abs(vr) * 1.0001 + 2.0 ** -10 * vs)
+    assert np.all(np.abs(kd - kr) <= 2.0 ** -4 * np.abs(kr) + 2.0 ** -10 * ks)
+    assert np.all(np.abs(vd - vr) <= 2.0 ** -4 * np.abs(vr) + 2.0 ** -10 * vs)
     # nothing else was touched
     untouched = np.ones(kf.shape[0], bool)
     untouched[s] = False
     assert np.all(kf[untouched] == 0x11) and np.all(vf[untouched] == 0x22)
+
+
+# ---------------------------------------------------------------------------
+# the FP8 write's error bound and acceptance rule (oracle/rope.py): a float32
+# evaluation of x c - y s (or a value) times the float32 reciprocal of the
+# scale stays within fp8_write_error_bounds of the exact quotient, and a
+# code the rule accepts is the nearest one or its neighbour across a
+# midpoint that the bound reaches
+
+def f32_keys(x, y, c, sn, ks):
+    """A float32 evaluation in another legitimate order than the model's:
+    fused products (x*c exact in fp64, rounded once with y*s) then the
+    reciprocal product."""
+    X, Y, C, S = (np.asarray(t, np.float64) for t in (x, y, c, sn))
+    d = (X * C - Y * S).astype(np.float32)
+    return (d * (np.float32(1) / np.float32(ks))).astype(np.float32)
+
+
+def keys_on_midpoints(rng, n, ks):
+    """Key pairs (x, y) and angles whose exact rotated value over ks lands
+    within a few float32 roundings of a midpoint between two E4M3FN codes."""
+    vals = rope.fp8_value(np.arange(0x7E, dtype=np.uint8))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    m = rng.choice(mids, size=n) * rng.choice([-1.0, 1.0], size=n)
+    a = rng.uniform(0, 2 * np.pi, n)
+    c, sn = np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
+    # x c - y s = m ks with y drawn, x solved and rounded to bf16
+    y = (rng.standard_normal(n) * 0.5).astype(np.float32)
+    x = ((m * ks + y.astype(np.float64) * sn) / np.where(np.abs(c) < 1e-3, 1e-3, c))
+    xb = oracle.widen(oracle.round_to_dtype(x, "bf16"), "bf16")
+    yb = oracle.widen(oracle.round_to_dtype(y, "bf16"), "bf16")
+    return xb, yb, c, sn
+
+
+@pytest.mark.parametrize("ks", [0.01, 0.0125, 0.003, 1.0 / 3.0, 7.5e-4])
+def test_fp8_key_error_bound_covers_float32_evaluations(ks):
+    rng = np.random.default_rng(int(ks * 1e6))
+    x, y, c, sn = keys_on_midpoints(rng, 200000, ks)
+    X, Y, C, S = (np.asarray(t, np.float64) for t in (x, y, c, sn))
+    exact = (X * C - Y * S) / np.float64(np.float32(ks))
+    A = np.abs(X * C) + np.abs(Y * S)
+    eps, _ = rope.fp8_write_error_bounds(A, np.zeros(1), np.float32(ks), np.float32(1))
+    x1, _ = rope.rotate_f32(x.astype(np.float32), y.astype(np.float32), c, sn)
+    model = (x1 * (np.float32(1) / np.float32(ks))).astype(np.float32).astype(np.float64)
+    other = f32_keys(x, y, c, sn, ks).astype(np.float64)
+    for v in (model, other):
+        err = np.abs(v - exact)
+        assert np.all(err <= eps)
+        # and the bound is not vacuous: some evaluation comes within 10x of it
+        assert (err / eps).max() > 0.1
+
+
+@pytest.mark.parametrize("vs", [0.01, 0.02, 0.003, 1.0 / 3.0])
+def test_fp8_value_error_bound_covers_float32_evaluations(vs):
+    rng = np.random.default_rng(int(vs * 1e6) + 1)
+    v = oracle.widen(oracle.round_to_dtype(rng.standard_normal(500000), "bf16"), "bf16")
+    exact = v / np.float64(np.float32(vs))
+    _, eps = rope.fp8_write_error_bounds(np.zeros(1), np.abs(v), np.float32(1), np.float32(vs))
+    model = (v.astype(np.float32) * (np.float32(1) / np.float32(vs))).astype(np.float32)
+    err = np.abs(model.astype(np.float64) - exact)
+    assert np.all(err <= eps) and (err / eps).max() > 0.1
+
+
+def test_fp8_acceptance_rule_takes_the_float32_model_and_counts_midpoint_cases():
+    case = wrope.scatter(64, Hq=32, Hkv=8, D=128, dtype="bf16", block_size=16, seed=3,
+                         pad_every=0, max_position=32768)
+    tab = rope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    zeros = np.zeros(case.k_cache.shape, np.uint8)
+    r = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions, case.slot_mapping, tab,
+                               zeros, zeros, dtype="bf16", k_scale=0.01, v_scale=0.01)
+    _, km, vm = rope.rope_kv_write_fp8_f32_model(case.q, case.k, case.v, case.positions,
+                                                 case.slot_mapping, tab, zeros, zeros,
+                                                 dtype="bf16", k_scale=0.01, v_scale=0.01)
+    s = r["slots"]
+    ok_k, n_k = rope.fp8_codes_within_rounding(km.reshape(-1, 8, 128)[s], r["k_exact"],
+                                               r["k_eps"])
+    ok_v, n_v = rope.fp8_codes_within_rounding(vm.reshape(-1, 8, 128)[s], r["v_exact"],
+                                               r["v_eps"])
+    assert ok_k.all() and ok_v.all()
+    # 1/0.01 is not a float32: bf16 values times fl(1/0.01) sit on either
+    # side of the codes' midpoints where the exact quotient does not
+    assert n_v > 0
+    assert n_k + n_v < 0.02 * (ok_k.size + ok_v.size)
+
+
+def test_fp8_acceptance_rule_rejects_planted_mistakes():
+    vals = rope.fp8_value(np.arange(0x7F, dtype=np.uint8))
+    exact = np.array([1.0, 1.0, 0.3, 101.0, -2.0, 448.0, 0.0])
+    eps = np.full(exact.shape, 1e-6)
+    ref = rope.fp8_encode_exact(exact)
+    assert rope.fp8_codes_within_rounding(ref, exact, eps)[0].all()
+    # one code too high, away from any midpoint
+    ok, _ = rope.fp8_codes_within_rounding(ref + 1, exact[:5].tolist() + [440.0, 0.01], eps)
+    assert not ok[:5].any()
+    # two codes off, the sign flipped, a NaN code
+    assert not rope.fp8_codes_within_rounding(ref[:1] + 2, exact[:1], eps[:1])[0].any()
+    assert not rope.fp8_codes_within_rounding(ref[4:5] ^ 0x80, exact[4:5], eps[4:5])[0].any()
+    assert not rope.fp8_codes_within_rounding(np.array([0x7F], np.uint8), exact[:1],
+                                              eps[:1])[0].any()
+    # a neighbour is taken only within eps of the midpoint between the two
+    mid = 0.5 * (vals[40] + vals[41])
+    for delta, want in ((0.5e-6, True), (2e-6, False)):
+        x = np.array([mid - delta])  # exact just below the midpoint: nearest is code 40
+        assert rope.fp8_encode_exact(x)[0] == 40
+        ok, n = rope.fp8_codes_within_rounding(np.array([41], np.uint8), x, np.array([1e-6]))
+        assert bool(ok[0]) == want and n == int(want)
+    # a rotation with the sign of the sine flipped fails the rule
+    case = wrope.scatter(8, Hq=4, Hkv=2, D=64, dtype="bf16", block_size=16, seed=4,
+                         pad_every=0, max_position=4096)
+    tab = rope.cos_sin_table_f32(case.max_position, case.D, case.base)
+    zeros = np.zeros(case.k_cache.shape, np.uint8)
+    r = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions, case.slot_mapping, tab,
+                               zeros, zeros, dtype="bf16", k_scale=0.01, v_scale=0.01)
+    bad = tab.copy()
+    bad[:, 32:] *= -1
+    rb = rope.rope_kv_write_fp8(case.q, case.k, case.v, case.positions, case.slot_mapping, bad,
+                                zeros, zeros, dtype="bf16", k_scale=0.01, v_scale=0.01)
+    s = r["slots"]
+    ok, _ = rope.fp8_codes_within_rounding(rb["k_cache"].reshape(-1, 2, 64)[s], r["k_exact"],
+                                           r["k_eps"])
+    assert ok.mean() < 0.5
