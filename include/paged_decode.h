@@ -87,6 +87,7 @@ extern "C" {
 #define PD_ERR_HIP 8           /* the HIP runtime rejected a launch */
 #define PD_ERR_INTERNAL 9      /* unexpected internal failure */
 #define PD_ERR_VALUE 10        /* scale is not a finite positive number */
+#define PD_ERR_SCRATCH 11      /* the split plan needs more than the no-allocation scratch */
 
 /* Version of this ABI (PAGED_DECODE_ABI_VERSION of the built library). */
 int32_t paged_decode_abi_version(void);
@@ -198,6 +199,34 @@ int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const voi
                                    float k_scale, float v_scale,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    int32_t num_splits);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * paged_decode_attention without a workspace argument. The split-K scratch
+ * is one static device array per GPU of PAGED_DECODE_NOALLOC_SCRATCH_BYTES
+ * (32 MiB: 256 KiB of arrival counters, then the fp32 partials), held from
+ * the library's first call on that GPU until the process ends; nothing is
+ * allocated or freed per call. Same arguments (minus the workspace), plan,
+ * kernels and result as paged_decode_attention, bit for bit.
+ *
+ * The first call on a GPU looks up that GPU's copy of the array and queues
+ * a fill kernel on `stream` that clears its counters; every call leaves
+ * them zero. All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (on different streams without ordering) race and give
+ * wrong results, so order them (one stream, or events).
+ *
+ * Errors as paged_decode_attention, plus PD_ERR_SCRATCH (nothing queued)
+ * when the shape's split plan needs more than the array holds, i.e. when
+ * paged_decode_workspace_bytes(...) > PAGED_DECODE_NOALLOC_SCRATCH_BYTES.
+ */
+#define PAGED_DECODE_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int32_t paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       int32_t max_blocks_per_seq, void* out,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t block_size, float scale, int32_t dtype,
+                                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ PD_OK = 0
 STATUS_NAMES = {
     0: "PD_OK", 1: "PD_ERR_NULL", 2: "PD_ERR_SHAPE", 3: "PD_ERR_DTYPE", 4: "PD_ERR_ALIGN",
     5: "PD_ERR_ALIAS", 6: "PD_ERR_WORKSPACE", 7: "PD_ERR_UNSUPPORTED", 8: "PD_ERR_HIP",
-    9: "PD_ERR_INTERNAL", 10: "PD_ERR_VALUE",
+    9: "PD_ERR_INTERNAL", 10: "PD_ERR_VALUE", 11: "PD_ERR_SCRATCH",
 }
 
 if not os.path.exists(LIB_PATH):
@@ -58,6 +58,9 @@ lib.paged_decode_attention_splits.argtypes = _ATTN + [_I]
 lib.paged_decode_attention_splits.restype = _I
 lib.paged_decode_attention_fp8.argtypes = _ATTN[:14] + [_F, _F] + _ATTN[14:] + [_I]
 lib.paged_decode_attention_fp8.restype = _I
+lib.paged_decode_attention_noalloc.argtypes = _ATTN[:14] + [_P]
+lib.paged_decode_attention_noalloc.restype = _I
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # PAGED_DECODE_NOALLOC_SCRATCH_BYTES
 _FP8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
@@ -239,7 +242,7 @@ _DECODE_NAMES = ("q", "k_cache", "v_cache", "block_table", "context_lens")
 
 
 def _decode_prep(q, k_cache, v_cache, block_table, context_lens, out, workspace, stream,
-                 num_splits, fp8):
+                 num_splits, fp8, noalloc=False):
     """Checks that keep a bad argument from reaching a kernel (host or other-GPU
     tensors, layouts the library cannot see), then `out` and the workspace.
     Shape rules the C ABI itself checks are left to it. Returns (dims, dev,
@@ -276,6 +279,8 @@ def _decode_prep(q, k_cache, v_cache, block_table, context_lens, out, workspace,
         raise ValueError(f"out must be a GPU tensor on cuda:{dev} (got {out.device})")
     elif out.shape != qs or out.dtype != dt or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    if noalloc:
+        return dims, dev, out, 0, 0, None
     if workspace is None:
         need = _workspace_need(*dims, _DTYPE_CODE[dt], num_splits)
         ws = _auto_workspace(q, need, dev, stream)
@@ -324,6 +329,29 @@ def paged_decode_attention_splits(q, k_cache, v_cache, block_table, context_lens
     """``paged_decode_attention`` with the split count forced to ``num_splits``."""
     return paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out,
                                   num_splits=num_splits, **kw)
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, context_lens, out, *,
+                                   scale=None, stream=None):
+    """``paged_decode_attention`` for callers that cannot allocate: the
+    library's static per-GPU scratch takes the workspace's place, and this
+    binding allocates nothing either, so ``out`` is required. Calls that
+    overlap in time on one GPU share that scratch and race. Returns ``out``.
+    """
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    (B, Hq, Hkv, D, MB, bs), dev, out, _, _, _ = _decode_prep(
+        q, k_cache, v_cache, block_table, context_lens, out, None, stream, None, False,
+        noalloc=True)
+    if scale is None:
+        scale = D ** -0.5
+    rc = lib.paged_decode_attention_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
+        _DTYPE_CODE[q.dtype], _stream_handle(stream, dev))
+    if rc != PD_OK:
+        raise PagedDecodeError(rc)
+    return out
 
 
 def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, out=None, *,

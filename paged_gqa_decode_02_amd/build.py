@@ -25,7 +25,8 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libpaged_decode.so")
 ARCH = "gfx950"
 
-SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_blocks.hip", "pd_api.cpp", "pd_kv_api.cpp", "pd_plan.cpp"]
+SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_blocks.hip", "pd_scratch.hip", "pd_api.cpp",
+           "pd_kv_api.cpp", "pd_plan.cpp"]
 HEADERS = ["pd_internal.h", "pd_fp8_code.h"]
 
 

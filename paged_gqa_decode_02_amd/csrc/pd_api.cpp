@@ -24,26 +24,31 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool positive_finite(float x) { return x > 0.0f && isfinite(x); }
 
-int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* context_lens,
-                       int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
-                       int32_t Hkv, int32_t D, int32_t block_size, float scale, int32_t dtype,
-                       void* workspace, size_t workspace_bytes, void* stream,
-                       int32_t requested_splits, bool kv_fp8 = false, float k_scale = 1.0f,
-                       float v_scale = 1.0f) {
+// Every host-side check of an attention call, then its plan, filled into
+// *l ready to launch. With `own_workspace` the workspace arguments are not
+// checked (the caller supplies scratch of its own afterwards) and
+// *workspace_need tells how much the plan needs.
+int32_t prepare(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, const int32_t* context_lens,
+                int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                int32_t D, int32_t block_size, float scale, int32_t dtype, void* workspace,
+                size_t workspace_bytes, void* stream, int32_t requested_splits, bool kv_fp8,
+                float k_scale, float v_scale, bool own_workspace, pd::Launch* l,
+                size_t* workspace_need) {
   pd::Shape s{B, Hq, Hkv, D, max_blocks_per_seq, block_size, dtype};
   pd::Plan plan;
   int32_t st = pd::make_plan(s, requested_splits, &plan, kv_fp8);
   if (st != PD_OK) return st;
   if (!positive_finite(scale)) return PD_ERR_VALUE;
   if (kv_fp8 && (!positive_finite(k_scale) || !positive_finite(v_scale))) return PD_ERR_VALUE;
+  const size_t need = pd::workspace_bytes(s, plan);
+  *workspace_need = need;
   if (B == 0) return PD_OK;  // empty batch: nothing to compute
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PD_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
     return PD_ERR_ALIGN;
-  const size_t need = pd::workspace_bytes(s, plan);
-  if (need > 0) {
+  if (need > 0 && !own_workspace) {
     if (!workspace || workspace_bytes < need) return PD_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return PD_ERR_ALIGN;
   }
@@ -51,10 +56,27 @@ int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
   if (overlap(out, qo_bytes, q, qo_bytes) ||
       overlap(out, qo_bytes, block_table, (size_t)B * max_blocks_per_seq * 4) ||
       overlap(out, qo_bytes, context_lens, (size_t)B * 4) ||
-      (need > 0 && overlap(out, qo_bytes, workspace, need)))
+      (need > 0 && !own_workspace && overlap(out, qo_bytes, workspace, need)))
     return PD_ERR_ALIAS;
-  pd::Launch l{q,     k_cache, v_cache, block_table, context_lens, out,     workspace,
-               s,     plan,    scale,   stream,      kv_fp8,       k_scale, v_scale};
+  *l = pd::Launch{q,     k_cache, v_cache, block_table, context_lens, out,     workspace,
+                  s,     plan,    scale,   stream,      kv_fp8,       k_scale, v_scale};
+  return PD_OK;
+}
+
+int32_t attention_impl(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* context_lens,
+                       int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t D, int32_t block_size, float scale, int32_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       int32_t requested_splits, bool kv_fp8 = false, float k_scale = 1.0f,
+                       float v_scale = 1.0f) {
+  pd::Launch l;
+  size_t need = 0;
+  const int32_t st = prepare(q, k_cache, v_cache, block_table, context_lens, max_blocks_per_seq,
+                             out, B, Hq, Hkv, D, block_size, scale, dtype, workspace,
+                             workspace_bytes, stream, requested_splits, kv_fp8, k_scale,
+                             v_scale, false, &l, &need);
+  if (st != PD_OK || B == 0) return st;
   return pd::launch(l);
 }
 
@@ -82,6 +104,30 @@ size_t workspace_impl(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
 
 }  // namespace
 
+namespace pd {
+
+int32_t attention_with_scratch(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
+                               int32_t Hkv, int32_t D, int32_t block_size, float scale,
+                               int32_t dtype, void* stream, size_t scratch_bytes,
+                               int32_t (*get_scratch)(void* stream, void** ptr)) {
+  Launch l;
+  size_t need = 0;
+  int32_t st = prepare(q, k_cache, v_cache, block_table, context_lens, max_blocks_per_seq, out,
+                       B, Hq, Hkv, D, block_size, scale, dtype, nullptr, 0, stream, 0, false,
+                       1.0f, 1.0f, true, &l, &need);
+  if (st != PD_OK || B == 0) return st;
+  if (need > scratch_bytes) return PD_ERR_SCRATCH;
+  if (need > 0) {
+    st = get_scratch(stream, &l.workspace);
+    if (st != PD_OK) return st;
+  }
+  return launch(l);
+}
+
+}  // namespace pd
+
 extern "C" {
 
 int32_t paged_decode_abi_version(void) { return PAGED_DECODE_ABI_VERSION; }
@@ -100,6 +146,9 @@ const char* paged_decode_strerror(int32_t code) {
     case PD_ERR_HIP: return "HIP runtime rejected the launch";
     case PD_ERR_INTERNAL: return "internal error";
     case PD_ERR_VALUE: return "scale (and k_scale, v_scale) must be finite and positive";
+    case PD_ERR_SCRATCH:
+      return "the split plan needs more scratch than the no-allocation entry point holds "
+             "(PAGED_DECODE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status code";
   }
 }

@@ -77,6 +77,17 @@ struct Launch {
 // Queues the decode kernel; PD_* status code.
 int32_t launch(const Launch& l);
 
+// paged_decode_attention with scratch the library owns (pd_api.cpp): every
+// host check first, then PD_ERR_SCRATCH if the plan needs more than
+// scratch_bytes, else get_scratch(stream, &ptr) supplies the scratch (only
+// when the plan needs any) and the kernel is queued.
+int32_t attention_with_scratch(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int32_t max_blocks_per_seq, void* out, int32_t B, int32_t Hq,
+                               int32_t Hkv, int32_t D, int32_t block_size, float scale,
+                               int32_t dtype, void* stream, size_t scratch_bytes,
+                               int32_t (*get_scratch)(void* stream, void** ptr));
+
 // Queues a kernel that zeroes `bytes` (a multiple of 4) at `ws`.
 int32_t zero_workspace(void* ws, size_t bytes, void* stream);
 

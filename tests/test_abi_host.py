@@ -246,3 +246,47 @@ def test_plan_at_other_geometries(Hq, Hkv, D, B, L):
     ws = pd.paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, 16, BF16)
     if S > 1:
         assert ws >= 256 * 1024 + B * Hq * S * D * 4 + B * Hq * S * 4
+
+
+# ---------------------------------------------------------------------------
+# the entry point that allocates nothing: every host check runs before the
+# library looks up its static scratch (no HIP call is made here)
+
+def call_noalloc(**over):
+    B, Hq, Hkv, D, MB, bs = 2, 32, 8, 128, 64, 16
+    a = dict(q=BASE, k=BASE + (1 << 24), v=BASE + (2 << 24), bt=BASE + (3 << 24),
+             cl=BASE + (3 << 24) + 4096, MB=MB, out=BASE + (4 << 24), B=B, Hq=Hq, Hkv=Hkv,
+             D=D, bs=bs, scale=0.0883883, dtype=BF16, stream=0)
+    a.update(over)
+    return pd.lib.paged_decode_attention_noalloc(
+        a["q"], a["k"], a["v"], a["bt"], a["cl"], a["MB"], a["out"], a["B"], a["Hq"], a["Hkv"],
+        a["D"], a["bs"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), "PD_ERR_DTYPE"),
+    (dict(D=96), "PD_ERR_UNSUPPORTED"),
+    (dict(scale=float("nan")), "PD_ERR_VALUE"),
+    (dict(q=0), "PD_ERR_NULL"),
+    (dict(q=BASE + 8), "PD_ERR_ALIGN"),
+    (dict(out=BASE + 4096), "PD_ERR_ALIAS"),
+    (dict(B=0, q=0, k=0, v=0, bt=0, cl=0, out=0), "PD_OK"),
+    # 64 sequences of up to 262,144 tokens: the split plan needs more than
+    # the 32 MiB scratch
+    (dict(B=64, MB=16384, out=BASE + (40 << 24)), "PD_ERR_SCRATCH"),
+])
+def test_noalloc_entry_point_checks_before_touching_the_device(over, code):
+    assert call_noalloc(**over) == CODES[code]
+
+
+def test_noalloc_scratch_limit_is_the_headers():
+    src = open(HEADER).read()
+    m = re.search(r"#define PAGED_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
+    assert m and int(m.group(1)) * (1 << 20) == pd.NOALLOC_SCRATCH_BYTES
+    need = pd.paged_decode_workspace_bytes(64, 32, 8, 128, 16384, 16, BF16)
+    assert need > pd.NOALLOC_SCRATCH_BYTES
+    # the split-K shapes of the workloads fit
+    for B in (1, 2, 4, 8):
+        for L in (128, 256, 512, 1024, 4096):
+            assert pd.paged_decode_workspace_bytes(B, 32, 8, 128, L // 16, 16, BF16) <= \
+                pd.NOALLOC_SCRATCH_BYTES

@@ -1,0 +1,80 @@
+"""The entry point that allocates nothing (paged_decode_attention_noalloc,
+for callers that cannot allocate) against paged_decode_attention: same plan
+and kernels, so the outputs agree bit for bit. Two calls in a row share the
+library's static scratch, the second on a smaller input; the split plan is
+in use for both, so the scratch's counters and partials carry over from one
+call to the next."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_decode_02_amd as pd
+import workloads
+from helpers import compare, device_case, out_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def planned_splits(case):
+    s, _ = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
+                                case.block_size, workloads.DTYPES[case.dtype])
+    return s
+
+
+def run_both(case, stream=None):
+    q, k, v, bt, cl = device_case(case)
+    ref = pd.paged_decode_attention(q, k, v, bt, cl, scale=case.scale)
+    out = torch.full_like(q, float("nan"))
+    pd.paged_decode_attention_noalloc(q, k, v, bt, cl, out, scale=case.scale, stream=stream)
+    torch.cuda.synchronize()
+    return out_bits(ref), out_bits(out)
+
+
+def test_noalloc_matches_the_workspace_entry_point_twice_bigger_then_smaller():
+    big = workloads.splitk(8, 1024, seed=31)
+    small = workloads.make_case("noalloc_small", 3, [300, 7, 129], dtype="f16", block_size=32,
+                                seed=32)
+    for case in (big, small, big):
+        print(case.describe(), "splits", planned_splits(case), flush=True)
+        assert planned_splits(case) > 1
+        ref, got = run_both(case)
+        assert np.array_equal(ref, got), case.name
+    # and the last one against the oracle, to the parity gates
+    oref, _ = oracle.attention_case(big)
+    compare(got, oref, big.dtype, what="noalloc " + big.name)
+
+
+def test_noalloc_single_pass_and_fp16_geometry():
+    case = workloads.geometry(14, 2, 64, 5, 300, seed=33)
+    print(case.describe(), "splits", planned_splits(case), flush=True)
+    ref, got = run_both(case)
+    assert np.array_equal(ref, got)
+    tiny = workloads.tiny(0)
+    ref, got = run_both(tiny)
+    assert np.array_equal(ref, got)
+
+
+def test_noalloc_on_a_side_stream():
+    case = workloads.splitk(4, 512, seed=34)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ref, got = run_both(case, stream=s)
+    assert np.array_equal(ref, got)
+
+
+def test_noalloc_refuses_a_plan_beyond_its_scratch():
+    # 64 sequences of up to 262,144 tokens: the planned split needs more
+    # than 32 MiB of partials; refused before anything is queued
+    B, MB = 64, 16384
+    need = pd.paged_decode_workspace_bytes(B, 32, 8, 128, MB, 16, torch.bfloat16)
+    assert need > pd.NOALLOC_SCRATCH_BYTES
+    q = torch.zeros(B, 32, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 16, 8, 128, dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros(B, MB, dtype=torch.int32, device="cuda")
+    cl = torch.ones(B, dtype=torch.int32, device="cuda")
+    out = torch.zeros_like(q)
+    with pytest.raises(pd.PagedDecodeError, match="SCRATCH"):
+        pd.paged_decode_attention_noalloc(q, k, k, bt, cl, out)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all())
