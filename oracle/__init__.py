@@ -54,9 +54,14 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        # PD_ORACLE_LIB: another build of the same source (the sanitizer
+        # tests load an instrumented one)
+        path = os.environ.get("PD_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_LIB):
+                build()
+            path = _LIB
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.pdo_attention.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64,
