@@ -551,7 +551,7 @@ def cpu_baseline(case, timing, min_seconds: float = 10.0, max_calls: int = 25):
             "seconds_min": round(times[0], 3), "seconds_max": round(times[-1], 3),
             "sample": f"{nseq} of {case.B} sequences of the same workload (full contexts), "
                       f"median of {calls} oracle calls, fp64, {used} threads",
-            "cpu_model": cpu_model()}
+            "threads_used": int(used), **host_cpu()}
     # one single-thread call on a smaller sample of the same sequences
     n1 = max(1, min(nseq, 4))
     t1 = time.perf_counter()
@@ -563,17 +563,47 @@ def cpu_baseline(case, timing, min_seconds: float = 10.0, max_calls: int = 25):
     return base
 
 
-def cpu_model() -> str:
-    """The host CPU's model name (/proc/cpuinfo), or the platform's."""
+def host_cpu() -> dict:
+    """The host's CPU: model name, vendor, family/model/stepping (from
+    /proc/cpuinfo), logical CPUs and physical cores in the machine, and the
+    CPUs this process may run on."""
+    info = {}
+    phys = set()
     try:
         with open("/proc/cpuinfo") as f:
+            cur = {}
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if cur:
+                        phys.add((cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                cur[k] = v
+                if k in ("model name", "vendor_id", "cpu family", "model", "stepping") and \
+                        k not in info:
+                    info[k] = v
+            if cur:
+                phys.add((cur.get("physical id"), cur.get("core id")))
     except OSError:
         pass
     import platform
-    return platform.processor() or platform.machine()
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_model": info.get("model name") or platform.processor() or platform.machine(),
+            "cpu_vendor": info.get("vendor_id"),
+            "cpu_family_model_stepping": [info.get("cpu family"), info.get("model"),
+                                          info.get("stepping")],
+            "host_logical_cpus": os.cpu_count(),
+            "host_physical_cores": len(phys) if phys and None not in next(iter(phys)) else None,
+            "cpus_available_to_process": avail}
+
+
+def device_info(torch) -> dict:
+    """The GPU the bench ran on and the software stack."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count,
+            "memory_bytes": pr.total_memory, "hip": torch.version.hip, "torch": torch.__version__}
 
 
 def launch_floor(torch, pd, iters=200):
@@ -766,7 +796,7 @@ def main():
                       "algorithmic_bytes": nbytes, "overhead_bytes": overhead_bytes(case, S)},
            "parity": {"ok": ok, "bitwise_stable_over_timed_calls": stable,
                       **{k2: round(v2, 6) for k2, v2 in err.items()}},
-           "roofline": roof, "samples": samp}
+           "roofline": roof, "samples": samp, "device": device_info(torch)}
     if not args.no_others:
         res["context"] = {"launch_floor": launch_floor(torch, pd), "d2d_copy_roof": copy_roof(torch)}
         others = {}

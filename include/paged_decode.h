@@ -39,10 +39,14 @@
  * Device-side contract (not checkable on the host, the caller's duty):
  * 0 <= context_lens[b] <= max_blocks_per_seq * block_size, and every block
  * id the first ceil(L / block_size) entries of a row hold is in
- * [0, num_blocks). Entries past those, and cache slots at or after L in the
- * last block, are never read. Outside that range the kernels still read
- * only the row: a length above max_blocks_per_seq * block_size is taken as
- * that, and a negative length as 0 (zero output rows).
+ * [0, num_blocks). The decode does not check block ids against the pool (it
+ * is not told num_blocks): an id outside it makes the kernel read outside
+ * the caches, which can fault the GPU. Entries of a row past the first
+ * ceil(L / block_size) may be loaded but are never used as addresses, and
+ * cache slots at or after L in the last block are never read. Lengths
+ * outside that range still keep the kernels inside the row: a length above
+ * max_blocks_per_seq * block_size is taken as that, and a negative length
+ * as 0 (zero output rows).
  *
  * Workspace contract (split plans, S > 1): the first 256 KiB of a
  * workspace hold arrival counters, at every shape, and must be zero when a
@@ -50,8 +54,11 @@
  * (paged_decode_workspace_init, or any fill with zeros); every call leaves
  * the counters zero, so the same workspace then serves any later shape.
  * Calls that share a workspace must not overlap in time (issue them on one
- * stream, or order them with events): the last workgroup to finish a
- * (sequence, head group) does the merge, found through those counters.
+ * stream, or order them with events). The partitions' fp32 partial outputs
+ * and log-sum-exps are merged by the last workgroup to finish a (sequence,
+ * head group), found through those counters, or, when that merge would
+ * read more than 32 KiB in one workgroup (many query heads per KV head,
+ * many partitions), by a second kernel queued right after the first.
  *
  * Errors: every entry point returns PD_OK or one of the codes below and
  * writes nothing when it fails before launching. No C++ exception crosses
@@ -100,9 +107,10 @@ const char* paged_decode_strerror(int32_t code);
  * per partition P (a multiple of block_size) that paged_decode_attention
  * will use. Partition p covers tokens [p*P, min((p+1)*P, L)) of a sequence;
  * S = 1 means a single pass that writes `out` directly. A pure function of
- * its arguments (the heuristic is tuned for a full 256-CU MI355X); it
- * touches no device. Returns PD_OK, or the error the attention call would
- * give for the shape.
+ * its arguments: the heuristic is tuned for a whole MI355X (256 CUs) and
+ * does not query the device, so a device with fewer CUs (a partition of
+ * the GPU) gets the same plan, with the same results. It touches no device.
+ * Returns PD_OK, or the error the attention call would give for the shape.
  */
 int32_t paged_decode_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                           int32_t max_blocks_per_seq, int32_t block_size, int32_t dtype,
@@ -126,8 +134,9 @@ size_t paged_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
 int32_t paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Paged decode attention (see the top of this file). Queues one kernel on
- * `stream` (a hipStream_t; NULL is the null stream) and returns without
+ * Paged decode attention (see the top of this file). Queues its kernel on
+ * `stream` (a hipStream_t; NULL is the null stream), and for split plans
+ * whose merge runs on its own a merge kernel after it, and returns without
  * waiting. `workspace` may be NULL when paged_decode_workspace_bytes(...)
  * is 0; otherwise it must follow the workspace contract above. `scale` is
  * usually 1/sqrt(D) rounded to float.

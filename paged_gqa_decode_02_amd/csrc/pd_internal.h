@@ -7,8 +7,8 @@
 
 namespace pd {
 
-// Geometries the decode kernels are built for: head dim 64 or 128 (FP8
-// caches: 128), and up to kMaxGroup query heads per KV head.
+// Geometries the decode kernels are built for: head dim 64 or 128 (16-bit
+// and FP8 caches alike), and up to kMaxGroup query heads per KV head.
 constexpr int kMaxGroup = 128;
 
 struct Shape {
@@ -28,13 +28,15 @@ struct Plan {
   int32_t wave_tokens;       // Pw: tokens per slice, a multiple of block_size,
                              //     at most 256 blocks; NT * Pw >= P
   int32_t head_split;        // HS: virtual KV heads per KV head, G / HS <= 16
+  bool merge_kernel;         // S > 1: merge in a kernel of its own, not in the
+                             //     workgroup that finishes a head group last
 };
 
 // Most blocks one wave's slice may span (four block ids per lane).
 constexpr int kMaxWaveBlocks = 256;
 // Most waves in a workgroup: each wave holds two 16-token K/V tiles in LDS
-// (17.5 KiB at D = 128; an FP8 cache: two staging tiles and one converted
-// tile, 16.75 KiB), so 8 waves fill at most 140 KiB of a CU's 160 KiB.
+// (17.5 KiB at D = 128 for a 16-bit cache, 8.1 KiB for FP8 codes, which are
+// widened in registers), so 8 waves fill at most 140 KiB of a CU's 160 KiB.
 constexpr int kMaxWaves = 8;
 
 // Host-only checks of the scalar shape arguments; PD_* status code.

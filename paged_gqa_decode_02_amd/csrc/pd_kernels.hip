@@ -91,6 +91,8 @@ struct KArgs {
   int32_t Pw;  // tokens per slice, a multiple of the block size, <= 256 blocks
   int32_t NH;  // KV heads per workgroup
   int32_t NT;  // token slices per workgroup
+  int32_t groups;  // head groups (workgroups per partition) per sequence: Hkv / NH
+  int32_t fused;   // S > 1: the last workgroup of a head group merges (else pd_merge_kernel)
   float scale_log2;    // scale * log2(e), times k_scale for an FP8 cache
   float out_scale;     // v_scale for an FP8 cache, else 1
   uint32_t blk_bytes;  // block_size * Hkv * D * element bytes
@@ -233,18 +235,13 @@ static_assert(Geo8<128>::kStage == 4160 && Geo8<64>::kStage == 2048, "FP8 tile l
 template <int D>
 constexpr uint32_t merge_bytes() { return 16u * (D + 2) * 4u; }
 
-// Tile buffers per wave (tiles in flight while one is computed: buffers - 1),
-// as many as fit the 160 KiB of LDS for the workgroup size, up to PD_NBUF.
-#ifndef PD_NBUF
-#define PD_NBUF 2
-#endif
-constexpr uint32_t kLdsBytes = 160 * 1024;
+// Two tile buffers per wave: one tile in flight while the other is
+// computed. (Three and four buffers, all tiles of a short slice in flight at
+// once, measured slower on every decode shape.)
 template <int D, bool KV8>
 constexpr uint32_t stage_bytes() { return KV8 ? Geo8<D>::kStage : Geo<D>::kLdsTile; }
 template <int D, bool KV8>
-constexpr int tile_buffers(int nw) {
-  return PD_NBUF >= 3 && 3 * nw * stage_bytes<D, KV8>() <= kLdsBytes ? 3 : 2;
-}
+constexpr int tile_buffers(int) { return 2; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -551,10 +548,12 @@ __device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu
       lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
     }
+    // branch-free, so that every load of the batch is in flight before the
+    // first is used: a partition past n_live read zeros and enters with
+    // weight 0
     float bm = M;
 #pragma unroll
-    for (int u = 0; u < KB; ++u)
-      if (i0 + u < n_live) bm = fmaxf(bm, lse[u]);
+    for (int u = 0; u < KB; ++u) bm = fmaxf(bm, i0 + u < n_live ? lse[u] : -INFINITY);
     const float alpha = exp2_fast(M - bm);  // 0 on the first batch
     den *= alpha;
 #pragma unroll
@@ -562,14 +561,12 @@ __device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu
     M = bm;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      if (i0 + u < n_live) {
-        const float wt = exp2_fast(lse[u] - M);
-        den += wt;
+      const float wt = i0 + u < n_live ? exp2_fast(lse[u] - M) : 0.f;
+      den += wt;
 #pragma unroll
-        for (int w = 0; w < W; ++w)
+      for (int w = 0; w < W; ++w)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[w][e] = fmaf(wt, x[u][w][e], acc[w][e]);
-      }
+        for (int e = 0; e < 4; ++e) acc[w][e] = fmaf(wt, x[u][w][e], acc[w][e]);
     }
   }
   const float inv = out_scale / den;
@@ -578,9 +575,15 @@ __device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu
     if (w < nb) store4<BF16>(op + 16 * w, acc[w], inv);
 }
 
+// The arguments the first loads depend on come first and on their own, so
+// that they can arrive preloaded in scalar registers (the library is built
+// with kernel-argument preloading); the rest are read from the argument
+// segment.
 template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void pd_decode_kernel(const KArgs a) {
+void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restrict__ cl_arg,
+                      const uint16_t* __restrict__ q_arg, int32_t MB, int32_t P_arg,
+                      int32_t Pw_arg, int32_t G_arg, int32_t groups, const KArgs a) {
   using Gm = Geo<D>;
   constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
   constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
@@ -595,10 +598,15 @@ void pd_decode_kernel(const KArgs a) {
   __shared__ __align__(16) char lds0[NW * (kStage > merge_bytes<D>() ? kStage : merge_bytes<D>())];
   __shared__ __align__(16) char lds1[NW * kStage];
   __shared__ __align__(16) char lds2[kNBuf > 2 ? NW * kStage : 16];
-  const int p = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
-  const int G = a.G;
+  // grid (head group, sequence, partition), x fastest: the partitions of a
+  // head group are B * groups workgroups apart, so with the usual multiple
+  // of 8 head groups per partition they share one XCD (workgroups are dealt
+  // to the 8 XCDs in turn) and every XCD gets an even share of every
+  // sequence's heads
+  const int hg = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
+  const int G = G_arg;
   const int Hq = a.Hkv * G;
   const int nw = a.NH * a.NT;
   const int lane = threadIdx.x & 63;
@@ -613,8 +621,8 @@ void pd_decode_kernel(const KArgs a) {
     return base + w * kStage;
   };
 
-  const int t0 = p * a.P;
-  const int tw0 = t0 + ts * a.Pw;
+  const int t0 = p * P_arg;
+  const int tw0 = t0 + ts * Pw_arg;
   const int bi0 = tw0 / BS;
   // q as the MFMA B operand: column lane%16 -> head (lane%16) % G, dims
   // 32s + 8(lane/16) .. +8. Loaded before the block ids, so that waiting for
@@ -623,14 +631,14 @@ void pd_decode_kernel(const KArgs a) {
   u32x4 qb[kS];
   {
     const int hc = (lane & 15) % G;
-    const uint16_t* qp = a.q + ((size_t)b * Hq + (size_t)g * G + hc) * D + 8 * row;
+    const uint16_t* qp = q_arg + ((size_t)b * Hq + (size_t)g * G + hc) * D + 8 * row;
 #pragma unroll
     for (int s = 0; s < kS; ++s) qb[s] = *(const u32x4*)(qp + 32 * s);
   }
   // block ids of the wave's whole slice, fetched before the context length
   // is known (entries past the live ones are loaded but never used)
-  const int nb_max = min(a.Pw / BS, a.MB - bi0);
-  const int32_t* btrow = a.bt + (size_t)b * a.MB + bi0;
+  const int nb_max = min(Pw_arg / BS, MB - bi0);
+  const int32_t* btrow = bt_arg + (size_t)b * MB + bi0;
   int ids[kIdRegs];
 #pragma unroll
   for (int i = 0; i < kIdRegs; ++i) ids[i] = 64 * i + lane < nb_max ? btrow[64 * i + lane] : 0;
@@ -644,7 +652,7 @@ void pd_decode_kernel(const KArgs a) {
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // loop bounds and block addresses in scalar registers. A length past the
   // row's MB blocks counts as MB blocks (a negative one is an empty context).
-  const int L = min(__builtin_amdgcn_readfirstlane(a.cl[b]), a.MB * BS);
+  const int L = min(__builtin_amdgcn_readfirstlane(cl_arg[b]), MB * BS);
   if constexpr (!SPLIT) {
     if (L <= 0) {
       // empty context: zero rows for every query head of the group
@@ -664,7 +672,7 @@ void pd_decode_kernel(const KArgs a) {
       return;
     }
   }
-  const int tw1 = min(min(tw0 + a.Pw, t0 + a.P), L);
+  const int tw1 = min(min(tw0 + Pw_arg, t0 + P_arg), L);
   const int nst = __builtin_amdgcn_readfirstlane(
       tw0 < tw1 ? (tw1 - tw0 + kTileTok - 1) / kTileTok : 0);
   const float c = a.scale_log2;
@@ -837,10 +845,13 @@ void pd_decode_kernel(const KArgs a) {
         const int wi = (i * a.NH + hl) * G + h;
         const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
         den = fmaf(wt, s_l[wi], den);
+        // every read is issued unconditionally (blocks past nown re-read the
+        // last owned one; those o[k] are never stored), so no read waits
+        // alone inside a branch
 #pragma unroll
         for (int k = 0; k < kOwn; ++k) {
-          if (k >= nown) continue;
-          const f32x4 x = *(const f32x4*)(s_acc + wi * D + d0 + 16 * k);
+          const int kk = FAST ? k : min(k, nown - 1);
+          const f32x4 x = *(const f32x4*)(s_acc + wi * D + d0 + 16 * kk);
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[k][e] = fmaf(wt, x[e], o[k][e]);
         }
@@ -881,14 +892,17 @@ void pd_decode_kernel(const KArgs a) {
                                              WeightBias<BF16>::log2),
             rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
     }
+    // a separate merge kernel runs after this one (the kernel boundary orders
+    // the stores before its loads)
+    if (!a.fused) return;
     // the stores are complete (and past every non-coherent cache) before the
     // counter moves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ int s_last;
-    const int n_live = (L + a.P - 1) / a.P;
+    const int n_live = (L + P_arg - 1) / P_arg;
     if (threadIdx.x == 0) {
-      int32_t* cnt = a.counters + (size_t)b * (a.Hkv / a.NH) + hg;
+      int32_t* cnt = a.counters + (size_t)b * groups + hg;
       const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = old == n_live - 1;
       if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -933,9 +947,84 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
+// The LSE merge as a kernel of its own, for plans whose merge would read too
+// much for the one workgroup that finishes a head group last (many query
+// heads per KV head, many partitions): one wave per (sequence, query head),
+// lane l holding dims [l * D/64, (l + 1) * D/64) of the head, the partitions
+// merged in order p = 0 .. n-1 in batches of kBatch loads.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part,
+                                                      const int32_t* __restrict__ cl,
+                                                      uint16_t* __restrict__ out, int32_t Hq,
+                                                      int32_t S, int32_t P, int32_t cap,
+                                                      float out_scale) {
+  constexpr int kDl = D / 64;  // dims per lane
+  constexpr int kBatch = 16;
+  const int bh = blockIdx.x;  // b * Hq + h
+  const int b = bh / Hq;
+  const int lane = threadIdx.x;
+  const int L = min(__builtin_amdgcn_readfirstlane(cl[b]), cap);
+  uint16_t* op = out + (size_t)bh * D + lane * kDl;
+  if (L <= 0) {  // empty context: a zero row
+#pragma unroll
+    for (int e = 0; e < kDl; ++e) op[e] = 0;
+    return;
+  }
+  const int n = (L + P - 1) / P;
+  const float* orow = o_part + (size_t)bh * S * D + lane * kDl;
+  const float* lrow = lse_part + (size_t)bh * S;
+  float M = -INFINITY, den = 0.f, acc[kDl];
+#pragma unroll
+  for (int e = 0; e < kDl; ++e) acc[e] = 0.f;
+  // Every load of a batch is issued before any is used, and every loaded
+  // value is used, without branches: a row past n re-reads row n - 1 and
+  // enters with weight 0 (adding exact zeros), so the compiler has nothing
+  // to sink into a conditional and wait for one load at a time.
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float x[kBatch][kDl], lse[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = min(i0 + u, n - 1);
+      lse[u] = lrow[i];
+      const float* r = orow + (size_t)i * D;
+      if constexpr (kDl == 2) {
+        const float2 v2 = *(const float2*)r;
+        x[u][0] = v2.x;
+        x[u][1] = v2.y;
+      } else {
+        x[u][0] = r[0];
+      }
+    }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, lse[u]);  // repeats change nothing
+    const float alpha = exp2_fast(M - bm);  // 0 on the first batch
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < kDl; ++e) acc[e] *= alpha;
+    M = bm;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float wt = i0 + u < n ? exp2_fast(lse[u] - M) : 0.f;
+      den += wt;
+#pragma unroll
+      for (int e = 0; e < kDl; ++e) acc[e] = fmaf(wt, x[u][e], acc[e]);
+    }
+  }
+  const float inv = out_scale / den;
+#pragma unroll
+  for (int e = 0; e < kDl; ++e) op[e] = to_bits<BF16>(acc[e] * inv);
+}
+
 template <bool BF16, int BS, bool SPLIT, bool KV8, int D, bool FAST>
 hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
-  void* args[] = {(void*)&ka};
+  const int32_t* bt = ka.bt;
+  const int32_t* cl = ka.cl;
+  const uint16_t* q = ka.q;
+  int32_t mb = ka.MB, p = ka.P, pw = ka.Pw, g = ka.G, groups = ka.groups;
+  void* args[] = {(void*)&bt, (void*)&cl, (void*)&q, (void*)&mb, (void*)&p, (void*)&pw,
+                  (void*)&g, (void*)&groups, (void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
   const void* f = nw <= 4
       ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, FAST>
@@ -1009,11 +1098,13 @@ int32_t launch(const Launch& l) {
   ka.Pw = l.plan.wave_tokens;
   ka.NH = l.plan.heads_per_group;
   ka.NT = l.plan.slices;
+  ka.groups = ka.Hkv / l.plan.heads_per_group;
+  ka.fused = l.plan.merge_kernel ? 0 : 1;
   ka.scale_log2 = l.scale * 1.4426950408889634f * (l.kv_fp8 ? l.k_scale : 1.0f);
   ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
                  (l.kv_fp8 ? 1u : 2u) * (uint32_t)l.shape.D;
-  const dim3 grid(l.plan.splits, ka.Hkv / l.plan.heads_per_group, l.shape.B);
+  const dim3 grid((unsigned)ka.groups, (unsigned)l.shape.B, (unsigned)l.plan.splits);
   const int nw = l.plan.heads_per_group * l.plan.slices;
   // each wave owns a tile's bytes of every tile buffer of its workgroup; the
   // slice merge needs G * (D + 2) floats of them per wave, so G <= 16
@@ -1023,8 +1114,23 @@ int32_t launch(const Launch& l) {
   hipStream_t st = (hipStream_t)l.stream;
   const bool split = l.plan.splits > 1;
   const bool bf16 = l.shape.dtype == PD_DTYPE_BF16;
-  const hipError_t e = pick_geometry(ka, grid, l.shape.block_size, nw, bf16, split, l.kv_fp8,
-                                     l.shape.D, st);
+  hipError_t e = pick_geometry(ka, grid, l.shape.block_size, nw, bf16, split, l.kv_fp8,
+                               l.shape.D, st);
+  if (e == hipSuccess && split && l.plan.merge_kernel) {
+    int32_t hq = l.shape.Hq, S = ka.S, P = ka.P, cap = ka.MB * l.shape.block_size;
+    float osc = ka.out_scale;
+    const float* op = ka.o_part;
+    const float* lp = ka.lse_part;
+    const int32_t* cl = ka.cl;
+    uint16_t* out = (uint16_t*)ka.out;
+    void* margs[] = {(void*)&op, (void*)&lp, (void*)&cl, (void*)&out, (void*)&hq,
+                     (void*)&S,  (void*)&P,  (void*)&cap, (void*)&osc};
+    const void* mf = bf16 ? (l.shape.D == 64 ? (const void*)&pd_merge_kernel<true, 64>
+                                             : (const void*)&pd_merge_kernel<true, 128>)
+                          : (l.shape.D == 64 ? (const void*)&pd_merge_kernel<false, 64>
+                                             : (const void*)&pd_merge_kernel<false, 128>);
+    e = hipLaunchKernel(mf, dim3((unsigned)(l.shape.B * l.shape.Hq)), dim3(64), margs, 0, st);
+  }
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }
 

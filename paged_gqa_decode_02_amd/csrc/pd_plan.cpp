@@ -15,14 +15,22 @@ namespace pd {
 
 namespace {
 
-constexpr int64_t kFillWaves = 1024;  // one wave per SIMD of the 256 CUs
+// The heuristic is tuned for a whole MI355X: 256 CUs of 4 SIMDs. It does not
+// query the device (plan and workspace queries are pure functions of the
+// shape); on a device with fewer CUs the same plan runs, equally correct.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kFillWaves = 4 * kCUs;  // one wave per SIMD
 constexpr int64_t kWaves = 4;         // waves per workgroup
 constexpr int64_t kTileTok = 16;      // tokens per K/V tile of a wave
 constexpr int64_t kMinSplitTiles = 2;  // tiles per wave a split must leave
 constexpr int64_t kNoSplitTiles = 4;   // tiles per wave below which a split never pays
 constexpr int64_t kPairTiles = 16;     // tiles per wave from which split KV heads go in pairs
-constexpr int64_t kMergeRows = 128;    // most (query head, partition) rows a head's merge reads
-constexpr int64_t kMaxSplits = 1 << 16;
+// A split's merge reads NH x G/HS query heads x S partitions x D floats. Up
+// to this many bytes the workgroup that finishes a head group last merges
+// them; beyond it one CU would stream too much alone (a CU reads some
+// 30-40 GB/s), and a merge kernel of its own spreads the reads over the GPU.
+constexpr int64_t kFusedMergeBytes = 32 * 1024;
+constexpr int64_t kMaxSplits = 65535;  // grid z
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -39,7 +47,7 @@ int32_t check_shape(const Shape& s) {
   if ((int64_t)s.max_blocks_per_seq * s.block_size > INT_MAX / 2) return PD_ERR_SHAPE;
   if ((s.D != 64 && s.D != 128) || s.Hq / s.Hkv > kMaxGroup) return PD_ERR_UNSUPPORTED;
   if (s.block_size != 16 && s.block_size != 32) return PD_ERR_UNSUPPORTED;
-  // grid limits: (S, Hkv, B) with y and z below 65536
+  // grid limits: (Hkv / NH, B, S) with y and z below 65536
   if (s.B > 65535 || s.Hkv > 65535) return PD_ERR_SHAPE;
   return PD_OK;
 }
@@ -65,8 +73,9 @@ int32_t check_shape(const Shape& s) {
 //     kNoSplitTiles tiles without it;
 //   * a split call whose waves still have kPairTiles or more tiles each
 //     does better with KV heads in pairs and twice the partitions;
-//   * with more than 4 query heads per wave the merge of a head reads
-//     G/HS x S partial rows, so S is capped at kMergeRows / (G/HS);
+//   * a split whose merge would read more than kFusedMergeBytes in one
+//     workgroup (many query heads per wave, many partitions) merges in a
+//     kernel of its own;
 //   * tiles with more work per byte (an FP8 cache; 16 query heads per wave
 //     at D 64) take four slices per KV-head pair instead of two, which puts
 //     two waves on each SIMD (S and P are unchanged).
@@ -99,10 +108,6 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
       S = ceil_div(kFillWaves, units * nt);
       const int64_t s_max = cap / (nt * kMinSplitTiles * kTileTok);
       if (S > s_max) S = s_max;
-      // the merge of a virtual head reads G/HS x S partial rows; with many
-      // query heads per wave, fewer partitions
-      const int64_t g_wave = G / hs;
-      if (g_wave > 4 && S * g_wave > kMergeRows) S = kMergeRows / g_wave;
       if (S < 1) S = 1;
       if (S > 1 && pairs && nh == 1 && cap / (S * nt) >= kPairTiles * kTileTok) {
         nh = 2;
@@ -112,12 +117,6 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
     }
     P = round_up(ceil_div(cap, S), bs);
   }
-#ifdef PD_FORCE_NT  // tuning builds only: fix the slices per workgroup
-  if (PD_FORCE_NT > 0) nt = PD_FORCE_NT;
-#endif
-#ifdef PD_FORCE_NH  // tuning builds only: fix the KV heads per workgroup
-  if (PD_FORCE_NH > 0 && hkv % PD_FORCE_NH == 0) nh = PD_FORCE_NH;
-#endif
   if (nh * nt > kMaxWaves) nt = kMaxWaves / nh;
   if (nt > P / bs) nt = P / bs;  // every slice at least one block
   int64_t pw = round_up(ceil_div(P, nt), bs);
@@ -137,13 +136,14 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
   if (S > kMaxSplits) return PD_ERR_SHAPE;
   // the split path keeps one arrival counter per (sequence, head group)
   if (S > 1 && (int64_t)s.B * (hkv / nh) > kMaxCounters) return PD_ERR_UNSUPPORTED;
-  if (hkv > 65535) return PD_ERR_SHAPE;  // grid y
+  if (hkv > 65535) return PD_ERR_SHAPE;
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
   plan->heads_per_group = (int32_t)nh;
   plan->slices = (int32_t)nt;
   plan->wave_tokens = (int32_t)pw;
   plan->head_split = (int32_t)hs;
+  plan->merge_kernel = S > 1 && nh * (G / hs) * S * s.D * 4 > kFusedMergeBytes;
   return PD_OK;
 }
 

@@ -46,7 +46,7 @@ def shapes(requests=(0,)):
 
 def test_every_plan_tiles_the_context_within_the_kernel_limits(probe):
     rows = list(shapes(requests=(0, 1, 2, 3, 7, 64)))
-    for r, (st, S, P, NH, NT, Pw, HS) in zip(rows, probe([r + (0,) for r in rows])):
+    for r, (st, S, P, NH, NT, Pw, HS, MK) in zip(rows, probe([r + (0,) for r in rows])):
         B, Hq, Hkv, D, MB, bs, _, req = r
         assert st == 0, r
         cap = MB * bs
@@ -60,6 +60,9 @@ def test_every_plan_tiles_the_context_within_the_kernel_limits(probe):
         assert Pw % bs == 0 and Pw <= MAX_WAVE_BLOCKS * bs, r
         assert NT * Pw >= P > (NT - 1) * Pw, r
         assert NH in (1, 2, 4, 8) and (Hkv * HS) % NH == 0 and NH * NT <= MAX_WAVES, r
+        # the merge runs in a kernel of its own exactly when a split's merge
+        # would read more than 32 KiB in one workgroup
+        assert MK == int(S > 1 and NH * (G // HS) * S * D * 4 > 32 * 1024), r
         if req:
             # a forced S fixes P, unless the waves' reach (whole slices of 256
             # blocks) caps the partition
@@ -84,3 +87,27 @@ def test_the_planner_rejects_what_the_kernels_are_not_built_for(probe):
             (1, 30, 8, 128, 4, 16, 1, 0, 0), (65536, 32, 8, 128, 4, 16, 1, 0, 0)]
     st = [x[0] for x in probe(rows)]
     assert st == [7, 7, 7, 3, 2, 2]
+
+
+def test_the_fill_target_is_one_wave_per_simd_of_a_whole_mi355x(probe):
+    # the heuristic assumes 256 CUs x 4 SIMDs and does not query the device:
+    # 32 sequences x 8 KV heads x 4 slices = 1,024 waves fill it, one
+    # sequence fewer leaves SIMDs idle and splits the context
+    rows = [(B, 32, 8, 128, 64, 16, 1, 0, 0) for B in (31, 32)]
+    (st31, S31, *_), (st32, S32, *_) = probe(rows)
+    assert st31 == st32 == 0
+    assert S31 > 1 and S32 == 1
+    # in 4-wave workgroups: B x 8 KV heads x 4 slices x S reaches 1,024
+    B = 4
+    (_, S, _, NH, NT, _, _, _), = probe([(B, 32, 8, 128, 64, 16, 1, 0, 0)])
+    assert NH * NT == 4 and B * 8 * NT * S // NH >= 1024
+
+
+def test_many_query_heads_per_kv_head_split_to_fill_the_gpu(probe):
+    # MQA 32/1 at batch 8: 16 virtual heads in pairs fill 1,024 waves with
+    # 32 partitions, merged by a kernel of its own; 32/8 at batch 8 keeps the
+    # merge in the last workgroup (8 KiB per workgroup)
+    (st, S, P, NH, NT, Pw, HS, MK), = probe([(8, 32, 1, 128, 256, 16, 1, 0, 0)])
+    assert st == 0 and HS == 2 and NH == 2 and S * NT * 8 * HS // NH >= 1024 // 2 and MK == 1
+    (st, S, P, NH, NT, Pw, HS, MK), = probe([(8, 32, 8, 128, 64, 16, 1, 0, 0)])
+    assert st == 0 and S == 4 and MK == 0
