@@ -1,11 +1,15 @@
 """MI355X-native paged GQA decode attention.
 
-A thin ctypes binding over the C ABI in ``include/paged_decode.h`` (built as
-``_lib/libpaged_decode.so`` by ``python paged_gqa_decode_02_amd/build.py``).
-The functions keep the C names; they only marshal torch tensors into pointers,
-sizes and the current HIP stream. Every step of the computation runs in the
-library's HIP kernels. Importing this package fails if the library has not
-been built: there is no fallback.
+A thin binding over the C ABI in ``include/paged_decode.h`` and
+``include/paged_kv.h`` (built as ``_lib/libpaged_decode.so`` by ``python
+paged_gqa_decode_02_amd/build.py``). The functions keep the C names; they only
+marshal torch tensors into pointers, sizes and the HIP stream. The per-step
+entry points (the decode attention in its forms, the RoPE + KV write, the
+workspace fill) go through a compiled binding (``_lib/_pd_binding*.so``,
+``csrc/pd_binding.cpp``) that checks the tensors and calls the library in
+well under a microsecond; the rest use ctypes. Every step of the computation
+runs in the library's HIP kernels. Importing this package fails if the
+library or the binding has not been built: there is no fallback.
 """
 from __future__ import annotations
 
@@ -34,6 +38,23 @@ if not os.path.exists(LIB_PATH):
         "run `python paged_gqa_decode_02_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
+
+
+def _load_binding():
+    import importlib.util
+    import sysconfig
+    path = os.path.join(_HERE, "_lib", "_pd_binding" + sysconfig.get_config_var("EXT_SUFFIX"))
+    if not os.path.exists(path):
+        raise ImportError(f"paged_gqa_decode_02_amd: compiled binding not built ({path} "
+                          "missing); run `python paged_gqa_decode_02_amd/build.py`")
+    spec = importlib.util.spec_from_file_location("_pd_binding", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+# loaded after the library: it links to the copy loaded above
+_b = _load_binding()
 _P, _I, _Z, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
 _PI = ctypes.POINTER(ctypes.c_int32)
 
@@ -61,7 +82,6 @@ lib.paged_decode_attention_fp8.restype = _I
 lib.paged_decode_attention_noalloc.argtypes = _ATTN[:14] + [_P]
 lib.paged_decode_attention_noalloc.restype = _I
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # PAGED_DECODE_NOALLOC_SCRATCH_BYTES
-_FP8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
 class PagedDecodeError(RuntimeError):
@@ -105,13 +125,6 @@ def _stream_handle(stream, dev: int) -> int:
     if stream is None:
         return _raw_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-
-
-def _stream_object(stream):
-    """A torch stream for `stream` (a torch stream or a raw handle)."""
-    if hasattr(stream, "cuda_stream"):
-        return stream
-    return torch.cuda.ExternalStream(int(stream))
 
 
 def paged_decode_abi_version() -> int:
@@ -167,16 +180,22 @@ def _shape(q, k_cache, block_table):
     return int(B), int(Hq), int(Hkv), int(D), int(block_table.shape[1]), int(bs)
 
 
-def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    """Zero a workspace on the current (or given) stream with the library's fill kernel."""
-    dev = _gpu_index(workspace, "workspace")
-    if not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
-    rc = lib.paged_decode_workspace_init(workspace.data_ptr(),
-                                         workspace.numel() * workspace.element_size(),
-                                         _stream_handle(stream, dev))
+def _stream_arg(stream):
+    """None (the device's current stream) or the raw HIP handle of `stream`
+    (a torch stream or a raw handle), for the compiled binding."""
+    if stream is None:
+        return None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(rc: int) -> None:
     if rc != PD_OK:
         raise PagedDecodeError(rc)
+
+
+def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero a workspace on the current (or given) stream with the library's fill kernel."""
+    _check(_b.workspace_init(workspace, _stream_arg(stream)))
 
 
 def alloc_workspace(q, k_cache, block_table, num_splits=None, stream=None) -> torch.Tensor:
@@ -185,114 +204,22 @@ def alloc_workspace(q, k_cache, block_table, num_splits=None, stream=None) -> to
     B, Hq, Hkv, D, MB, bs = _shape(q, k_cache, block_table)
     _gpu_index(q, "q")
     n = _workspace_need(B, Hq, Hkv, D, MB, bs, _DTYPE_CODE.get(q.dtype, q.dtype), num_splits)
-    if stream is None:
-        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-        paged_decode_workspace_init(ws)
-        return ws
-    with torch.cuda.stream(_stream_object(stream)):
-        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
-        paged_decode_workspace_init(ws, stream)
-    return ws
-
-
-# Workspaces the binding supplies when the caller gives none: one per (GPU,
-# stream), grown when a call needs more and never freed, so that a graph that
-# captured a call keeps a valid pointer. Calls on one stream run in order and
-# leave the counters zero, so they can share it; calls on different streams
-# use different workspaces.
-_WS = {}
-_WS_RETIRED = []
-
-
-def _auto_workspace(q, need, dev, stream):
-    """(pointer, bytes) of a zeroed workspace of at least `need` bytes for a
-    call on `stream` (None: the current stream), or (0, 0) when none is needed."""
-    if need == 0:
-        return 0, 0
-    if stream is not None or torch.cuda.is_current_stream_capturing():
-        # an explicit stream, or a capture: a workspace of this call's own,
-        # allocated and zeroed on the stream the call runs on
-        ws = alloc_workspace_bytes(need, q.device, stream)
-        return ws.data_ptr(), ws.numel(), ws
-    key = (dev, _raw_stream(dev))
-    ws = _WS.get(key)
-    if ws is None or ws.numel() < need:
-        if ws is not None:
-            _WS_RETIRED.append(ws)
-        ws = alloc_workspace_bytes(need, q.device, None)
-        _WS[key] = ws
-    return ws.data_ptr(), ws.numel(), ws
+    return alloc_workspace_bytes(n, q.device, stream)
 
 
 def alloc_workspace_bytes(nbytes, device, stream=None) -> torch.Tensor:
     """A zeroed uint8 device workspace of `nbytes` (at least 256), allocated
     and zeroed on the current (or given) stream."""
-    n = max(int(nbytes), 256)
-    if stream is None:
-        ws = torch.empty(n, dtype=torch.uint8, device=device)
-        paged_decode_workspace_init(ws)
-        return ws
-    with torch.cuda.stream(_stream_object(stream)):
-        ws = torch.empty(n, dtype=torch.uint8, device=device)
-        paged_decode_workspace_init(ws, stream)
+    device = torch.device(device)
+    if device.type != "cuda":
+        raise ValueError(f"a workspace must be on a GPU, not {device}")
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    ws, rc = _b.alloc_workspace_bytes(int(nbytes), dev, _stream_arg(stream))
+    _check(rc)
     return ws
 
 
-_DECODE_NAMES = ("q", "k_cache", "v_cache", "block_table", "context_lens")
-
-
-def _decode_prep(q, k_cache, v_cache, block_table, context_lens, out, workspace, stream,
-                 num_splits, fp8, noalloc=False):
-    """Checks that keep a bad argument from reaching a kernel (host or other-GPU
-    tensors, layouts the library cannot see), then `out` and the workspace.
-    Shape rules the C ABI itself checks are left to it. Returns (dims, dev,
-    out, workspace pointer, workspace bytes, keep-alive)."""
-    dev = _gpu_index(q, "q")
-    for name, t in zip(_DECODE_NAMES, (q, k_cache, v_cache, block_table, context_lens)):
-        if t.get_device() != dev:
-            raise ValueError(f"{name} must be a GPU tensor on cuda:{dev} (got {t.device})")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    qs, ks = q.shape, k_cache.shape
-    if len(qs) != 3 or len(ks) != 4 or v_cache.shape != ks or ks[3] != qs[2]:
-        raise ValueError("q must be [B,Hq,D] and k_cache/v_cache [num_blocks,block_size,Hkv,D]")
-    dt = q.dtype
-    if fp8:
-        if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype or dt not in _DTYPE_CODE:
-            raise ValueError("k_cache/v_cache must be float8_e4m3fn (or uint8 codes), q f16 or bf16")
-    elif k_cache.dtype != dt or v_cache.dtype != dt or dt not in _DTYPE_CODE:
-        raise ValueError("q, k_cache and v_cache must share one dtype, float16 or bfloat16")
-    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_table and context_lens must be int32")
-    bts = block_table.shape
-    B = qs[0]
-    if len(bts) != 2 or bts[0] != B or context_lens.shape != (B,):
-        raise ValueError("block_table must be [B, max_blocks_per_seq] and context_lens [B]")
-    dims = (B, qs[1], ks[2], qs[2], bts[1], ks[1])
-    if out is None:
-        if stream is None:
-            out = torch.empty_like(q)
-        else:
-            with torch.cuda.stream(_stream_object(stream)):
-                out = torch.empty_like(q)
-    elif out.get_device() != dev:
-        raise ValueError(f"out must be a GPU tensor on cuda:{dev} (got {out.device})")
-    elif out.shape != qs or out.dtype != dt or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
-    if noalloc:
-        return dims, dev, out, 0, 0, None
-    if workspace is None:
-        need = _workspace_need(*dims, _DTYPE_CODE[dt], num_splits)
-        ws = _auto_workspace(q, need, dev, stream)
-        if ws[0] == 0:
-            return dims, dev, out, 0, 0, None
-        return dims, dev, out, ws[0], ws[1], ws[2]
-    if workspace.get_device() != dev:
-        raise ValueError(f"workspace must be a GPU tensor on cuda:{dev} (got {workspace.device})")
-    if not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
-    return (dims, dev, out, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            workspace)
+_PLAIN, _FP8_MODE, _NOALLOC = 0, 1, 2
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=None, *,
@@ -305,22 +232,13 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=N
     not given. Without a ``workspace`` the binding supplies one: a zeroed
     buffer kept per (GPU, stream) for calls on the current stream, or one of
     the call's own, allocated on ``stream``, for calls given a stream or made
-    under graph capture. ``num_splits`` forces the split count
-    (``paged_decode_attention_splits``). Returns ``out``.
+    under graph capture. ``scale`` defaults to D ** -0.5. ``num_splits``
+    forces the split count (``paged_decode_attention_splits``). Returns
+    ``out``.
     """
-    (B, Hq, Hkv, D, MB, bs), dev, out, wp, wn, keep = _decode_prep(
-        q, k_cache, v_cache, block_table, context_lens, out, workspace, stream, num_splits, False)
-    if scale is None:
-        scale = D ** -0.5
-    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-            context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
-            _DTYPE_CODE[q.dtype], wp, wn, _stream_handle(stream, dev))
-    if num_splits is None:
-        rc = lib.paged_decode_attention(*args)
-    else:
-        rc = lib.paged_decode_attention_splits(*args, int(num_splits))
-    if rc != PD_OK:
-        raise PagedDecodeError(rc)
+    out, rc = _b.decode(q, k_cache, v_cache, block_table, context_lens, out, workspace, scale,
+                        num_splits, _stream_arg(stream), _PLAIN, 1.0, 1.0)
+    _check(rc)
     return out
 
 
@@ -340,17 +258,9 @@ def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, context_len
     """
     if out is None:
         raise ValueError("out is required: this entry point allocates nothing")
-    (B, Hq, Hkv, D, MB, bs), dev, out, _, _, _ = _decode_prep(
-        q, k_cache, v_cache, block_table, context_lens, out, None, stream, None, False,
-        noalloc=True)
-    if scale is None:
-        scale = D ** -0.5
-    rc = lib.paged_decode_attention_noalloc(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
-        _DTYPE_CODE[q.dtype], _stream_handle(stream, dev))
-    if rc != PD_OK:
-        raise PagedDecodeError(rc)
+    out, rc = _b.decode(q, k_cache, v_cache, block_table, context_lens, out, None, scale, None,
+                        _stream_arg(stream), _NOALLOC, 1.0, 1.0)
+    _check(rc)
     return out
 
 
@@ -363,17 +273,10 @@ def paged_decode_attention_fp8(q, k_cache, v_cache, block_table, context_lens, o
     uint8 holding the codes), standing for code * k_scale and code * v_scale;
     q (and out) f16 or bf16 [B,Hq,D]. Otherwise as ``paged_decode_attention``.
     """
-    (B, Hq, Hkv, D, MB, bs), dev, out, wp, wn, keep = _decode_prep(
-        q, k_cache, v_cache, block_table, context_lens, out, workspace, stream, num_splits, True)
-    if scale is None:
-        scale = D ** -0.5
-    rc = lib.paged_decode_attention_fp8(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        context_lens.data_ptr(), MB, out.data_ptr(), B, Hq, Hkv, D, bs, float(scale),
-        _DTYPE_CODE[q.dtype], float(k_scale), float(v_scale), wp, wn, _stream_handle(stream, dev),
-        0 if num_splits is None else int(num_splits))
-    if rc != PD_OK:
-        raise PagedDecodeError(rc)
+    out, rc = _b.decode(q, k_cache, v_cache, block_table, context_lens, out, workspace, scale,
+                        num_splits, _stream_arg(stream), _FP8_MODE, float(k_scale),
+                        float(v_scale))
+    _check(rc)
     return out
 
 
@@ -411,62 +314,6 @@ def rope_cos_sin_table(max_position, rotary_dim, base, *, device="cuda", out=Non
     return out
 
 
-def _rows(name, t, H, D):
-    """Row stride (elements) of a [T, H, D] view whose heads are contiguous."""
-    sh = t.shape
-    if len(sh) != 3 or sh[1] != H or sh[2] != D:
-        raise ValueError(f"{name} must be [T, {H}, {D}]")
-    st = t.stride()
-    if sh[0] > 0 and (st[2] != 1 or st[1] != D):
-        raise ValueError(f"{name}: heads of a token must be contiguous (strides [*, D, 1])")
-    return st[0] if sh[0] > 1 else H * D
-
-
-def _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out, fp8, stream):
-    """Checked pointer and size arguments shared by the two RoPE writes, and
-    the stream handle (q_out, when not given, is allocated on that stream)."""
-    dev = _gpu_index(q, "q")
-    _same_gpu(dev, k=k, v=v, positions=positions, slot_mapping=slot_mapping, cos_sin=cos_sin,
-              k_cache=k_cache, v_cache=v_cache, q_out=q_out)
-    dt = q.dtype
-    if dt not in _DTYPE_CODE or k.dtype != dt or v.dtype != dt:
-        raise ValueError("q, k and v must share one dtype, float16 or bfloat16")
-    if fp8:
-        if k_cache.dtype not in _FP8 or v_cache.dtype != k_cache.dtype:
-            raise ValueError("FP8 caches must be float8_e4m3fn (or uint8 codes), both alike")
-    elif k_cache.dtype != dt or v_cache.dtype != dt:
-        raise ValueError("the caches must have q's dtype")
-    cs = k_cache.shape
-    if len(cs) != 4 or v_cache.shape != cs or not k_cache.is_contiguous() or \
-            not v_cache.is_contiguous():
-        raise ValueError("k_cache/v_cache must be contiguous [num_blocks,block_size,Hkv,D]")
-    NB, bs, Hkv, D = cs
-    qsh = q.shape
-    T, Hq = qsh[0], qsh[1]
-    qs, ks, vs = _rows("q", q, Hq, D), _rows("k", k, Hkv, D), _rows("v", v, Hkv, D)
-    if k.shape[0] != T or v.shape[0] != T:
-        raise ValueError("q, k and v must have the same number of tokens")
-    for name, t in (("positions", positions), ("slot_mapping", slot_mapping)):
-        if t.dtype != torch.int32 or t.shape != (T,) or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 [T] tensor")
-    tsh = cos_sin.shape
-    if cos_sin.dtype != torch.float32 or len(tsh) != 2 or tsh[1] != D or \
-            not cos_sin.is_contiguous():
-        raise ValueError("cos_sin must be a contiguous float32 [max_position, D] tensor")
-    if q_out is None:
-        if stream is None:
-            q_out = torch.empty((T, Hq, D), dtype=dt, device=q.device)
-        else:
-            with torch.cuda.stream(_stream_object(stream)):
-                q_out = torch.empty((T, Hq, D), dtype=dt, device=q.device)
-    elif q_out.shape != (T, Hq, D) or q_out.dtype != dt or not q_out.is_contiguous():
-        raise ValueError("q_out must be a contiguous [T, Hq, D] tensor of q's dtype")
-    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), qs, ks, vs, positions.data_ptr(),
-            slot_mapping.data_ptr(), cos_sin.data_ptr(), tsh[0], q_out.data_ptr(),
-            k_cache.data_ptr(), v_cache.data_ptr(), NB, T, Hq, Hkv, D, bs, _DTYPE_CODE[dt]]
-    return args, q_out, _stream_handle(stream, dev)
-
-
 def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out=None,
                         *, stream=None):
     """RoPE + paged KV-cache write (``rope_paged_kv_write``) on the current
@@ -478,11 +325,9 @@ def rope_paged_kv_write(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_ca
     k_cache/v_cache [num_blocks,block_size,Hkv,D] (written in place). Returns
     q_out [T,Hq,D] (allocated when not given; may be q itself).
     """
-    args, q_out, h = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
-                                q_out, False, stream)
-    rc = lib.rope_paged_kv_write(*args, h)
-    if rc != PD_OK:
-        raise PagedDecodeError(rc)
+    q_out, rc = _b.rope(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
+                        False, 1.0, 1.0, _stream_arg(stream))
+    _check(rc)
     return q_out
 
 
@@ -493,11 +338,9 @@ def rope_paged_kv_write_fp8(q, k, v, positions, slot_mapping, cos_sin, k_cache, 
     [num_blocks,block_size,Hkv,D] receiving the E4M3FN codes of the rotated
     key times the float32 reciprocal of k_scale and of the value times that
     of v_scale. Returns q_out (16-bit)."""
-    args, q_out, h = _rope_args(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
-                                q_out, True, stream)
-    rc = lib.rope_paged_kv_write_fp8(*args, float(k_scale), float(v_scale), h)
-    if rc != PD_OK:
-        raise PagedDecodeError(rc)
+    q_out, rc = _b.rope(q, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache, q_out,
+                        True, float(k_scale), float(v_scale), _stream_arg(stream))
+    _check(rc)
     return q_out
 
 

@@ -5,11 +5,16 @@
 (run as a file: importing the package would load the library it rebuilds)
 
 Compiles the kernels (``csrc/pd_kernels.hip``, ``csrc/pd_rope.hip``,
-``csrc/pd_blocks.hip``) and the host side (``csrc/pd_api.cpp``,
-``csrc/pd_kv_api.cpp``, ``csrc/pd_plan.cpp``) with hipcc into one shared
-library exporting the C ABI of ``include/paged_decode.h`` and
-``include/paged_kv.h``. Packed fp32 VALU
-instructions are disabled for the device code.
+``csrc/pd_blocks.hip``, ``csrc/pd_scratch.hip``) and the host side
+(``csrc/pd_api.cpp``, ``csrc/pd_kv_api.cpp``, ``csrc/pd_plan.cpp``) with hipcc
+into one shared library exporting the C ABI of ``include/paged_decode.h`` and
+``include/paged_kv.h``. Packed fp32 VALU instructions are disabled for the
+device code.
+
+Then compiles the Python binding of the per-step entry points
+(``csrc/pd_binding.cpp``, argument checks and marshalling over torch
+tensors) with g++ against torch's headers into ``_lib/_pd_binding*.so``,
+linked to the library above.
 """
 from __future__ import annotations
 
@@ -25,6 +30,7 @@ LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libpaged_decode.so")
 ARCH = "gfx950"
 
+BINDING_SRC = "pd_binding.cpp"
 SOURCES = ["pd_kernels.hip", "pd_rope.hip", "pd_blocks.hip", "pd_scratch.hip", "pd_api.cpp",
            "pd_kv_api.cpp", "pd_plan.cpp"]
 HEADERS = ["pd_internal.h", "pd_fp8_code.h"]
@@ -51,7 +57,9 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
            "-I", os.path.join(ROOT, "include")]
     cmd += list(extra_flags or [])
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", tmp]
+    # the binding names the library by this soname; the package loads it
+    # by path first, and the loader then reuses that copy
+    cmd += ["-Wl,-soname,libpaged_decode.so", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,5 +74,55 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     return LIB
 
 
+def binding_path() -> str:
+    import sysconfig
+    return os.path.join(LIB_DIR, "_pd_binding" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def build_binding(verbose: bool = False) -> str:
+    """Compile the Python binding (always) against the built library and
+    torch's headers; return its path."""
+    import sysconfig
+
+    import torch.utils.cpp_extension as ce
+    out = binding_path()
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-fPIC", "-shared",
+           "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+           f"-D_GLIBCXX_USE_CXX11_ABI={int(torch_cxx11_abi())}",
+           # torch's ROCm headers: HIP streams present themselves as CUDA ones
+           "-D__HIP_PLATFORM_AMD__=1", "-DUSE_ROCM=1", "-DTORCH_EXTENSION_NAME=_pd_binding",
+           "-I", os.path.join(ROOT, "include")]
+    for inc in ce.include_paths() + [rocm_include(), sysconfig.get_paths()["include"]]:
+        cmd += ["-isystem", inc]
+    cmd += [os.path.join(CSRC, BINDING_SRC), "-o", tmp, "-L", LIB_DIR, "-lpaged_decode",
+            "-Wl,-rpath,$ORIGIN"]
+    for d in ce.library_paths():
+        cmd += ["-L", d, "-Wl,-rpath," + d]
+    cmd += ["-lc10", "-lc10_hip", "-ltorch", "-ltorch_cpu", "-ltorch_hip", "-ltorch_python"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed ({res.returncode}) building the binding:\n{res.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
+def torch_cxx11_abi() -> bool:
+    import torch
+    return bool(torch._C._GLIBCXX_USE_CXX11_ABI)
+
+
+def rocm_include() -> str:
+    root = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(root, "include")
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """The library, then the binding linked to it."""
+    return [build(verbose), build_binding(verbose)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

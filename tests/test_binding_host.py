@@ -73,3 +73,17 @@ def test_block_moves_refuse_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         pd.paged_kv_remap_block_table(torch.zeros(4, dtype=torch.int32),
                                       torch.arange(8, dtype=torch.int32))
+
+
+def test_the_compiled_binding_is_the_in_tree_one():
+    # the per-step calls go through _lib/_pd_binding*.so, built in-tree and
+    # linked to the library the package loaded
+    import os
+    lib_dir = os.path.dirname(pd.LIB_PATH)
+    assert os.path.dirname(os.path.abspath(pd._b.__file__)) == lib_dir
+    for name in ("decode", "rope", "workspace_init", "alloc_workspace_bytes"):
+        assert callable(getattr(pd._b, name))
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert maps.count(os.path.realpath(pd.LIB_PATH)) >= 1
+    assert "libpaged_decode.so" not in maps.replace(os.path.realpath(pd.LIB_PATH), "")

@@ -1,6 +1,9 @@
-"""The binding's refusals on a GPU: a host tensor mixed with device ones, and
-an `out` of the wrong shape, dtype or layout, are refused before any library
-call, and the next valid call still matches the oracle."""
+"""The binding on a GPU: a host tensor mixed with device ones, and an `out`
+of the wrong shape, dtype or layout, are refused before any library call,
+and the next valid call still matches the oracle; calls that leave `out`,
+the workspace or `q_out` to the binding get them on the stream they run on
+(a given stream, a raw handle, overlapping streams, graph capture)."""
+import numpy as np
 import pytest
 import torch
 
@@ -49,3 +52,90 @@ def test_rope_write_with_a_host_cache_is_refused():
     kc = torch.zeros(2, 16, Hkv, D, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         pd.rope_paged_kv_write(q, k, k.clone(), pos, slots, cs, kc, kc.clone())
+
+
+def test_calls_without_out_or_workspace_on_given_streams():
+    # out and the split workspace are supplied by the binding, allocated on
+    # the stream the call runs on: a torch stream, a raw handle, and two
+    # streams whose calls overlap (each stream's cached workspace is its own)
+    import paged_gqa_decode_02_amd as pd
+    cases = [workloads.splitk(4, 1024, seed=31), workloads.splitk(8, 2048, seed=32)]
+    devs = [device_case(c) for c in cases]
+    refs = [oracle.attention_case(c)[0] for c in cases]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for c, d in zip(cases, devs):
+        print(c.describe(), pd.paged_decode_plan(c.B, c.Hq, c.Hkv, c.D, c.max_blocks_per_seq,
+                                                 c.block_size, torch.bfloat16), flush=True)
+    torch.cuda.synchronize()
+    out_a = pd.paged_decode_attention(*devs[0], scale=cases[0].scale, stream=s1)
+    out_b = pd.paged_decode_attention(*devs[1], scale=cases[1].scale, stream=s2.cuda_stream)
+    torch.cuda.synchronize()
+    compare(out_bits(out_a), refs[0], "bf16", what="torch stream")
+    compare(out_bits(out_b), refs[1], "bf16", what="raw handle")
+    outs = {}
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            torch.cuda._sleep(1_000_000)
+            outs[1] = pd.paged_decode_attention(*devs[0], scale=cases[0].scale)
+        with torch.cuda.stream(s2):
+            outs[2] = pd.paged_decode_attention(*devs[1], scale=cases[1].scale)
+        torch.cuda.synchronize()
+        compare(out_bits(outs[1]), refs[0], "bf16", what=f"overlapping streams s1 {rep}")
+        compare(out_bits(outs[2]), refs[1], "bf16", what=f"overlapping streams s2 {rep}")
+
+
+def test_graph_capture_without_a_workspace():
+    # under capture the binding gives the call a workspace of its own from
+    # the graph's pool, zeroed by a captured fill kernel on every replay
+    import paged_gqa_decode_02_amd as pd
+    c = workloads.splitk(4, 2048, seed=33)
+    q, k, v, bt, cl = device_case(c)
+    S, _ = pd.paged_decode_plan(c.B, c.Hq, c.Hkv, c.D, c.max_blocks_per_seq, c.block_size,
+                                torch.bfloat16)
+    print(c.describe(), "S", S, flush=True)
+    assert S > 1
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pd.paged_decode_attention(q, k, v, bt, cl, out, scale=c.scale)
+    rng = np.random.default_rng(34)
+    for rep in range(4):
+        lens = rng.integers(1, 2049, size=c.B).astype(np.int32)
+        cl.copy_(torch.from_numpy(lens))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_bits(out)
+        assert np.array_equal(got, out_bits(pd.paged_decode_attention(q, k, v, bt, cl,
+                                                                      scale=c.scale))), rep
+        c.context_lens[:] = lens
+        compare(got, oracle.attention_case(c)[0], "bf16", what=f"capture replay {rep}")
+
+
+def test_rope_write_allocates_q_out_on_the_given_stream():
+    import paged_gqa_decode_02_amd as pd
+    T, Hq, Hkv, D, bs = 5, 8, 2, 128, 16
+    g = torch.Generator().manual_seed(35)
+    qkv = torch.randn(T, Hq + 2 * Hkv, D, generator=g).to(torch.bfloat16).cuda()
+    q, k, v = qkv[:, :Hq], qkv[:, Hq:Hq + Hkv], qkv[:, Hq + Hkv:]
+    pos = torch.tensor([0, 7, 100, 3, 4095], dtype=torch.int32, device="cuda")
+    slots = torch.tensor([3, 17, 40, -1, 63], dtype=torch.int32, device="cuda")
+    cs = pd.rope_cos_sin_table(4096, D, 10000.0)
+    kc = torch.zeros(4, bs, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    ref_q = pd.rope_paged_kv_write(q, k, v, pos, slots, cs, kc, vc)
+    ref_k, ref_v = kc.clone(), vc.clone()
+    kc.zero_()
+    vc.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    got_q = pd.rope_paged_kv_write(q, k, v, pos, slots, cs, kc, vc, stream=s)
+    s.synchronize()
+    assert torch.equal(got_q.view(torch.int16), ref_q.view(torch.int16))
+    assert torch.equal(kc.view(torch.int16), ref_k.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), ref_v.view(torch.int16))
