@@ -78,7 +78,9 @@ int32_t check_shape(const Shape& s) {
 //     kernel of its own;
 //   * tiles with more work per byte (an FP8 cache; 16 query heads per wave
 //     at D 64) take four slices per KV-head pair instead of two, which puts
-//     two waves on each SIMD (S and P are unchanged).
+//     two waves on each SIMD (S and P are unchanged); an unsplit FP8 call
+//     with one KV head per workgroup likewise takes eight slices instead
+//     of four.
 // A forced S fixes P instead and cuts it into up to NT slices.
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_fp8) {
   int32_t st = check_shape(s);
@@ -129,6 +131,13 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
   // heads then cut the partition, now fixed, into four slices instead of two
   if (nh == 2 && nt == 2 && (kv_fp8 || (s.D == 64 && G / hs > 8)) && P / bs > 2) {
     nt = P / bs < 4 ? P / bs : 4;
+    pw = round_up(ceil_div(P, nt), bs);
+  }
+  // likewise an unsplit FP8 call with one KV head per workgroup: eight
+  // slices instead of four (a split one keeps four: its merge then reads
+  // twice the slices and costs more than the second wave per SIMD gains)
+  if (nh == 1 && nt == 4 && kv_fp8 && ceil_div(cap, P) == 1 && P / bs >= 8) {
+    nt = 8;
     pw = round_up(ceil_div(P, nt), bs);
   }
   nt = ceil_div(P, pw);  // drop slices that would start past the partition
