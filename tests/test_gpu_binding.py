@@ -67,6 +67,9 @@ def test_calls_without_out_or_workspace_on_given_streams():
         print(c.describe(), pd.paged_decode_plan(c.B, c.Hq, c.Hkv, c.D, c.max_blocks_per_seq,
                                                  c.block_size, torch.bfloat16), flush=True)
     torch.cuda.synchronize()
+    # the current stream is held up: anything the binding queued there for
+    # these calls (zeroing their workspaces) would run after the decode
+    torch.cuda._sleep(2_000_000)
     out_a = pd.paged_decode_attention(*devs[0], scale=cases[0].scale, stream=s1)
     out_b = pd.paged_decode_attention(*devs[1], scale=cases[1].scale, stream=s2.cuda_stream)
     torch.cuda.synchronize()
