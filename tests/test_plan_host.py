@@ -111,3 +111,22 @@ def test_many_query_heads_per_kv_head_split_to_fill_the_gpu(probe):
     assert st == 0 and HS == 2 and NH == 2 and S * NT * 8 * HS // NH >= 1024 // 2 and MK == 1
     (st, S, P, NH, NT, Pw, HS, MK), = probe([(8, 32, 8, 128, 64, 16, 1, 0, 0)])
     assert st == 0 and S == 4 and MK == 0
+
+
+def test_unsplit_fp8_plans_with_one_kv_head_per_workgroup_take_eight_slices(probe):
+    # an FP8 cache's tiles carry more work per byte: an unsplit plan with
+    # one KV head per workgroup puts two waves on each SIMD (eight slices);
+    # the 16-bit plan of the same shape keeps four, and a split FP8 plan
+    # keeps four as well
+    ragged = (32, 32, 8, 128, 32, 32, 1, 0)        # contexts up to 1,024, block 32
+    uniform = (32, 32, 8, 128, 64, 16, 1, 0)       # B32 ctx1024
+    split = (8, 32, 8, 128, 64, 16, 1, 0)          # B8 ctx1024: S = 4
+    short = (1, 32, 8, 128, 4, 16, 1, 0)           # 64 tokens: four blocks
+    rows = probe([r + (fp8,) for r in (ragged, uniform, split, short) for fp8 in (0, 1)])
+    (r16, r8), (u16, u8), (s16, s8), (t16, t8) = zip(rows[::2], rows[1::2])
+    for a, b in ((r16, r8), (u16, u8)):
+        assert a[1] == b[1] == 1 and a[2] == b[2], (a, b)   # same S and P
+        assert a[3] == b[3] == 1 and a[4] == 4 and b[4] == 8, (a, b)
+        assert b[5] * b[4] == b[2], b                       # eight equal slices
+    assert s16[1] == s8[1] > 1 and s16[4] == s8[4] == 4, (s16, s8)
+    assert t8[4] == t16[4] == 4, (t16, t8)                  # a slice is at least a block
