@@ -104,9 +104,11 @@ Tensor fresh_workspace(size_t need, int dev, const OptInt& stream, const Stream&
 // captured a call keeps a valid pointer. Calls on one stream run in order
 // and leave the counters zero, so they can share one; calls on different
 // streams use different workspaces.
+// (Held in objects that are never destroyed: their tensors must not be freed
+// by static destructors at exit, after torch's allocator may be gone.)
 std::mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, Tensor> g_ws;
-std::vector<Tensor> g_ws_retired;
+auto& g_ws = *new std::map<std::pair<int, uintptr_t>, Tensor>();
+auto& g_ws_retired = *new std::vector<Tensor>();
 
 // (pointer, bytes, keep-alive) of a zeroed workspace of at least `need`
 // bytes for a call on `s`, or nulls when none is needed; `rc` receives the
