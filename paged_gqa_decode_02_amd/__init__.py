@@ -72,6 +72,9 @@ lib.paged_decode_workspace_bytes_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, 
 lib.paged_decode_workspace_bytes_splits.restype = _Z
 lib.paged_decode_workspace_init.argtypes = [_P, _Z, _P]
 lib.paged_decode_workspace_init.restype = _I
+# The per-step entry points below are called through the compiled binding;
+# their ctypes declarations serve direct calls of the C ABI (the host-side
+# ABI tests make them).
 _ATTN = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]
 lib.paged_decode_attention.argtypes = _ATTN
 lib.paged_decode_attention.restype = _I
