@@ -167,6 +167,8 @@ std::tuple<Tensor, int64_t> decode(const Tensor& q, const Tensor& k, const Tenso
     refuse("block_table must be [B, max_blocks_per_seq] and context_lens [B]");
   if (!fits_int32({B, qs[1], ks[2], qs[2], bts[1], ks[1]}))
     refuse("a size of q, the caches or block_table exceeds the int32 range of the C ABI");
+  if (num_splits && (*num_splits < INT32_MIN || *num_splits > INT32_MAX))
+    refuse("num_splits exceeds the int32 range of the C ABI");
   const int32_t Hq = (int32_t)qs[1], Hkv = (int32_t)ks[2], D = (int32_t)qs[2];
   const int32_t MB = (int32_t)bts[1], bs = (int32_t)ks[1];
   if (out) {
