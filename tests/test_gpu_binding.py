@@ -142,3 +142,49 @@ def test_rope_write_allocates_q_out_on_the_given_stream():
     assert torch.equal(got_q.view(torch.int16), ref_q.view(torch.int16))
     assert torch.equal(kc.view(torch.int16), ref_k.view(torch.int16))
     assert torch.equal(vc.view(torch.int16), ref_v.view(torch.int16))
+
+
+def test_empty_batch_and_empty_token_list_pass_through():
+    # a batch of no sequences and a write of no tokens queue nothing and
+    # return empty outputs
+    import paged_gqa_decode_02_amd as pd
+    q = torch.empty(0, 32, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(4, 16, 8, 128, dtype=torch.bfloat16, device="cuda")
+    bt = torch.empty(0, 4, dtype=torch.int32, device="cuda")
+    cl = torch.empty(0, dtype=torch.int32, device="cuda")
+    out = pd.paged_decode_attention(q, k, k, bt, cl)
+    assert out.shape == (0, 32, 128)
+    out = pd.paged_decode_attention_noalloc(q, k, k, bt, cl, torch.empty_like(q))
+    assert out.shape == (0, 32, 128)
+    qr = torch.empty(0, 32, 128, dtype=torch.bfloat16, device="cuda")
+    kr = torch.empty(0, 8, 128, dtype=torch.bfloat16, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    cs = pd.rope_cos_sin_table(16, 128, 10000.0)
+    before = k.clone()
+    q_out = pd.rope_paged_kv_write(qr, kr, kr, none, none, cs, k, k.clone())
+    torch.cuda.synchronize()
+    assert q_out.shape == (0, 32, 128) and torch.equal(k, before)
+
+
+def test_layouts_the_library_cannot_see_are_refused():
+    import paged_gqa_decode_02_amd as pd
+    c = workloads.tiny(0)
+    q, k, v, bt, cl = device_case(c)
+    qt = torch.empty(q.shape[2], q.shape[1], q.shape[0], dtype=q.dtype,
+                     device="cuda").permute(2, 1, 0)
+    qt.copy_(q)
+    with pytest.raises(ValueError, match="contiguous"):
+        pd.paged_decode_attention(qt, k, v, bt, cl)
+    with pytest.raises(ValueError, match="int32"):
+        pd.paged_decode_attention(q, k, v, bt, cl, num_splits=2 ** 40)
+    with pytest.raises(ValueError, match="out is required"):
+        pd.paged_decode_attention_noalloc(q, k, v, bt, cl, None)
+    # a q whose heads are not contiguous cannot be a RoPE input
+    T, Hq, Hkv, D = 2, 4, 2, 64
+    x = torch.zeros(T, D, Hq, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    kk = torch.zeros(T, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(T, dtype=torch.int32, device="cuda")
+    cs = pd.rope_cos_sin_table(8, D, 10000.0)
+    kc = torch.zeros(2, 16, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="heads of a token must be contiguous"):
+        pd.rope_paged_kv_write(x, kk, kk, pos, pos, cs, kc, kc.clone())
