@@ -11,7 +11,7 @@ import paged_gqa_decode_02_amd as pd
 import workloads
 from workloads import blocks as wb
 
-from helpers import out_bits, run_library
+from helpers import out_bits
 
 pytestmark = pytest.mark.gpu
 
