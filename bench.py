@@ -595,9 +595,19 @@ def host_cpu() -> dict:
             "cpu_vendor": info.get("vendor_id"),
             "cpu_family_model_stepping": [info.get("cpu family"), info.get("model"),
                                           info.get("stepping")],
+            "cpu_core_family": _core_family(info.get("vendor_id"), info.get("cpu family")),
             "host_logical_cpus": os.cpu_count(),
             "host_physical_cores": len(phys) if phys and None not in next(iter(phys)) else None,
             "cpus_available_to_process": avail}
+
+
+def _core_family(vendor, family):
+    """AMD's published core family for its CPU family numbers (a virtual
+    machine often reports only a generic model name)."""
+    if vendor != "AuthenticAMD" or family is None:
+        return None
+    return {"23": "Zen / Zen 2 (family 17h)", "25": "Zen 3 / Zen 4 (family 19h)",
+            "26": "Zen 5 (family 1Ah)"}.get(str(family))
 
 
 def device_info(torch) -> dict:
