@@ -50,8 +50,9 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # the decode kernel's first arguments (block table, lengths, q and
-           # the sizes their addresses need) arrive in scalar registers
-           "-mllvm", "-amdgpu-kernarg-preload-count=8",
+           # the sizes and packed geometry their addresses need) arrive in
+           # scalar registers
+           "-mllvm", "-amdgpu-kernarg-preload-count=9",
            "-Wall", "-Wno-unused-function", "-Werror=float-conversion",
            "-Werror=implicit-int-float-conversion",
            "-I", os.path.join(ROOT, "include")]

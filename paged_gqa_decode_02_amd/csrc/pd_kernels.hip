@@ -82,6 +82,8 @@ struct KArgs {
   float* o_part;      // [B, Hq, S, D]
   float* lse_part;    // [B, Hq, S], log2 domain
   int32_t* counters;  // [B, Hkv / NH], at the start of the workspace
+  // Hkv, HS and NH serve the host: the kernel takes NH, HS and the physical
+  // KV heads packed in its preloaded `geo` argument
   int32_t Hkv;  // virtual KV heads: physical KV heads x HS
   int32_t HS;   // virtual KV heads per physical KV head
   int32_t G;    // query heads per virtual KV head, <= 16
@@ -583,7 +585,8 @@ template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restrict__ cl_arg,
                       const uint16_t* __restrict__ q_arg, int32_t MB, int32_t P_arg,
-                      int32_t Pw_arg, int32_t G_arg, int32_t groups, const KArgs a) {
+                      int32_t Pw_arg, int32_t G_arg, int32_t groups, int32_t geo,
+                      const KArgs a) {
   using Gm = Geo<D>;
   constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
   constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
@@ -607,14 +610,17 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
   const int b = blockIdx.y;
   const int p = blockIdx.z;
   const int G = G_arg;
-  const int Hq = a.Hkv * G;
-  const int nw = a.NH * a.NT;
+  // the geometry the first loads' addresses need, from a preloaded argument:
+  // NH (bits 0-3), HS (bits 4-11), physical KV heads (bits 12-31)
+  const int NH = geo & 15, HS = (geo >> 4) & 255, Hkv_phys = geo >> 12;
+  const int Hq = Hkv_phys * HS * G;
+  const int nw = NH * a.NT;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hl = w % a.NH;  // KV head within the workgroup's group
-  const int ts = w / a.NH;  // token slice
-  const int g = hg * a.NH + hl;  // virtual KV head
-  const int gk = g / a.HS;        // the physical KV head it reads
+  const int hl = w % NH;  // KV head within the workgroup's group
+  const int ts = w / NH;  // token slice
+  const int g = hg * NH + hl;  // virtual KV head
+  const int gk = g / HS;        // the physical KV head it reads
   const int row = lane >> 4;
   auto tile_buf = [&](int d) -> char* {
     char* base = d == 0 ? lds0 : d == 1 ? lds1 : lds2;
@@ -656,8 +662,8 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
   if constexpr (!SPLIT) {
     if (L <= 0) {
       // empty context: zero rows for every query head of the group
-      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * a.NH * G) * D;
-      for (int i = threadIdx.x; i < a.NH * G * D / 8; i += nw * 64)
+      uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * NH * G) * D;
+      for (int i = threadIdx.x; i < NH * G * D / 8; i += nw * 64)
         *(u32x4*)(o + i * 8) = u32x4{0u, 0u, 0u, 0u};
       return;
     }
@@ -665,8 +671,8 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
     if (t0 >= L) {  // empty partition: neither counted nor merged
       if (L <= 0 && p == 0) {
         // empty context: partition 0 writes the zero rows, no merge runs
-        uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * a.NH * G) * D;
-        for (int i = threadIdx.x; i < a.NH * G * D / 8; i += nw * 64)
+        uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * NH * G) * D;
+        for (int i = threadIdx.x; i < NH * G * D / 8; i += nw * 64)
           *(u32x4*)(o + i * 8) = u32x4{0u, 0u, 0u, 0u};
       }
       return;
@@ -678,7 +684,7 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
   const float c = a.scale_log2;
   constexpr uint32_t kRow = KV8 ? G8::kRowBytes : Gm::kRowBytes;
   constexpr int kChunks = KV8 ? G8::kChunks : Gm::kChunks;  // 16-byte chunks per row as loaded
-  const uint32_t tok_bytes = (a.Hkv / a.HS) * kRow;  // physical KV heads
+  const uint32_t tok_bytes = Hkv_phys * kRow;  // a token row: every physical KV head
   // global offsets of this lane's 16 bytes in load instruction 0 of a tile:
   // a row takes C lanes (64 / C rows per instruction), the chunks in the
   // rotated order of the tile layouts above
@@ -837,12 +843,12 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
     __syncthreads();
     if (ts == 0 && own.active) {
       float M = m_r;
-      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * a.NH + hl) * G + h]);
+      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * NH + hl) * G + h]);
       float den = 0.f;
 #pragma unroll
       for (int k = 0; k < kOwn; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int i = 0; i < a.NT; ++i) {
-        const int wi = (i * a.NH + hl) * G + h;
+        const int wi = (i * NH + hl) * G + h;
         const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
         den = fmaf(wt, s_l[wi], den);
         // every read is issued unconditionally (blocks past nown re-read the
@@ -1023,8 +1029,9 @@ hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   const int32_t* cl = ka.cl;
   const uint16_t* q = ka.q;
   int32_t mb = ka.MB, p = ka.P, pw = ka.Pw, g = ka.G, groups = ka.groups;
+  int32_t geo = ka.NH | (ka.HS << 4) | ((ka.Hkv / ka.HS) << 12);
   void* args[] = {(void*)&bt, (void*)&cl, (void*)&q, (void*)&mb, (void*)&p, (void*)&pw,
-                  (void*)&g, (void*)&groups, (void*)&ka};
+                  (void*)&g, (void*)&groups, (void*)&geo, (void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
   const void* f = nw <= 4
       ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, FAST>
@@ -1108,7 +1115,9 @@ int32_t launch(const Launch& l) {
   const int nw = l.plan.heads_per_group * l.plan.slices;
   // each wave owns a tile's bytes of every tile buffer of its workgroup; the
   // slice merge needs G * (D + 2) floats of them per wave, so G <= 16
-  if (nw < 1 || nw > kMaxWaves || hs < 1 || ka.Hkv % l.plan.heads_per_group != 0 ||
+  // (NH, HS and the physical KV heads travel packed in one argument)
+  if (nw < 1 || nw > kMaxWaves || hs < 1 || hs > 255 || l.plan.heads_per_group > 15 ||
+      l.shape.Hkv >= (1 << 19) || ka.Hkv % l.plan.heads_per_group != 0 ||
       ka.G * ka.Hkv != l.shape.Hq || ka.G > 16 || (l.shape.D != 64 && l.shape.D != 128))
     return PD_ERR_INTERNAL;
   hipStream_t st = (hipStream_t)l.stream;
