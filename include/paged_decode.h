@@ -27,7 +27,6 @@
  *   block_table    int32 [B, max_blocks_per_seq]
  *   context_lens   int32 [B]
  *   workspace      caller-owned device scratch for the split-K partials
- *                  and per-(sequence, head group) arrival counters
  *
  * Ownership: every pointer is borrowed device memory that the caller keeps
  * alive until the work queued on `stream` has finished. The library never
@@ -48,17 +47,14 @@
  * max_blocks_per_seq * block_size is taken as that, and a negative length
  * as 0 (zero output rows).
  *
- * Workspace contract (split plans, S > 1): the first 256 KiB of a
- * workspace hold arrival counters, at every shape, and must be zero when a
- * call starts. Zero the workspace once after allocating it
- * (paged_decode_workspace_init, or any fill with zeros); every call leaves
- * the counters zero, so the same workspace then serves any later shape.
- * Calls that share a workspace must not overlap in time (issue them on one
- * stream, or order them with events). The partitions' fp32 partial outputs
- * and log-sum-exps are merged by the last workgroup to finish a (sequence,
- * head group), found through those counters, or, when that merge would
- * read more than 32 KiB in one workgroup (many query heads per KV head,
- * many partitions), by a second kernel queued right after the first.
+ * Workspace contract (split plans, S > 1): the workspace holds the
+ * partitions' fp32 partial outputs and log-sum-exps, which a second kernel,
+ * queued right after the first on the same stream, merges into `out`. A
+ * call writes every workspace byte it reads, so the workspace needs no
+ * initialisation and keeps nothing from one call to the next; any
+ * workspace at least as large as the shape needs serves it. Calls that
+ * share a workspace must not overlap in time (issue them on one stream, or
+ * order them with events).
  *
  * Errors: every entry point returns PD_OK or one of the codes below and
  * writes nothing when it fails before launching. No C++ exception crosses
@@ -118,8 +114,8 @@ int32_t paged_decode_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
 
 /*
  * Workspace bytes paged_decode_attention needs for this shape: 0 when the
- * plan has S = 1, else 256 KiB of counters plus room for fp32 partial
- * outputs [B, Hq, S, D] and fp32 partial log-sum-exps [B, Hq, S]. Returns 0
+ * plan has S = 1, else room for fp32 partial outputs [B, Hq, S, D] and fp32
+ * partial log-sum-exps [B, Hq, S], each rounded up to 256 bytes. Returns 0
  * for an invalid shape too (paged_decode_plan tells the two apart).
  */
 size_t paged_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -130,14 +126,15 @@ size_t paged_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
  * Zeroes `workspace_bytes` bytes (rounded down to a multiple of 4) of a
  * workspace on `stream` with a fill kernel (no memset node, so it is safe
  * to capture). `workspace` must be 256-byte aligned. PD_OK for 0 bytes.
+ * The decode never needs it (see the workspace contract); it gives a
+ * workspace defined contents for callers that want them.
  */
 int32_t paged_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Paged decode attention (see the top of this file). Queues its kernel on
  * `stream` (a hipStream_t; NULL is the null stream), and for split plans
- * whose merge runs on its own a merge kernel after it, and returns without
- * waiting. `workspace` may be NULL when paged_decode_workspace_bytes(...)
+ * the merge kernel after it, and returns without waiting. `workspace` may be NULL when paged_decode_workspace_bytes(...)
  * is 0; otherwise it must follow the workspace contract above. `scale` is
  * usually 1/sqrt(D) rounded to float.
  */
@@ -214,16 +211,16 @@ int32_t paged_decode_attention_fp8(const void* q, const void* k_cache, const voi
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * paged_decode_attention without a workspace argument. The split-K scratch
  * is one static device array per GPU of PAGED_DECODE_NOALLOC_SCRATCH_BYTES
- * (32 MiB: 256 KiB of arrival counters, then the fp32 partials), held from
- * the library's first call on that GPU until the process ends; nothing is
- * allocated or freed per call. Same arguments (minus the workspace), plan,
- * kernels and result as paged_decode_attention, bit for bit.
+ * (32 MiB of fp32 partials), held from the library's first call on that GPU
+ * until the process ends; nothing is allocated or freed per call. Same
+ * arguments (minus the workspace), plan, kernels and result as
+ * paged_decode_attention, bit for bit.
  *
- * The first call on a GPU looks up that GPU's copy of the array and queues
- * a fill kernel on `stream` that clears its counters; every call leaves
- * them zero. All calls on one GPU share the array: calls that overlap in
- * time on one GPU (on different streams without ordering) race and give
- * wrong results, so order them (one stream, or events).
+ * The first call on a GPU looks up that GPU's copy of the array. A call
+ * writes every byte of it that it reads, so nothing needs clearing; but all
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (on different streams without ordering) race and give wrong results, so
+ * order them (one stream, or events).
  *
  * Errors as paged_decode_attention, plus PD_ERR_SCRATCH (nothing queued)
  * when the shape's split plan needs more than the array holds, i.e. when

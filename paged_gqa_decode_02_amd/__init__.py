@@ -197,7 +197,9 @@ def _check(rc: int) -> None:
 
 
 def paged_decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
-    """Zero a workspace on the current (or given) stream with the library's fill kernel."""
+    """Zero a workspace on the current (or given) stream with the library's
+    fill kernel (the decode does not need it: a call writes every workspace
+    byte it reads)."""
     _check(_b.workspace_init(workspace, _stream_arg(stream)))
 
 
@@ -232,8 +234,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, out=N
     q [B,Hq,D], k_cache/v_cache [num_blocks,block_size,Hkv,D] (f16 or bf16,
     contiguous, on the GPU); block_table int32 [B,max_blocks_per_seq];
     context_lens int32 [B]. ``out`` (same shape/dtype as q) is allocated when
-    not given. Without a ``workspace`` the binding supplies one: a zeroed
-    buffer kept per (GPU, stream) for calls on the current stream, or one of
+    not given. Without a ``workspace`` the binding supplies one: a buffer
+    kept per (GPU, stream) for calls on the current stream, or one of
     the call's own, allocated on ``stream``, for calls given a stream or made
     under graph capture. ``scale`` defaults to D ** -0.5. ``num_splits``
     forces the split count (``paged_decode_attention_splits``). Returns

@@ -52,7 +52,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
            # the decode kernel's first arguments (block table, lengths, q and
            # the sizes and packed geometry their addresses need) arrive in
            # scalar registers
-           "-mllvm", "-amdgpu-kernarg-preload-count=9",
+           "-mllvm", "-amdgpu-kernarg-preload-count=8",
            "-Wall", "-Wno-unused-function", "-Werror=float-conversion",
            "-Werror=implicit-int-float-conversion",
            "-I", os.path.join(ROOT, "include")]

@@ -101,32 +101,32 @@ Tensor fresh_workspace(size_t need, int dev, const OptInt& stream, const Stream&
 
 // Workspaces supplied when the caller gives none: one per (GPU, stream),
 // grown when a call needs more and never freed, so that a graph that
-// captured a call keeps a valid pointer. Calls on one stream run in order
-// and leave the counters zero, so they can share one; calls on different
-// streams use different workspaces.
+// captured a call keeps a valid pointer. The decode needs no particular
+// contents (a call writes every workspace byte it reads), and calls on one
+// stream run in order, so they can share one; calls on different streams
+// use different workspaces.
 // (Held in objects that are never destroyed: their tensors must not be freed
 // by static destructors at exit, after torch's allocator may be gone.)
 std::mutex g_ws_mu;
 auto& g_ws = *new std::map<std::pair<int, uintptr_t>, Tensor>();
 auto& g_ws_retired = *new std::vector<Tensor>();
 
-// (pointer, bytes, keep-alive) of a zeroed workspace of at least `need`
-// bytes for a call on `s`, or nulls when none is needed; `rc` receives the
-// status of a fill. An explicit stream or a call under graph capture gets
-// one of its own, allocated and zeroed on the stream the call runs on.
+// (pointer, bytes, keep-alive) of a workspace of at least `need` bytes for
+// a call on `s`, or nulls when none is needed. An explicit stream or a call
+// under graph capture gets one of its own, allocated on the stream the call
+// runs on.
 std::tuple<void*, size_t, Tensor> auto_workspace(size_t need, int dev, const OptInt& stream,
-                                                 const Stream& s, int32_t* rc) {
-  *rc = PD_OK;
+                                                 const Stream& s) {
   if (need == 0) return {nullptr, 0, Tensor()};
+  const int64_t n = (int64_t)std::max<size_t>(need, 256);
   if (stream || c10::hip::currentStreamCaptureStatusMayInitCtx() != c10::hip::CaptureStatus::None) {
-    Tensor ws = fresh_workspace(need, dev, stream, s, rc);
+    Tensor ws = empty_on({n}, at::kByte, dev, stream, s);
     return {ws.data_ptr(), nbytes(ws), ws};
   }
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Tensor& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(handle(s))}];
   if (!ws.defined() || nbytes(ws) < need) {
-    Tensor fresh = fresh_workspace(need, dev, stream, s, rc);
-    if (*rc != PD_OK) return {nullptr, 0, Tensor()};
+    Tensor fresh = empty_on({n}, at::kByte, dev, stream, s);
     if (ws.defined()) g_ws_retired.push_back(ws);
     ws = fresh;
   }
@@ -204,8 +204,7 @@ std::tuple<Tensor, int64_t> decode(const Tensor& q, const Tensor& k, const Tenso
         num_splits ? paged_decode_workspace_bytes_splits((int32_t)B, Hq, Hkv, D, MB, bs, code,
                                                          (int32_t)*num_splits)
                    : paged_decode_workspace_bytes((int32_t)B, Hq, Hkv, D, MB, bs, code);
-    std::tie(wp, wn, keep) = auto_workspace(need, dev, stream, s, &rc);
-    if (rc != PD_OK) return {*out, rc};
+    std::tie(wp, wn, keep) = auto_workspace(need, dev, stream, s);
   }
   if (mode == kFp8) {
     rc = paged_decode_attention_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(),

@@ -28,8 +28,6 @@ struct Plan {
   int32_t wave_tokens;       // Pw: tokens per slice, a multiple of block_size,
                              //     at most 256 blocks; NT * Pw >= P
   int32_t head_split;        // HS: virtual KV heads per KV head, G / HS <= 16
-  bool merge_kernel;         // S > 1: merge in a kernel of its own, not in the
-                             //     workgroup that finishes a head group last
 };
 
 // Most blocks one wave's slice may span (four block ids per lane).
@@ -47,13 +45,9 @@ int32_t check_shape(const Shape& s);
 // and workspace queries, which do not know the cache format, stay right).
 int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_fp8 = false);
 
-// Workspace layout for S > 1: a fixed region of int32 arrival counters
-// [B, Hkv / NH] (kCounterBytes, the same at every shape, so it only ever
-// holds counters), then fp32 partial outputs [B, Hq, S, D], then fp32
-// partial log2-sum-exps [B, Hq, S], each 256-byte aligned. The counters
-// must be zero when a call starts; every call leaves them zero.
-constexpr size_t kCounterBytes = 256 * 1024;
-constexpr int64_t kMaxCounters = kCounterBytes / 4;
+// Workspace layout for S > 1: fp32 partial outputs [B, Hq, S, D], then fp32
+// partial log2-sum-exps [B, Hq, S], each 256-byte aligned. Every call
+// writes what it reads, so the workspace holds no state between calls.
 size_t partials_bytes(const Shape& s, const Plan& p);
 size_t lse_bytes(const Shape& s, const Plan& p);
 size_t workspace_bytes(const Shape& s, const Plan& p);
@@ -76,7 +70,8 @@ struct Launch {
   float v_scale;  // with kv_fp8: value = code * v_scale
 };
 
-// Queues the decode kernel; PD_* status code.
+// Queues the decode kernel, and for S > 1 the merge kernel after it on the
+// same stream; PD_* status code.
 int32_t launch(const Launch& l);
 
 // paged_decode_attention with scratch the library owns (pd_api.cpp): every

@@ -45,11 +45,11 @@
 //     the NT slices of a head are merged through LDS.
 //   * S == 1: the workgroup writes `out`, rounded to the dtype.
 //   * S > 1: the workgroup writes its fp32 partial output and log2-sum-exp
-//     with write-through (device-coherent) stores, then bumps a per
-//     (sequence, head group) counter; the workgroup that brings it to the
-//     number of non-empty partitions merges them in fixed order p = 0..n-1
-//     with L2-bypassing loads, writes `out` and resets the counter to zero.
-//     No device-wide cache flush is involved.
+//     (write-through stores), and a second kernel, queued right after on the
+//     same stream, merges the non-empty partitions of every (sequence, query
+//     head) in fixed order p = 0..n-1 and writes `out`. The kernel boundary
+//     orders the partials' stores before the merge's loads; no state is kept
+//     between calls.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -81,9 +81,8 @@ struct KArgs {
   void* out;
   float* o_part;      // [B, Hq, S, D]
   float* lse_part;    // [B, Hq, S], log2 domain
-  int32_t* counters;  // [B, Hkv / NH], at the start of the workspace
-  // Hkv, HS and NH serve the host: the kernel takes NH, HS and the physical
-  // KV heads packed in its preloaded `geo` argument
+  // Hkv, HS, NH and groups serve the host: the kernel takes NH, HS and the
+  // physical KV heads packed in its preloaded `geo` argument
   int32_t Hkv;  // virtual KV heads: physical KV heads x HS
   int32_t HS;   // virtual KV heads per physical KV head
   int32_t G;    // query heads per virtual KV head, <= 16
@@ -94,7 +93,6 @@ struct KArgs {
   int32_t NH;  // KV heads per workgroup
   int32_t NT;  // token slices per workgroup
   int32_t groups;  // head groups (workgroups per partition) per sequence: Hkv / NH
-  int32_t fused;   // S > 1: the last workgroup of a head group merges (else pd_merge_kernel)
   float scale_log2;    // scale * log2(e), times k_scale for an FP8 cache
   float out_scale;     // v_scale for an FP8 cache, else 1
   uint32_t blk_bytes;  // block_size * Hkv * D * element bytes
@@ -518,65 +516,6 @@ __device__ __forceinline__ Owner make_owner(int u, int G, int kM) {
   return o;
 }
 
-// LSE merge of nb <= W owned dim blocks of one head (dims dim0 + 16 w ..
-// +4, w < nb) over its n_live published partitions (rows slot0 + i of the
-// partial buffers), in order, KB partitions per batch of loads: the partial
-// outputs weighted by exp2(lse_i - max), normalised, rounded to the dtype
-// and stored at op + 16 w.
-template <bool BF16, int W, int KB>
-__device__ __forceinline__ void merge_blocks(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
-                                             uint32_t slot0, int n_live, uint32_t D,
-                                             uint32_t dim0, int nb, float out_scale,
-                                             uint16_t* op) {
-  float M = -INFINITY, den = 0.f;
-  f32x4 acc[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) acc[w] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; i0 < n_live; i0 += KB) {
-    float lse[KB];
-    f32x4 x[KB][W];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      // partitions past n_live and blocks past nb read zeros (and are
-      // skipped below)
-      const bool ok = i0 + u < n_live;
-      const uint32_t slot = slot0 + (uint32_t)(i0 + u);
-      const uint32_t off = (slot * D + dim0) * 4;
-#pragma unroll
-      for (int w = 0; w < W; ++w)
-        x[u][w] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       ro, ok && w < nb ? off + 64 * w : kOutOfBlock, 0, kCoherent));
-      lse[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             rl, ok ? slot * 4 : kOutOfBlock, 0, kCoherent));
-    }
-    // branch-free, so that every load of the batch is in flight before the
-    // first is used: a partition past n_live read zeros and enters with
-    // weight 0
-    float bm = M;
-#pragma unroll
-    for (int u = 0; u < KB; ++u) bm = fmaxf(bm, i0 + u < n_live ? lse[u] : -INFINITY);
-    const float alpha = exp2_fast(M - bm);  // 0 on the first batch
-    den *= alpha;
-#pragma unroll
-    for (int w = 0; w < W; ++w) acc[w] *= alpha;
-    M = bm;
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const float wt = i0 + u < n_live ? exp2_fast(lse[u] - M) : 0.f;
-      den += wt;
-#pragma unroll
-      for (int w = 0; w < W; ++w)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[w][e] = fmaf(wt, x[u][w][e], acc[w][e]);
-    }
-  }
-  const float inv = out_scale / den;
-#pragma unroll
-  for (int w = 0; w < W; ++w)
-    if (w < nb) store4<BF16>(op + 16 * w, acc[w], inv);
-}
-
 // The arguments the first loads depend on come first and on their own, so
 // that they can arrive preloaded in scalar registers (the library is built
 // with kernel-argument preloading); the rest are read from the argument
@@ -585,8 +524,7 @@ template <bool BF16, int BS, bool SPLIT, int NW, bool KV8, int D, bool FAST>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restrict__ cl_arg,
                       const uint16_t* __restrict__ q_arg, int32_t MB, int32_t P_arg,
-                      int32_t Pw_arg, int32_t G_arg, int32_t groups, int32_t geo,
-                      const KArgs a) {
+                      int32_t Pw_arg, int32_t G_arg, int32_t geo, const KArgs a) {
   using Gm = Geo<D>;
   constexpr int kS = Gm::kSteps, kM = Gm::kBlocks;
   constexpr int kOwn = FAST ? kM / 4 : kM;  // most dim blocks a lane owns
@@ -668,15 +606,9 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
       return;
     }
   } else {
-    if (t0 >= L) {  // empty partition: neither counted nor merged
-      if (L <= 0 && p == 0) {
-        // empty context: partition 0 writes the zero rows, no merge runs
-        uint16_t* o = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * NH * G) * D;
-        for (int i = threadIdx.x; i < NH * G * D / 8; i += nw * 64)
-          *(u32x4*)(o + i * 8) = u32x4{0u, 0u, 0u, 0u};
-      }
-      return;
-    }
+    // an empty partition publishes nothing: the merge reads partitions
+    // 0 .. ceil(L / P) - 1 only, and writes the zero rows of an empty context
+    if (t0 >= L) return;
   }
   const int tw1 = min(min(tw0 + Pw_arg, t0 + P_arg), L);
   const int nst = __builtin_amdgcn_readfirstlane(
@@ -898,66 +830,24 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
                                              WeightBias<BF16>::log2),
             rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
     }
-    // a separate merge kernel runs after this one (the kernel boundary orders
-    // the stores before its loads)
-    if (!a.fused) return;
-    // the stores are complete (and past every non-coherent cache) before the
-    // counter moves
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int s_last;
-    const int n_live = (L + P_arg - 1) / P_arg;
-    if (threadIdx.x == 0) {
-      int32_t* cnt = a.counters + (size_t)b * groups + hg;
-      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == n_live - 1;
-      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last || !own.active) return;
-
-    // ---- last workgroup: LSE merge over the n_live partitions, in order.
-    // It reads only the published partials, so the NT slice waves of a head
-    // share it: wave ts merges its share (per) of the lane's owned dim
-    // blocks, in passes of two blocks (eight partitions per batch of loads)
-    // or, when it has more, four blocks (four partitions per batch).
-    uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
-    const uint32_t hrow = (uint32_t)(h * a.S);  // the head's partition 0
-    const int per = (nown + a.NT - 1) / a.NT;
-    const int kb = ts * per, ke = min(nown, kb + per);
-    if (kOwn <= 2 || per <= 2) {
-#pragma unroll
-      for (int k0 = 0; k0 < kOwn; k0 += 2) {
-        if (kb + k0 >= ke) break;
-        merge_blocks<BF16, 2, 8>(ro, rl, hrow, n_live, (uint32_t)D,
-                                 (uint32_t)(d0 + 16 * (kb + k0)), min(2, ke - kb - k0),
-                                 a.out_scale, op + 16 * (kb + k0));
-      }
-    } else if constexpr (kOwn > 2) {
-#pragma unroll
-      for (int k0 = 0; k0 < kOwn; k0 += 4) {
-        if (kb + k0 >= ke) break;
-        merge_blocks<BF16, 4, 4>(ro, rl, hrow, n_live, (uint32_t)D,
-                                 (uint32_t)(d0 + 16 * (kb + k0)), min(4, ke - kb - k0),
-                                 a.out_scale, op + 16 * (kb + k0));
-      }
-    }
   }
 }
 
-// Zero the workspace (the split path's counters must start at zero).
+// Zero a workspace (paged_decode_workspace_init; the decode itself needs no
+// zeroed memory).
 __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
 }
 
-// The LSE merge as a kernel of its own, for plans whose merge would read too
-// much for the one workgroup that finishes a head group last (many query
-// heads per KV head, many partitions): one wave per (sequence, query head),
-// lane l holding dims [l * D/64, (l + 1) * D/64) of the head, the partitions
-// merged in order p = 0 .. n-1 in batches of kBatch loads.
+// The LSE merge of a split call, queued after the decode kernel on the same
+// stream: one wave per (sequence, query head), lane l holding dims
+// [l * D/64, (l + 1) * D/64) of the head, the n = ceil(L / P) non-empty
+// partitions merged in order p = 0 .. n-1 in batches of kBatch loads (an
+// empty context writes a zero row). A merge spread over B * Hq waves reads
+// the partials at the whole GPU's rate; merging in the workgroup that
+// finishes a head group last was slower on every split shape measured.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
@@ -1028,10 +918,10 @@ hipError_t launch_decode(const KArgs& ka, dim3 grid, int nw, hipStream_t st) {
   const int32_t* bt = ka.bt;
   const int32_t* cl = ka.cl;
   const uint16_t* q = ka.q;
-  int32_t mb = ka.MB, p = ka.P, pw = ka.Pw, g = ka.G, groups = ka.groups;
+  int32_t mb = ka.MB, p = ka.P, pw = ka.Pw, g = ka.G;
   int32_t geo = ka.NH | (ka.HS << 4) | ((ka.Hkv / ka.HS) << 12);
   void* args[] = {(void*)&bt, (void*)&cl, (void*)&q, (void*)&mb, (void*)&p, (void*)&pw,
-                  (void*)&g, (void*)&groups, (void*)&geo, (void*)&ka};
+                  (void*)&g, (void*)&geo, (void*)&ka};
   // the LDS tile buffers are sized for the largest workgroup of the instance
   const void* f = nw <= 4
       ? (const void*)&pd_decode_kernel<BF16, BS, SPLIT, 4, KV8, D, FAST>
@@ -1088,12 +978,10 @@ int32_t launch(const Launch& l) {
   ka.out = l.out;
   ka.o_part = nullptr;
   ka.lse_part = nullptr;
-  ka.counters = nullptr;
   if (l.plan.splits > 1) {
     char* ws = (char*)l.workspace;
-    ka.counters = (int32_t*)ws;
-    ka.o_part = (float*)(ws + kCounterBytes);
-    ka.lse_part = (float*)(ws + kCounterBytes + partials_bytes(l.shape, l.plan));
+    ka.o_part = (float*)ws;
+    ka.lse_part = (float*)(ws + partials_bytes(l.shape, l.plan));
   }
   const int hs = l.plan.head_split;
   ka.Hkv = l.shape.Hkv * hs;
@@ -1106,7 +994,6 @@ int32_t launch(const Launch& l) {
   ka.NH = l.plan.heads_per_group;
   ka.NT = l.plan.slices;
   ka.groups = ka.Hkv / l.plan.heads_per_group;
-  ka.fused = l.plan.merge_kernel ? 0 : 1;
   ka.scale_log2 = l.scale * 1.4426950408889634f * (l.kv_fp8 ? l.k_scale : 1.0f);
   ka.out_scale = l.kv_fp8 ? l.v_scale : 1.0f;
   ka.blk_bytes = (uint32_t)l.shape.block_size * (uint32_t)l.shape.Hkv *
@@ -1125,7 +1012,7 @@ int32_t launch(const Launch& l) {
   const bool bf16 = l.shape.dtype == PD_DTYPE_BF16;
   hipError_t e = pick_geometry(ka, grid, l.shape.block_size, nw, bf16, split, l.kv_fp8,
                                l.shape.D, st);
-  if (e == hipSuccess && split && l.plan.merge_kernel) {
+  if (e == hipSuccess && split) {
     int32_t hq = l.shape.Hq, S = ka.S, P = ka.P, cap = ka.MB * l.shape.block_size;
     float osc = ka.out_scale;
     const float* op = ka.o_part;

@@ -25,11 +25,6 @@ constexpr int64_t kTileTok = 16;      // tokens per K/V tile of a wave
 constexpr int64_t kMinSplitTiles = 2;  // tiles per wave a split must leave
 constexpr int64_t kNoSplitTiles = 4;   // tiles per wave below which a split never pays
 constexpr int64_t kPairTiles = 16;     // tiles per wave from which split KV heads go in pairs
-// A split's merge reads NH x G/HS query heads x S partitions x D floats. Up
-// to this many bytes the workgroup that finishes a head group last merges
-// them; beyond it one CU would stream too much alone (a CU reads some
-// 30-40 GB/s), and a merge kernel of its own spreads the reads over the GPU.
-constexpr int64_t kFusedMergeBytes = 32 * 1024;
 constexpr int64_t kMaxSplits = 65535;  // grid z
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -68,14 +63,11 @@ int32_t check_shape(const Shape& s) {
 //     per token);
 //   * when B * Hkv * NT / NH waves would leave SIMDs idle, the context is
 //     split until they are filled, keeping at least kMinSplitTiles tiles per
-//     wave; a split costs a cross-workgroup merge (about three memory round
-//     trips), so it is not used when a wave would have at most
-//     kNoSplitTiles tiles without it;
+//     wave; a split costs the partials' round trip through memory and a
+//     second kernel that merges them, so it is not used when a wave would
+//     have at most kNoSplitTiles tiles without it;
 //   * a split call whose waves still have kPairTiles or more tiles each
 //     does better with KV heads in pairs and twice the partitions;
-//   * a split whose merge would read more than kFusedMergeBytes in one
-//     workgroup (many query heads per wave, many partitions) merges in a
-//     kernel of its own;
 //   * tiles with more work per byte (an FP8 cache; 16 query heads per wave
 //     at D 64) take four slices per KV-head pair instead of two, which puts
 //     two waves on each SIMD (S and P are unchanged); an unsplit FP8 call
@@ -143,16 +135,15 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
   nt = ceil_div(P, pw);  // drop slices that would start past the partition
   const int64_t S = ceil_div(cap, P);
   if (S > kMaxSplits) return PD_ERR_SHAPE;
-  // the split path keeps one arrival counter per (sequence, head group)
-  if (S > 1 && (int64_t)s.B * (hkv / nh) > kMaxCounters) return PD_ERR_UNSUPPORTED;
   if (hkv > 65535) return PD_ERR_SHAPE;
+  // the merge kernel runs one workgroup per (sequence, query head)
+  if (S > 1 && (int64_t)s.B * s.Hq > INT_MAX) return PD_ERR_SHAPE;
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
   plan->heads_per_group = (int32_t)nh;
   plan->slices = (int32_t)nt;
   plan->wave_tokens = (int32_t)pw;
   plan->head_split = (int32_t)hs;
-  plan->merge_kernel = S > 1 && nh * (G / hs) * S * s.D * 4 > kFusedMergeBytes;
   return PD_OK;
 }
 
@@ -166,7 +157,7 @@ size_t lse_bytes(const Shape& s, const Plan& p) {
 
 size_t workspace_bytes(const Shape& s, const Plan& p) {
   if (p.splits <= 1) return 0;
-  return kCounterBytes + partials_bytes(s, p) + lse_bytes(s, p);
+  return partials_bytes(s, p) + lse_bytes(s, p);
 }
 
 }  // namespace pd

@@ -1,13 +1,14 @@
 // The decode entry point for callers that cannot allocate: its split-K
-// scratch (arrival counters, fp32 partial outputs and log-sum-exps) lives in
-// one static device array per GPU instead of a caller-owned workspace.
+// scratch (fp32 partial outputs and log-sum-exps) lives in one static device
+// array per GPU instead of a caller-owned workspace.
 //
 // The array's name is a host-side stand-in in host code; the device address
 // of each GPU's copy is looked up once per device (hipGetSymbolAddress, with
-// that device current) and only that address ever reaches a kernel or a
-// fill. Every GPU keeps its copy until the process ends. All calls on one
-// GPU share it and each call leaves its counters zero; calls that overlap in
-// time on one GPU (different streams, unordered) race on it.
+// that device current) and only that address ever reaches a kernel. Every
+// GPU keeps its copy until the process ends. A call writes every byte of it
+// that it reads, so no call depends on what an earlier one left; but all
+// calls on one GPU share it, and calls that overlap in time on one GPU
+// (different streams, unordered) race on it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,19 +20,13 @@
 namespace {
 
 static_assert(PAGED_DECODE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
-static_assert(PAGED_DECODE_NOALLOC_SCRATCH_BYTES > pd::kCounterBytes, "scratch size");
 
 static __device__ __align__(256) char scratch[PAGED_DECODE_NOALLOC_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
 
-struct DeviceScratch {
-  void* ptr = nullptr;  // device address of this GPU's copy of `scratch`
-  bool zeroed = false;  // counters cleared by an eager (not captured) fill
-};
-
 std::mutex g_mu;
-DeviceScratch g_dev[kMaxDevices];
+void* g_ptr[kMaxDevices];  // device address of each GPU's copy of `scratch`
 
 // The device `stream` belongs to (the current device for the null stream).
 int32_t stream_device(hipStream_t stream, int* dev) {
@@ -40,17 +35,14 @@ int32_t stream_device(hipStream_t stream, int* dev) {
 }
 
 // This GPU's copy of the scratch array, looked up on the first call on the
-// device; its counters are cleared by a fill kernel queued on `stream`
-// ahead of the decode. A fill queued under graph capture only runs with the
-// graph, so the first uncaptured call on the device queues one again.
+// device (with that device current).
 int32_t device_scratch(void* stream_arg, void** out) {
   const hipStream_t stream = (hipStream_t)stream_arg;
   int dev = 0;
   int32_t st = stream_device(stream, &dev);
   if (st != PD_OK) return st;
   std::lock_guard<std::mutex> lock(g_mu);
-  DeviceScratch& d = g_dev[dev];
-  if (!d.ptr) {
+  if (!g_ptr[dev]) {
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) return PD_ERR_HIP;
     if (cur != dev && hipSetDevice(dev) != hipSuccess) return PD_ERR_HIP;
@@ -58,16 +50,9 @@ int32_t device_scratch(void* stream_arg, void** out) {
     const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (cur != dev && hipSetDevice(cur) != hipSuccess) return PD_ERR_HIP;
     if (e != hipSuccess || !p) return PD_ERR_HIP;
-    d.ptr = p;
+    g_ptr[dev] = p;
   }
-  if (!d.zeroed) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return PD_ERR_HIP;
-    st = pd::zero_workspace(d.ptr, pd::kCounterBytes, stream);
-    if (st != PD_OK) return st;
-    if (cs == hipStreamCaptureStatusNone) d.zeroed = true;
-  }
-  *out = d.ptr;
+  *out = g_ptr[dev];
   return PD_OK;
 }
 

@@ -136,7 +136,7 @@ void fuzz_decode(int iters) {
     if (sp == PD_OK) {
       CHECK(S >= 1 && P >= 1 && (int64_t)S * P >= (int64_t)MB * bs);
       const size_t w = paged_decode_workspace_bytes(B, Hq, Hkv, D, MB, bs, dtype);
-      CHECK((S == 1) == (w == 0));
+      CHECK((S == 1 || B == 0) == (w == 0));
     }
     const int32_t sps = paged_decode_plan_splits(B, Hq, Hkv, D, MB, bs, dtype, splits, &S, &P);
     CHECK(known_status(sps));

@@ -68,7 +68,8 @@ def test_calls_without_out_or_workspace_on_given_streams():
                                                  c.block_size, torch.bfloat16), flush=True)
     torch.cuda.synchronize()
     # the current stream is held up: anything the binding queued there for
-    # these calls (zeroing their workspaces) would run after the decode
+    # these calls (say, to prepare their workspaces) would run after the
+    # decode
     torch.cuda._sleep(2_000_000)
     out_a = pd.paged_decode_attention(*devs[0], scale=cases[0].scale, stream=s1)
     out_b = pd.paged_decode_attention(*devs[1], scale=cases[1].scale, stream=s2.cuda_stream)
@@ -89,7 +90,7 @@ def test_calls_without_out_or_workspace_on_given_streams():
 
 def test_graph_capture_without_a_workspace():
     # under capture the binding gives the call a workspace of its own from
-    # the graph's pool, zeroed by a captured fill kernel on every replay
+    # the graph's pool
     import paged_gqa_decode_02_amd as pd
     c = workloads.splitk(4, 2048, seed=33)
     q, k, v, bt, cl = device_case(c)

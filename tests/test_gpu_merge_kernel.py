@@ -1,9 +1,9 @@
-"""The split path whose LSE merge runs in a kernel of its own (plans whose
-merge would read more than 32 KiB in one workgroup: many query heads per KV
-head, or many partitions), against the fp64 oracle: planned MQA shapes,
-forced partition counts on both sides of the switch, ragged and empty
-contexts, an FP8 cache, and a HIP graph holding both kernels replayed with
-the context lengths rewritten between replays."""
+"""The LSE merge kernel that every split call queues after the decode
+kernel, against the fp64 oracle: planned MQA shapes (many query heads per KV
+head, many partitions), forced partition counts up to 64 over a ragged
+batch, ragged and empty contexts, an FP8 cache, lengths outside the row, and
+a HIP graph holding both kernels replayed with the context lengths
+rewritten between replays."""
 import math
 
 import numpy as np
@@ -18,31 +18,26 @@ from helpers import check_case, compare, device_case, out_bits, run_library
 pytestmark = pytest.mark.gpu
 
 
-def merge_in_kernel(case, splits=None):
-    """(S, whether the merge runs in a kernel of its own) by the planner's
-    rule: NH x query heads per wave x S x D x 4 bytes above 32 KiB, with NH
-    = 2 when the virtual heads of a KV head pair up (informational)."""
+def planned_splits(case, splits=None):
+    """The partition count S the call will use (S > 1: the merge kernel runs)."""
     S, _ = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
                                 case.block_size, workloads.DTYPES[case.dtype], splits)
-    G = case.Hq // case.Hkv
-    hs = next(h for h in range(1, G + 1) if G % h == 0 and G // h <= 16)
-    nh = 2 if (case.Hkv * hs) % 2 == 0 and (hs % 2 == 0 or case.B * case.Hkv * hs >= 512) else 1
-    return S, S > 1 and nh * (G // hs) * S * case.D * 4 > 32 * 1024
+    return S
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,B,L", [(32, 1, 128, 8, 4096), (32, 1, 64, 4, 2048),
                                           (64, 1, 128, 2, 1024), (40, 2, 128, 3, 3000)])
-def test_planned_mqa_splits_merge_in_their_own_kernel(Hq, Hkv, D, B, L):
+def test_planned_mqa_splits_through_the_merge_kernel(Hq, Hkv, D, B, L):
     case = workloads.geometry(Hq, Hkv, D, B, L, seed=Hq + D + B)
-    S, mk = merge_in_kernel(case)
-    print(case.describe(), "S", S, "merge kernel", mk, flush=True)
+    S = planned_splits(case)
+    print(case.describe(), "S", S, flush=True)
     assert S > 1
     check_case(case)
 
 
 @pytest.mark.parametrize("splits", [9, 16, 17, 40, 64])
-def test_forced_splits_past_the_switch(splits):
-    # 32/8 with a ragged batch: S x 4 heads x 512 bytes crosses 32 KiB at S = 16
+def test_forced_splits_over_a_ragged_batch(splits):
+    # 32/8, contexts from empty to full: most sequences leave partitions empty
     case = workloads.make_case("mk_ragged", 5, [1024, 1, 333, 0, 1000], dtype="bf16",
                                block_size=16, seed=splits, max_blocks_per_seq=64)
     print(case.describe(), "splits", splits, flush=True)
@@ -51,7 +46,7 @@ def test_forced_splits_past_the_switch(splits):
 
 def test_fp8_cache_through_the_merge_kernel():
     case = workloads.geometry(32, 1, 128, 4, 2048, seed=77, kv_dtype="fp8")
-    S, mk = merge_in_kernel(case)
+    S = planned_splits(case)
     print(case.describe(), "S", S, flush=True)
     assert S > 1
     check_case(case)
@@ -75,9 +70,9 @@ def test_graph_with_both_kernels_reads_lengths_at_replay():
     case = workloads.make_case("mk_graph", 4, [4000, 2500, 4096, 1], Hq=32, Hkv=1, D=128,
                                dtype="bf16", block_size=16, seed=79, max_blocks_per_seq=256,
                                scale=float(np.float32(1 / math.sqrt(128))))
-    S, mk = merge_in_kernel(case)
-    print(case.describe(), "S", S, "merge kernel", mk, flush=True)
-    assert S > 1 and mk
+    S = planned_splits(case)
+    print(case.describe(), "S", S, flush=True)
+    assert S > 1
     q, k, v, bt, cl = device_case(case)
     out = torch.empty_like(q)
     ws = pd.alloc_workspace(q, k, bt)

@@ -111,8 +111,9 @@ def test_outputs_lie_within_the_range_of_the_valid_values(geom, splits):
 def test_lengths_outside_the_row_count_as_its_bounds(geom, splits):
     # a length above the row's capacity (max_blocks_per_seq * block_size) is
     # taken as the capacity and a negative one as 0: the outputs equal those
-    # of the lengths at the bounds, and the split counters stay clean (the
-    # same workspace then gives the in-range call's bits again)
+    # of the lengths at the bounds, and nothing of the call lingers in the
+    # split workspace (the same workspace then gives the in-range call's bits
+    # again)
     import torch
     import paged_gqa_decode_02_amd as pd
     Hq, Hkv, D, dtype, bs, kv = geom

@@ -46,7 +46,7 @@ def shapes(requests=(0,)):
 
 def test_every_plan_tiles_the_context_within_the_kernel_limits(probe):
     rows = list(shapes(requests=(0, 1, 2, 3, 7, 64)))
-    for r, (st, S, P, NH, NT, Pw, HS, MK) in zip(rows, probe([r + (0,) for r in rows])):
+    for r, (st, S, P, NH, NT, Pw, HS) in zip(rows, probe([r + (0,) for r in rows])):
         B, Hq, Hkv, D, MB, bs, _, req = r
         assert st == 0, r
         cap = MB * bs
@@ -60,9 +60,6 @@ def test_every_plan_tiles_the_context_within_the_kernel_limits(probe):
         assert Pw % bs == 0 and Pw <= MAX_WAVE_BLOCKS * bs, r
         assert NT * Pw >= P > (NT - 1) * Pw, r
         assert NH in (1, 2, 4, 8) and (Hkv * HS) % NH == 0 and NH * NT <= MAX_WAVES, r
-        # the merge runs in a kernel of its own exactly when a split's merge
-        # would read more than 32 KiB in one workgroup
-        assert MK == int(S > 1 and NH * (G // HS) * S * D * 4 > 32 * 1024), r
         if req:
             # a forced S fixes P, unless the waves' reach (whole slices of 256
             # blocks) caps the partition
@@ -99,18 +96,17 @@ def test_the_fill_target_is_one_wave_per_simd_of_a_whole_mi355x(probe):
     assert S31 > 1 and S32 == 1
     # in 4-wave workgroups: B x 8 KV heads x 4 slices x S reaches 1,024
     B = 4
-    (_, S, _, NH, NT, _, _, _), = probe([(B, 32, 8, 128, 64, 16, 1, 0, 0)])
+    (_, S, _, NH, NT, _, _), = probe([(B, 32, 8, 128, 64, 16, 1, 0, 0)])
     assert NH * NT == 4 and B * 8 * NT * S // NH >= 1024
 
 
 def test_many_query_heads_per_kv_head_split_to_fill_the_gpu(probe):
     # MQA 32/1 at batch 8: 16 virtual heads in pairs fill 1,024 waves with
-    # 32 partitions, merged by a kernel of its own; 32/8 at batch 8 keeps the
-    # merge in the last workgroup (8 KiB per workgroup)
-    (st, S, P, NH, NT, Pw, HS, MK), = probe([(8, 32, 1, 128, 256, 16, 1, 0, 0)])
-    assert st == 0 and HS == 2 and NH == 2 and S * NT * 8 * HS // NH >= 1024 // 2 and MK == 1
-    (st, S, P, NH, NT, Pw, HS, MK), = probe([(8, 32, 8, 128, 64, 16, 1, 0, 0)])
-    assert st == 0 and S == 4 and MK == 0
+    # 32 partitions; 32/8 at batch 8 takes 4
+    (st, S, P, NH, NT, Pw, HS), = probe([(8, 32, 1, 128, 256, 16, 1, 0, 0)])
+    assert st == 0 and HS == 2 and NH == 2 and S * NT * 8 * HS // NH >= 1024 // 2
+    (st, S, P, NH, NT, Pw, HS), = probe([(8, 32, 8, 128, 64, 16, 1, 0, 0)])
+    assert st == 0 and S == 4
 
 
 def test_unsplit_fp8_plans_with_one_kv_head_per_workgroup_take_eight_slices(probe):
@@ -130,3 +126,15 @@ def test_unsplit_fp8_plans_with_one_kv_head_per_workgroup_take_eight_slices(prob
         assert b[5] * b[4] == b[2], b                       # eight equal slices
     assert s16[1] == s8[1] > 1 and s16[4] == s8[4] == 4, (s16, s8)
     assert t8[4] == t16[4] == 4, (t16, t8)                  # a slice is at least a block
+
+
+def test_split_plans_keep_the_merge_grid_within_int32(probe):
+    # the merge kernel takes one workgroup per (sequence, query head): a
+    # split whose B x Hq passes INT32_MAX is refused (PD_ERR_SHAPE), the
+    # unsplit plan of the same shape is not
+    big = (65535, 4096 * 16, 4096, 128, 4, 16, 1)
+    (st1, S1, *_), (st2, *_), (st3, S3, *_) = probe(
+        [big + (0, 0), big + (2, 0), (65535, 8, 1, 128, 4, 16, 1, 2, 0)])
+    assert st1 == 0 and S1 == 1
+    assert st2 == 2
+    assert st3 == 0 and S3 == 2

@@ -2,8 +2,8 @@
 for callers that cannot allocate) against paged_decode_attention: same plan
 and kernels, so the outputs agree bit for bit. Two calls in a row share the
 library's static scratch, the second on a smaller input; the split plan is
-in use for both, so the scratch's counters and partials carry over from one
-call to the next."""
+in use for both, so the scratch's partials of the first call are still there
+when the second runs."""
 import numpy as np
 import pytest
 import torch
