@@ -842,10 +842,11 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
 }
 
 // The LSE merge of a split call, queued after the decode kernel on the same
-// stream: one wave per (sequence, query head), lane l holding dims
+// stream: one wave per (query head, sequence) of a (Hq, B) grid, lane l holding dims
 // [l * D/64, (l + 1) * D/64) of the head, the n = ceil(L / P) non-empty
 // partitions merged in order p = 0 .. n-1 in batches of kBatch loads (an
-// empty context writes a zero row). A merge spread over B * Hq waves reads
+// empty context writes a zero row); the first batch is loaded beside the
+// context length rather than after it. A merge spread over B * Hq waves reads
 // the partials at the whole GPU's rate; merging in the workgroup that
 // finishes a head group last was slower on every split shape measured.
 template <bool BF16, int D>
@@ -857,31 +858,20 @@ __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ 
                                                       float out_scale) {
   constexpr int kDl = D / 64;  // dims per lane
   constexpr int kBatch = 16;
-  const int bh = blockIdx.x;  // b * Hq + h
-  const int b = bh / Hq;
+  const int b = blockIdx.y;
+  const size_t bh = (size_t)b * Hq + blockIdx.x;  // (sequence, query head)
   const int lane = threadIdx.x;
-  const int L = min(__builtin_amdgcn_readfirstlane(cl[b]), cap);
-  uint16_t* op = out + (size_t)bh * D + lane * kDl;
-  if (L <= 0) {  // empty context: a zero row
-#pragma unroll
-    for (int e = 0; e < kDl; ++e) op[e] = 0;
-    return;
-  }
-  const int n = (L + P - 1) / P;
-  const float* orow = o_part + (size_t)bh * S * D + lane * kDl;
-  const float* lrow = lse_part + (size_t)bh * S;
-  float M = -INFINITY, den = 0.f, acc[kDl];
-#pragma unroll
-  for (int e = 0; e < kDl; ++e) acc[e] = 0.f;
-  // Every load of a batch is issued before any is used, and every loaded
-  // value is used, without branches: a row past n re-reads row n - 1 and
-  // enters with weight 0 (adding exact zeros), so the compiler has nothing
-  // to sink into a conditional and wait for one load at a time.
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
-    float x[kBatch][kDl], lse[kBatch];
+  const int L_arg = __builtin_amdgcn_readfirstlane(cl[b]);
+  const float* orow = o_part + bh * S * D + lane * kDl;
+  const float* lrow = lse_part + bh * S;
+  // Every load of a batch is issued before any is used. Row i of a batch
+  // reads partition min(i, last) (inside the call's rows), so no load waits
+  // alone inside a branch.
+  float x[kBatch][kDl], lse[kBatch];
+  auto load_batch = [&](int i0, int last) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int i = min(i0 + u, n - 1);
+      const int i = min(i0 + u, last);
       lse[u] = lrow[i];
       const float* r = orow + (size_t)i * D;
       if constexpr (kDl == 2) {
@@ -892,9 +882,24 @@ __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ 
         x[u][0] = r[0];
       }
     }
+  };
+  // The first batch goes out together with the length, over all S rows:
+  // rows of partitions past the live ones hold whatever an earlier call
+  // left (or nothing written yet) and are excluded by selects below, never
+  // multiplied in.
+  // (An empty context runs the same code with n = 0 and stores a zero row
+  // by a select at the end: a branch on the length here would let the
+  // compiler sink these loads behind the length's arrival.)
+  load_batch(0, S - 1);
+  const int L = min(L_arg, cap);
+  const int n = L > 0 ? (L + P - 1) / P : 0;
+  float M = -INFINITY, den = 0.f, acc[kDl];
+#pragma unroll
+  for (int e = 0; e < kDl; ++e) acc[e] = 0.f;
+  for (int i0 = 0;;) {
     float bm = M;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, lse[u]);  // repeats change nothing
+    for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, i0 + u < n ? lse[u] : -INFINITY);
     const float alpha = exp2_fast(M - bm);  // 0 on the first batch
     den *= alpha;
 #pragma unroll
@@ -902,15 +907,20 @@ __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ 
     M = bm;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const float wt = i0 + u < n ? exp2_fast(lse[u] - M) : 0.f;
+      const bool live = i0 + u < n;
+      const float wt = live ? exp2_fast(lse[u] - M) : 0.f;
       den += wt;
 #pragma unroll
-      for (int e = 0; e < kDl; ++e) acc[e] = fmaf(wt, x[u][e], acc[e]);
+      for (int e = 0; e < kDl; ++e) acc[e] = live ? fmaf(wt, x[u][e], acc[e]) : acc[e];
     }
+    i0 += kBatch;
+    if (i0 >= n) break;
+    load_batch(i0, n - 1);
   }
   const float inv = out_scale / den;
+  uint16_t* op = out + bh * D + lane * kDl;
 #pragma unroll
-  for (int e = 0; e < kDl; ++e) op[e] = to_bits<BF16>(acc[e] * inv);
+  for (int e = 0; e < kDl; ++e) op[e] = n > 0 ? to_bits<BF16>(acc[e] * inv) : (uint16_t)0;
 }
 
 template <bool BF16, int BS, bool SPLIT, bool KV8, int D, bool FAST>
@@ -1025,7 +1035,8 @@ int32_t launch(const Launch& l) {
                                              : (const void*)&pd_merge_kernel<true, 128>)
                           : (l.shape.D == 64 ? (const void*)&pd_merge_kernel<false, 64>
                                              : (const void*)&pd_merge_kernel<false, 128>);
-    e = hipLaunchKernel(mf, dim3((unsigned)(l.shape.B * l.shape.Hq)), dim3(64), margs, 0, st);
+    e = hipLaunchKernel(mf, dim3((unsigned)l.shape.Hq, (unsigned)l.shape.B), dim3(64), margs, 0,
+                        st);
   }
   return e == hipSuccess ? PD_OK : PD_ERR_HIP;
 }

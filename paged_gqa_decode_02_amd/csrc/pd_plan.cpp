@@ -136,7 +136,8 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
   const int64_t S = ceil_div(cap, P);
   if (S > kMaxSplits) return PD_ERR_SHAPE;
   if (hkv > 65535) return PD_ERR_SHAPE;
-  // the merge kernel runs one workgroup per (sequence, query head)
+  // the merge kernel runs one workgroup per (sequence, query head): keep
+  // their count within int32
   if (S > 1 && (int64_t)s.B * s.Hq > INT_MAX) return PD_ERR_SHAPE;
   plan->splits = (int32_t)S;
   plan->partition_tokens = (int32_t)P;
