@@ -844,12 +844,12 @@ __global__ void pd_zero_kernel(uint32_t* p, size_t n) {
 // The LSE merge of a split call, queued after the decode kernel on the same
 // stream: one wave per (query head, sequence) of a (Hq, B) grid, lane l holding dims
 // [l * D/64, (l + 1) * D/64) of the head, the n = ceil(L / P) non-empty
-// partitions merged in order p = 0 .. n-1 in batches of kBatch loads (an
+// partitions merged in order p = 0 .. n-1 in batches of KB loads (an
 // empty context writes a zero row); the first batch is loaded beside the
 // context length rather than after it. A merge spread over B * Hq waves reads
 // the partials at the whole GPU's rate; merging in the workgroup that
 // finishes a head group last was slower on every split shape measured.
-template <bool BF16, int D>
+template <bool BF16, int D, int KB>
 __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const int32_t* __restrict__ cl,
@@ -857,7 +857,7 @@ __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ 
                                                       int32_t S, int32_t P, int32_t cap,
                                                       float out_scale) {
   constexpr int kDl = D / 64;  // dims per lane
-  constexpr int kBatch = 16;
+  constexpr int kBatch = KB;  // S <= KB (one batch) unless KB = 16
   const int b = blockIdx.y;
   const size_t bh = (size_t)b * Hq + blockIdx.x;  // (sequence, query head)
   const int lane = threadIdx.x;
@@ -921,6 +921,20 @@ __global__ __launch_bounds__(64) void pd_merge_kernel(const float* __restrict__ 
   uint16_t* op = out + bh * D + lane * kDl;
 #pragma unroll
   for (int e = 0; e < kDl; ++e) op[e] = n > 0 ? to_bits<BF16>(acc[e] * inv) : (uint16_t)0;
+}
+
+// The merge instance for a call: the batch is the smallest of 4, 8 and 16
+// loads that holds S rows (16 for more), so no load repeats a row in vain.
+template <bool BF16, int D>
+const void* pick_merge_batch(int S) {
+  return S <= 4   ? (const void*)&pd_merge_kernel<BF16, D, 4>
+         : S <= 8 ? (const void*)&pd_merge_kernel<BF16, D, 8>
+                  : (const void*)&pd_merge_kernel<BF16, D, 16>;
+}
+
+const void* pick_merge(bool bf16, int D, int S) {
+  if (bf16) return D == 64 ? pick_merge_batch<true, 64>(S) : pick_merge_batch<true, 128>(S);
+  return D == 64 ? pick_merge_batch<false, 64>(S) : pick_merge_batch<false, 128>(S);
 }
 
 template <bool BF16, int BS, bool SPLIT, bool KV8, int D, bool FAST>
@@ -1031,10 +1045,7 @@ int32_t launch(const Launch& l) {
     uint16_t* out = (uint16_t*)ka.out;
     void* margs[] = {(void*)&op, (void*)&lp, (void*)&cl, (void*)&out, (void*)&hq,
                      (void*)&S,  (void*)&P,  (void*)&cap, (void*)&osc};
-    const void* mf = bf16 ? (l.shape.D == 64 ? (const void*)&pd_merge_kernel<true, 64>
-                                             : (const void*)&pd_merge_kernel<true, 128>)
-                          : (l.shape.D == 64 ? (const void*)&pd_merge_kernel<false, 64>
-                                             : (const void*)&pd_merge_kernel<false, 128>);
+    const void* mf = pick_merge(bf16, l.shape.D, S);
     e = hipLaunchKernel(mf, dim3((unsigned)l.shape.Hq, (unsigned)l.shape.B), dim3(64), margs, 0,
                         st);
   }

@@ -25,6 +25,7 @@ constexpr int64_t kTileTok = 16;      // tokens per K/V tile of a wave
 constexpr int64_t kMinSplitTiles = 2;  // tiles per wave a split must leave
 constexpr int64_t kNoSplitTiles = 4;   // tiles per wave below which a split never pays
 constexpr int64_t kPairTiles = 16;     // tiles per wave from which split KV heads go in pairs
+constexpr int64_t kMergeBatch = 16;    // partitions the merge kernel loads in one batch
 constexpr int64_t kMaxSplits = 65535;  // grid z
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -68,6 +69,11 @@ int32_t check_shape(const Shape& s) {
 //     have at most kNoSplitTiles tiles without it;
 //   * a split call whose waves still have kPairTiles or more tiles each
 //     does better with KV heads in pairs and twice the partitions;
+//   * a split call that still has fewer workgroups than CUs (a small batch
+//     whose split the kMinSplitTiles floor capped) takes workgroups of two
+//     waves and up to twice the partitions, kept within one merge batch
+//     (kMergeBatch): the same waves then spread over twice the CUs, and one
+//     CU reads at most some 44 GB/s;
 //   * tiles with more work per byte (an FP8 cache; 16 query heads per wave
 //     at D 64) take four slices per KV-head pair instead of two, which puts
 //     two waves on each SIMD (S and P are unchanged); an unsplit FP8 call
@@ -107,6 +113,16 @@ int32_t make_plan(const Shape& s, int32_t requested_splits, Plan* plan, bool kv_
         nh = 2;
         nt = kWaves / nh;
         S *= 2;
+      }
+      if (nh == 1 && nt == 4 && S > 1 && units * S < kCUs) {
+        int64_t s2 = ceil_div(kFillWaves, units * 2);
+        const int64_t s2_max = cap / (2 * kMinSplitTiles * kTileTok);
+        if (s2 > s2_max) s2 = s2_max;
+        if (s2 > kMergeBatch) s2 = kMergeBatch;
+        if (s2 > S) {
+          nt = 2;
+          S = s2;
+        }
       }
     }
     P = round_up(ceil_div(cap, S), bs);

@@ -138,3 +138,20 @@ def test_split_plans_keep_the_merge_grid_within_int32(probe):
     assert st1 == 0 and S1 == 1
     assert st2 == 2
     assert st3 == 0 and S3 == 2
+
+
+def test_small_split_batches_spread_over_more_cus(probe):
+    # B1 ctx1024: 8 KV heads x 4 slices would stop at S = 8 (two tiles per
+    # wave), 64 workgroups; two-wave workgroups reach S = 16, 128
+    # workgroups, the same 256 waves on twice the CUs. B1 ctx2048 keeps its
+    # 16 partitions (more would take a second merge batch) and B4 ctx1024
+    # already has a workgroup per CU.
+    rows = probe([(1, 32, 8, 128, 64, 16, 1, 0, 0), (1, 32, 8, 128, 128, 16, 1, 0, 0),
+                  (4, 32, 8, 128, 64, 16, 1, 0, 0), (2, 32, 8, 128, 32, 16, 1, 0, 0)])
+    (st1, S1, P1, NH1, NT1, *_), (st2, S2, _, NH2, NT2, *_), (st3, S3, _, NH3, NT3, *_), \
+        (st4, S4, _, NH4, NT4, *_) = rows
+    assert st1 == st2 == st3 == st4 == 0
+    assert (S1, NH1, NT1) == (16, 1, 2) and P1 == 64
+    assert (S2, NH2, NT2) == (16, 1, 4)
+    assert (S3, NH3, NT3) == (8, 1, 4)
+    assert (S4, NH4, NT4) == (8, 1, 2)      # B2 ctx512: 64 -> 128 workgroups
