@@ -107,3 +107,38 @@ def test_merge_kernel_results_are_bitwise_stable():
     a = out_bits(run_library(case, dev=dev))
     for _ in range(3):
         assert np.array_equal(out_bits(run_library(case, dev=dev)), a)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 4, 5, 8, 9, 16, 17, 33])
+@pytest.mark.parametrize("kv", ["", "fp8"])
+def test_every_merge_batch_ignores_what_empty_partitions_hold(splits, kv):
+    # the merge kernel loads its first batch over all S rows before it knows
+    # the length, and drops the rows of empty partitions by selects: with
+    # the workspace filled with NaN bytes before every call, batches of 4,
+    # 8 and 16 (and a second batch past 16) must still give the oracle's
+    # rows, for contexts that leave most partitions empty
+    lens = [1024, 1, 333, 0, 1000, 17, 512, 64]
+    case = workloads.make_case(f"mk_nan_S{splits}{'_' + kv if kv else ''}", len(lens), lens,
+                               dtype="bf16", block_size=16, seed=100 + splits,
+                               max_blocks_per_seq=64, kv_dtype=kv)
+    q, k, v, bt, cl = device_case(case)
+    S, _ = pd.paged_decode_plan(case.B, case.Hq, case.Hkv, case.D, case.max_blocks_per_seq,
+                                case.block_size, torch.bfloat16, splits)
+    print(case.describe(), "splits", splits, "S", S, flush=True)
+    assert S > 1
+    need = pd.paged_decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.D,
+                                           case.max_blocks_per_seq, case.block_size,
+                                           torch.bfloat16, splits)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ref, _ = oracle.attention_case(case)
+    for rep in range(2):
+        ws.fill_(0xFF)
+        if kv:
+            out = pd.paged_decode_attention_fp8(q, k, v, bt, cl, k_scale=case.k_scale,
+                                                v_scale=case.v_scale, scale=case.scale,
+                                                workspace=ws, num_splits=splits)
+        else:
+            out = pd.paged_decode_attention(q, k, v, bt, cl, scale=case.scale, workspace=ws,
+                                            num_splits=splits)
+        torch.cuda.synchronize()
+        compare(out_bits(out), ref, "bf16", what=f"{case.name} rep {rep}")
