@@ -143,7 +143,8 @@ int32_t rope_paged_kv_write_fp8(const void* q, const void* k, const void* v,
  * naming an id outside the pool is skipped, so nothing outside the arrays
  * is touched). Errors: PD_ERR_SHAPE (negative counts, num_blocks < 1,
  * block_bytes not a positive multiple of 16, too many items for one
- * launch), PD_ERR_NULL, PD_ERR_ALIGN, PD_ERR_ALIAS, PD_ERR_HIP.
+ * launch: n * ceil(block_bytes / 4096) >= 2^24), PD_ERR_NULL, PD_ERR_ALIGN,
+ * PD_ERR_ALIAS, PD_ERR_HIP.
  */
 
 /*

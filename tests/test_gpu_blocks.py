@@ -16,13 +16,16 @@ from helpers import out_bits
 pytestmark = pytest.mark.gpu
 
 GEOMS = [
-    # num_blocks, block_size, Hkv, D, dtype: 32 KiB, 64 KiB, 4 KiB (part of a
-    # 16 KiB chunk), 12 KiB and 48 KiB (3 chunks) blocks
+    # num_blocks, block_size, Hkv, D, dtype: 32 KiB, 64 KiB, 4 KiB (one
+    # 4 KiB chunk), 12 KiB and 48 KiB (3 and 12 chunks), 2 KiB (half a chunk)
+    # and 6 KiB (a chunk and a half) blocks
     (512, 16, 8, 128, "bf16"),
     (256, 32, 8, 128, "f16"),
     (300, 16, 2, 64, "bf16"),
     (200, 16, 3, 128, "bf16"),
     (128, 16, 12, 128, "f16"),
+    (256, 16, 1, 64, "bf16"),
+    (96, 16, 3, 64, "f16"),
 ]
 
 
