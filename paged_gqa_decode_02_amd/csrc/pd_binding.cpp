@@ -99,12 +99,13 @@ Tensor fresh_workspace(size_t need, int dev, const OptInt& stream, const Stream&
   return ws;
 }
 
-// Workspaces supplied when the caller gives none: one per (GPU, stream),
-// grown when a call needs more and never freed, so that a graph that
-// captured a call keeps a valid pointer. The decode needs no particular
-// contents (a call writes every workspace byte it reads), and calls on one
-// stream run in order, so they can share one; calls on different streams
-// use different workspaces.
+// Workspaces supplied to eager calls on the current stream when the caller
+// gives none: one per (GPU, stream), replaced by a larger one when a call
+// needs more (the outgrown ones are kept, not freed, while calls queued
+// earlier may still read them). The decode needs no particular contents (a
+// call writes every workspace byte it reads), and calls on one stream run in
+// order, so they can share one; calls on different streams use different
+// workspaces, and captured calls get their own from the graph's pool.
 // (Held in objects that are never destroyed: their tensors must not be freed
 // by static destructors at exit, after torch's allocator may be gone.)
 std::mutex g_ws_mu;
