@@ -42,7 +42,8 @@
 //     (read from LDS with the transposing ds_read_b64_tr_b16) and the
 //     weights, accumulating in fp32.
 //   * end of slice: each head's D sums sit in the 4 lanes of its column;
-//     the NT slices of a head are merged through LDS.
+//     the NT slices of a head are merged through LDS, every wave of the
+//     workgroup taking a share of the outputs.
 //   * S == 1: the workgroup writes `out`, rounded to the dtype.
 //   * S > 1: the workgroup writes its fp32 partial output and log2-sum-exp
 //     (write-through stores), and a second kernel, queued right after on the
@@ -756,8 +757,10 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
   const int d0 = 16 * own.block(0) + 4 * row;  // first owned dim; runs of 4 every 16
 
   // ---- merge the NT slices of each head through LDS (the first tile
-  // buffer, sized to hold G * (D + 2) floats per wave as G <= 16); slice 0
-  // keeps the result
+  // buffer, sized to hold G * (D + 2) floats per wave as G <= 16): every
+  // wave writes its slice's sums, then all the workgroup's waves share the
+  // merge, one thread per (KV head of the group, query head, 4 dims), each
+  // combining the NT slices in order i = 0..NT-1, and store the result
   if (a.NT > 1) {
     __syncthreads();  // every wave is done with its tile buffers
     float* s_acc = (float*)lds0;                 // [(w*G + h)*D + dim]
@@ -773,63 +776,77 @@ void pd_decode_kernel(const int32_t* __restrict__ bt_arg, const int32_t* __restr
       }
     }
     __syncthreads();
-    if (ts == 0 && own.active) {
-      float M = m_r;
-      for (int i = 1; i < a.NT; ++i) M = fmaxf(M, s_m[(i * NH + hl) * G + h]);
+    constexpr int kD4 = D / 4;
+    const int units = NH * G * kD4;
+    // the head group's rows of the partial buffers (split calls only)
+    const size_t gslot0 = ((size_t)b * Hq + (size_t)hg * NH * G) * a.S;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(SPLIT ? a.o_part + gslot0 * D : nullptr,
+                  SPLIT ? (uint32_t)(NH * G) * a.S * D * 4 : 0u);
+    const __amdgpu_buffer_rsrc_t rl =
+        make_rsrc(SPLIT ? a.lse_part + gslot0 : nullptr, SPLIT ? (uint32_t)(NH * G) * a.S * 4 : 0u);
+    for (int u = threadIdx.x; u < units; u += nw * 64) {
+      const int uh = u / kD4;  // hl * G + h: the group's query head
+      const int d4 = u - uh * kD4;
+      const int uhl = uh / G, uhh = uh - uhl * G;
+      float M = -INFINITY;
+      for (int i = 0; i < a.NT; ++i) M = fmaxf(M, s_m[(i * NH + uhl) * G + uhh]);
       float den = 0.f;
-#pragma unroll
-      for (int k = 0; k < kOwn; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int i = 0; i < a.NT; ++i) {
-        const int wi = (i * NH + hl) * G + h;
+        const int wi = (i * NH + uhl) * G + uhh;
         const float wt = exp2_fast(s_m[wi] - M);  // 0 for a slice with no tokens
         den = fmaf(wt, s_l[wi], den);
-        // every read is issued unconditionally (blocks past nown re-read the
-        // last owned one; those o[k] are never stored), so no read waits
-        // alone inside a branch
+        const f32x4 x = *(const f32x4*)(s_acc + wi * D + 4 * d4);
 #pragma unroll
-        for (int k = 0; k < kOwn; ++k) {
-          const int kk = FAST ? k : min(k, nown - 1);
-          const f32x4 x = *(const f32x4*)(s_acc + wi * D + d0 + 16 * kk);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[k][e] = fmaf(wt, x[e], o[k][e]);
-        }
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
       }
-      m_r = M;
-      l_r = den;
-    }
-  }
-  const bool owner = ts == 0 && own.active;
-
-  if constexpr (!SPLIT) {
-    if (owner) {
-      uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
-      const float inv = a.out_scale / l_r;
-#pragma unroll
-      for (int k = 0; k < kOwn; ++k)
-        if (k < nown) store4<BF16>(op + 16 * k, o[k], inv);
+      if constexpr (!SPLIT) {
+        uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)hg * NH * G + uh) * D + 4 * d4;
+        store4<BF16>(op, acc, a.out_scale / den);
+      } else {
+        // this partition's (o_p, lse_p), write-through; the raw buffer
+        // builtins move 32-bit words, so floats go through bit casts
+        const uint32_t row_off = (uint32_t)(uh * a.S + p);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc * (1.0f / den)), ro,
+                                               (row_off * D + 4 * d4) * 4, 0, kCoherent);
+        if (d4 == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, M + __builtin_amdgcn_logf(den) -
+                                               WeightBias<BF16>::log2),
+              rl, row_off * 4, 0, kCoherent);
+      }
     }
     return;
+  }
+
+  // ---- one slice per head: the lanes that own the results store them
+  if (!own.active) return;
+  if constexpr (!SPLIT) {
+    uint16_t* op = (uint16_t*)a.out + ((size_t)b * Hq + (size_t)g * G + h) * D + d0;
+    const float inv = a.out_scale / l_r;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k)
+      if (k < nown) store4<BF16>(op + 16 * k, o[k], inv);
   } else {
     // ---- publish this partition's (o_p, lse_p), write-through
     const size_t slot0 = ((size_t)b * Hq + (size_t)g * G) * a.S;  // (head 0, partition 0)
     const uint32_t rows_bytes = (uint32_t)G * a.S * D * 4;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o_part + slot0 * D, rows_bytes);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse_part + slot0, (uint32_t)G * a.S * 4);
-    if (owner) {
-      // the raw buffer builtins move 32-bit words: floats go through bit casts
-      const float inv = 1.0f / l_r;
-      const uint32_t off = ((uint32_t)(h * a.S + p) * D + d0) * 4;
+    // the raw buffer builtins move 32-bit words: floats go through bit casts
+    const float inv = 1.0f / l_r;
+    const uint32_t off = ((uint32_t)(h * a.S + p) * D + d0) * 4;
 #pragma unroll
-      for (int k = 0; k < kOwn; ++k)
-        if (k < nown)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[k] * inv), ro,
-                                                 off + 64 * k, 0, kCoherent);
-      if (row == 0 && own.copy == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r) -
-                                             WeightBias<BF16>::log2),
-            rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
-    }
+    for (int k = 0; k < kOwn; ++k)
+      if (k < nown)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[k] * inv), ro,
+                                               off + 64 * k, 0, kCoherent);
+    if (row == 0 && own.copy == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __builtin_bit_cast(uint32_t, m_r + __builtin_amdgcn_logf(l_r) -
+                                           WeightBias<BF16>::log2),
+          rl, (uint32_t)(h * a.S + p) * 4, 0, kCoherent);
   }
 }
 
